@@ -1,0 +1,353 @@
+"""CPU oracle for Q8_0 weight-only GEMV, LM-head argmax and routed-expert FFN.
+
+TEST INFRASTRUCTURE ONLY: only ``tests/``, ``__graft_entry__.smoke()`` and the
+benchmark's CPU-baseline leg may import this package. It shares no code with
+the HIP library (``quantized_weight_gemv_q8_amd``) and imports nothing from
+it; both are fed from the seeded generator, which holds no GEMV arithmetic.
+
+Layers:
+
+* ``q8_oracle.c`` (plain C, fp64, sequential in k; built by gcc with
+  -ffp-contract=off, no fast-math): the dequant-and-dot itself, its own fp16
+  and GGUF block decoders.
+* this module: the gates built on it. Each function names the passage it
+  follows.
+
+Sources: memra wiki (feature list: Q8_0 decode matvecs, expert-major CSR
+MoE batching, CUDA-graph decode returning 4 bytes/token; gate paragraph:
+kernel-check of every kernel against a CPU reference, the run-gen argmax
+gate) and memra performance (serving exactness arc: a request's tokens must
+not depend on its co-arrivals). The numeric contract (per-output error at
+most 1e-3 * sum|d*q*x|; argmax identical wherever the top-2 gap exceeds that
+bound) is the library's stated acceptance bar; the pages fix the format and
+the gates, not a tolerance.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "q8_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+REL_TOL = 1e-3  # per-output bound: |err| <= REL_TOL * sum_k |d*q*x|
+QK = 32
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile q8_oracle.c with gcc (plain C, IEEE fp64, no contraction)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        cmd = ["gcc", "-O2", "-std=c99", "-ffp-contract=off", "-fno-fast-math",
+               "-fPIC", "-shared", "-o", tmp, _SRC, "-lpthread", "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _get():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build(force=True)
+        L = ctypes.CDLL(_LIB)
+        i64, vp, i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+        L.or_half_to_double.argtypes = [ctypes.c_uint16]
+        L.or_half_to_double.restype = ctypes.c_double
+        L.or_decode_blocks.argtypes = [vp, i64, i64, vp, vp]
+        L.or_decode_blocks.restype = i32
+        L.or_gemv_f16x.argtypes = [vp, vp, i64, i64, vp, i64, vp, vp, i32]
+        L.or_gemv_f16x.restype = i32
+        L.or_gemv_f32x.argtypes = [vp, vp, i64, i64, vp, i64, vp, vp, i32]
+        L.or_gemv_f32x.restype = i32
+        L.or_gemv_rows_f16x.argtypes = [vp, vp, i64, i64, vp, i64, vp, i64, vp, vp, i32]
+        L.or_gemv_rows_f16x.restype = i32
+        _lib = L
+    return _lib
+
+
+def _p(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def default_threads() -> int:
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+# ---------------------------------------------------------------- decoding
+def half_to_double(bits: int) -> float:
+    """IEEE binary16 bit pattern -> exact float (oracle's own decoder)."""
+    return _get().or_half_to_double(bits & 0xFFFF)
+
+
+def decode_blocks(blocks: np.ndarray):
+    """GGUF Q8_0 blocks uint8 [M][K/32][34] -> (q int8 [M][K], d fp16 [M][K/32])."""
+    blocks = np.ascontiguousarray(blocks, dtype=np.uint8)
+    M, nb, bb = blocks.shape
+    if bb != 2 + QK:
+        raise ValueError("Q8_0 blocks are 34 bytes")
+    K = nb * QK
+    q = np.empty((M, K), np.int8)
+    d = np.empty((M, nb), np.uint16)
+    rc = _get().or_decode_blocks(_p(blocks), M, K, _p(q), _p(d))
+    if rc:
+        raise ValueError(f"or_decode_blocks rc={rc}")
+    return q, d.view(np.float16)
+
+
+# ---------------------------------------------------------------- the GEMV
+def gemv(q: np.ndarray, d: np.ndarray, x: np.ndarray, threads: int = 1):
+    """y[n][m] = sum_k d[m][k/32]*q[m][k]*x[n][k] in fp64; also A = sum|terms|.
+
+    x may be fp16 (decode activations) or fp32 (MoE intermediate h).
+    Returns (y, A), both float64 [N][M].
+    """
+    q = np.ascontiguousarray(q, np.int8)
+    d16 = np.ascontiguousarray(d, np.float16).view(np.uint16)
+    M, K = q.shape
+    if d16.shape != (M, K // QK) or K % QK:
+        raise ValueError("shape mismatch between q and d")
+    x = np.ascontiguousarray(x)
+    if x.ndim != 2 or x.shape[1] != K:
+        raise ValueError("x must be [N][K]")
+    N = x.shape[0]
+    y = np.empty((N, M), np.float64)
+    A = np.empty((N, M), np.float64)
+    L = _get()
+    if x.dtype == np.float16:
+        rc = L.or_gemv_f16x(_p(q), _p(d16), M, K, _p(x.view(np.uint16)), N, _p(y), _p(A), threads)
+    elif x.dtype == np.float32:
+        rc = L.or_gemv_f32x(_p(q), _p(d16), M, K, _p(x), N, _p(y), _p(A), threads)
+    else:
+        raise TypeError("x must be float16 or float32")
+    if rc:
+        raise ValueError(f"oracle gemv rc={rc}")
+    return y, A
+
+
+def gemv_rows(q, d, x, rows, threads: int = 1):
+    """Oracle on a sample of weight rows: returns (y, A) float64 [N][len(rows)]."""
+    q = np.ascontiguousarray(q, np.int8)
+    d16 = np.ascontiguousarray(d, np.float16).view(np.uint16)
+    x = np.ascontiguousarray(x, np.float16)
+    rows = np.ascontiguousarray(rows, np.int64)
+    M, K = q.shape
+    N = x.shape[0]
+    R = rows.shape[0]
+    y = np.empty((N, R), np.float64)
+    A = np.empty((N, R), np.float64)
+    rc = _get().or_gemv_rows_f16x(_p(q), _p(d16), M, K, _p(x.view(np.uint16)), N,
+                                  _p(rows), R, _p(y), _p(A), threads)
+    if rc:
+        raise ValueError(f"oracle gemv_rows rc={rc}")
+    return y, A
+
+
+def bound(A: np.ndarray, y: np.ndarray | None = None, out_dtype: str = "f32") -> np.ndarray:
+    """Per-output acceptance bound.
+
+    b = 1e-3 * A. When the output is stored as fp16, add half an fp16 ulp of
+    the exact result, which covers the final rounding for fp16-subnormal
+    outputs; for normal outputs the fp16 rounding already fits inside b.
+    """
+    b = REL_TOL * np.asarray(A, np.float64)
+    if out_dtype == "f16":
+        if y is None:
+            raise ValueError("fp16 bound needs y")
+        b = b + 0.5 * fp16_ulp(y)
+    return b
+
+
+def fp16_ulp(v: np.ndarray) -> np.ndarray:
+    """Spacing of fp16 values at |v| (2^-24 for subnormals and zero)."""
+    a = np.abs(np.asarray(v, np.float64))
+    out = np.full(a.shape, 2.0 ** -24)
+    nz = a >= 2.0 ** -14
+    e = np.floor(np.log2(a[nz]))
+    out[nz] = 2.0 ** (e - 10)
+    return out
+
+
+def check_close(y_gpu: np.ndarray, y: np.ndarray, A: np.ndarray, out_dtype: str = "f32"):
+    """GEMV gate: pass iff |y_gpu - y| <= bound for every output.
+
+    Returns (ok, max_rel, n_bad) with max_rel = max |y_gpu - y| / A (0 where
+    A == 0; there y_gpu must be exactly zero).
+    """
+    y_gpu = np.asarray(y_gpu, np.float64)
+    err = np.abs(y_gpu - y)
+    b = bound(A, y, out_dtype)
+    bad = ~(err <= b)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        rel = np.where(A > 0, err / np.where(A > 0, A, 1.0), np.where(err > 0, np.inf, 0.0))
+    return (not bad.any()), float(rel.max(initial=0.0)), int(bad.sum())
+
+
+# ---------------------------------------------------------------- argmax gate
+def argmax_first(L: np.ndarray) -> np.ndarray:
+    """Index of the first maximum of each row (ties -> lowest index; -0 == +0)."""
+    return np.argmax(np.asarray(L, np.float64), axis=-1)
+
+
+def argmax_gate(L: np.ndarray, A: np.ndarray):
+    """Which tokens have an argmax that the bound cannot flip.
+
+    For each token n: i* = first argmax of the oracle logits L[n];
+    b = 1e-3*A[n]. Token n is gated (exact argmax required) iff
+    L[n,i*] - b[n,i*] > max_{j != i*} (L[n,j] + b[n,j]); otherwise any id in
+    the candidate set {j : L[n,j] + b[n,j] >= L[n,i*] - b[n,i*]} is correct.
+    Follows the run-gen argmax gate (memra wiki, gate paragraph: the argmax
+    must MATCH before any number counts).
+
+    Returns (istar int64 [N], gated bool [N], candidates list of int arrays).
+    """
+    L = np.asarray(L, np.float64)
+    b = REL_TOL * np.asarray(A, np.float64)
+    N = L.shape[0]
+    istar = argmax_first(L)
+    gated = np.zeros(N, bool)
+    cands = []
+    for n in range(N):
+        i = istar[n]
+        lo = L[n, i] - b[n, i]
+        hi = L[n] + b[n]
+        others = np.delete(hi, i)
+        gated[n] = bool(lo > (others.max() if others.size else -np.inf))
+        cands.append(np.nonzero(hi >= lo)[0])
+    return istar, gated, cands
+
+
+# ---------------------------------------------------------------- MoE
+def moe_route(expert_ids: np.ndarray, E: int):
+    """Expert-major CSR of the routed (token, slot) pairs.
+
+    Pair p = t*topk + j. counts[e] = #pairs routed to e; offsets = exclusive
+    prefix sum (E+1 entries); pairs lists p grouped by expert in ascending e,
+    and inside one expert in ascending p. active = experts with counts > 0,
+    ascending. Follows the expert-major CSR batching of routed experts
+    (memra wiki, feature list, "MoE on 24 GB").
+    """
+    ids = np.asarray(expert_ids)
+    T, topk = ids.shape
+    counts = np.zeros(E, np.int32)
+    buckets = [[] for _ in range(E)]
+    for t in range(T):
+        for j in range(topk):
+            e = int(ids[t, j])
+            if not 0 <= e < E:
+                raise ValueError(f"expert id {e} out of range")
+            counts[e] += 1
+            buckets[e].append(t * topk + j)
+    offsets = np.zeros(E + 1, np.int32)
+    for e in range(E):
+        offsets[e + 1] = offsets[e] + counts[e]
+    pairs = np.array([p for e in range(E) for p in buckets[e]], np.int32)
+    active = np.array([e for e in range(E) if counts[e] > 0], np.int32)
+    return counts, offsets, pairs, active
+
+
+def silu(z: np.ndarray) -> np.ndarray:
+    """silu(z) = z / (1 + exp(-z)) in fp64."""
+    z = np.asarray(z, np.float64)
+    return z / (1.0 + np.exp(-z))
+
+
+def moe_gate_up(case, threads: int = 1):
+    """Stage 1 of the routed FFN: per pair p=(t,j) with e = ids[t,j]:
+    g = W_gate[e] x_t, u = W_up[e] x_t (fp64), their A sums, and
+    h = silu(g) * u with a propagated bound.
+
+    Bound on h (fp32 GPU h vs this fp64 h): with b_g, b_u the GEMV bounds,
+    |dh| <= 1.1*b_g*|u| + |silu(g)|*b_u + b_g*b_u*1.1 + 1e-6*|h|: 1.1 bounds
+    |silu'|, the last term covers fp32 exp, division and products.
+    Returns dict of [P][F] arrays in pair order p = t*topk + j.
+    """
+    T, topk = case.expert_ids.shape
+    F = case.q_gate.shape[1]
+    P = T * topk
+    g = np.empty((P, F)); u = np.empty((P, F)); Ag = np.empty((P, F)); Au = np.empty((P, F))
+    for e in np.unique(case.expert_ids):
+        tj = np.argwhere(case.expert_ids == e)
+        xs = case.x[tj[:, 0]]
+        ge, age = gemv(case.q_gate[e], case.d_gate[e], xs, threads)
+        ue, aue = gemv(case.q_up[e], case.d_up[e], xs, threads)
+        p = tj[:, 0] * topk + tj[:, 1]
+        g[p], Ag[p], u[p], Au[p] = ge, age, ue, aue
+    h = silu(g) * u
+    bg, bu = REL_TOL * Ag, REL_TOL * Au
+    bh = 1.1 * bg * np.abs(u) + np.abs(silu(g)) * bu + 1.1 * bg * bu + 1e-6 * np.abs(h)
+    return dict(g=g, u=u, Ag=Ag, Au=Au, h=h, bh=bh)
+
+
+def moe_down(case, h_pairs: np.ndarray, threads: int = 1):
+    """Stage 2: y_pair[p] = W_down[e] h[p] (fp64) for the given fp32 h [P][F].
+
+    Takes the GPU's own h as input so the down GEMV is gated against exactly
+    the activations it consumed. Returns (y_pair [P][H], A [P][H]).
+    """
+    T, topk = case.expert_ids.shape
+    H = case.q_down.shape[1]
+    P = T * topk
+    h_pairs = np.ascontiguousarray(h_pairs, np.float32)
+    y = np.empty((P, H)); A = np.empty((P, H))
+    for e in np.unique(case.expert_ids):
+        tj = np.argwhere(case.expert_ids == e)
+        p = tj[:, 0] * topk + tj[:, 1]
+        ye, ae = gemv(case.q_down[e], case.d_down[e], h_pairs[p], threads)
+        y[p], A[p] = ye, ae
+    return y, A
+
+
+def moe_combine(gate_w: np.ndarray, y_pairs: np.ndarray):
+    """Stage 3: out[t] = sum_j gate_w[t,j] * y_pair[t*topk+j] (ascending j), fp64.
+
+    Returns (out [T][H], S [T][H] = sum_j |gate_w * y_pair|).
+    """
+    gw = np.asarray(gate_w, np.float64)
+    T, topk = gw.shape
+    yp = np.asarray(y_pairs, np.float64).reshape(T, topk, -1)
+    out = np.zeros((T, yp.shape[2]))
+    S = np.zeros_like(out)
+    for j in range(topk):
+        out = out + gw[:, j:j + 1] * yp[:, j]
+        S = S + np.abs(gw[:, j:j + 1] * yp[:, j])
+    return out, S
+
+
+def moe_ffn(case, threads: int = 1):
+    """End-to-end chain: out[t] = sum_j w_tj * W_down[e] (silu(W_gate[e] x_t) * W_up[e] x_t).
+
+    The down stage consumes h rounded to fp32 (the activation dtype the
+    GPU's down GEMV reads); that rounding (<= 2^-24 |h|) is inside the
+    1e-6*|h| term of the h bound. Also returns a propagated bound for an
+    fp32 GPU result: per pair, the down GEMV bound (1e-3 * A_down) plus
+    |W_down| applied to the h bound, gate-weighted and summed over j, plus
+    1e-6 of the combine magnitude.
+    """
+    s1 = moe_gate_up(case, threads)
+    y, Ay = moe_down(case, s1["h"].astype(np.float32), threads)
+    T, topk = case.expert_ids.shape
+    H = case.q_down.shape[1]
+    prop = np.zeros((T * topk, H))
+    for e in np.unique(case.expert_ids):
+        tj = np.argwhere(case.expert_ids == e)
+        p = tj[:, 0] * topk + tj[:, 1]
+        qa = np.abs(case.q_down[e].astype(np.int32)).astype(np.float64)
+        wabs = (qa.reshape(H, -1, QK) * case.d_down[e].astype(np.float64)[:, :, None]).reshape(H, -1)
+        prop[p] = s1["bh"][p] @ wabs.T
+    out, S = moe_combine(case.gate_w, y)
+    per_pair = REL_TOL * Ay + prop
+    gw = np.asarray(case.gate_w, np.float64)
+    b = (gw[:, :, None] * per_pair.reshape(T, topk, H)).sum(axis=1) + 1e-6 * S
+    return dict(out=out, bound=b, stage1=s1, y_pair=y, A_pair=Ay)

@@ -1,0 +1,15 @@
+"""Shared pytest configuration.
+
+Markers: ``gpu`` marks tests that need an MI355X (gfx950) device; everything
+else runs on a CPU-only host.
+"""
+import os
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU")
