@@ -1,0 +1,209 @@
+/*
+ * q8gemv.h -- C ABI of the MI355X (gfx950) Q8_0 weight-only GEMV library.
+ *
+ * What the library computes. A Q8_0 weight matrix W [M][K] is stored as
+ * blocks of 32 consecutive elements along K; each block holds one fp16
+ * scale d and 32 int8 quants q, and the weight is d*q. This is the GGUF
+ * Q8_0 format that the memra engine loads and runs through its decode
+ * matvecs (memra wiki, feature list: "NVFP4 / Q4_0 / Q8_0 decode" with
+ * split-plane repacked matvecs and per-shape auto-dispatch; "Loaders").
+ * For N tokens x [N][K]:
+ *
+ *     y[n][m] = sum_k d[m][k/32] * q[m][k] * x[n][k]
+ *
+ * N = 1 is plain decode; N = 2..8 is the batched K+1 verify of speculative
+ * decoding (memra wiki, feature list: "MTP speculative decoding ... one
+ * batched K+1 verify"). Accuracy contract: every output is within
+ * 1e-3 * sum_k |d*q*x| of the exact value (fp32 accumulation); the result
+ * for token n is bitwise independent of N and of the other tokens' values
+ * (the pages require verify logits to equal plain decode exactly: memra
+ * wiki gate paragraph, "K=1..8 self-consistency gate"; bw24 README
+ * "zero differing logits").
+ *
+ * Conventions for every entry point:
+ *  - Pointers marked [dev] are device memory (hipMalloc or a torch
+ *    tensor's data pointer) owned by the caller; [host] are host memory.
+ *    The library allocates nothing and keeps no per-call state; it caches
+ *    only per-device properties, once, thread-safely.
+ *  - Inputs are never written; outputs are fully overwritten.
+ *  - `stream` is a hipStream_t (NULL = the null stream). Hot-path calls
+ *    only enqueue kernels on it: no allocation, no synchronisation, no
+ *    host<->device copy, so they can be captured in a HIP graph (the pages
+ *    run one graph replay per decoded token: memra wiki, feature list,
+ *    "CUDA-graph decode").
+ *  - Errors: arguments are validated before anything is enqueued; a
+ *    negative q8_status is returned and nothing is launched. A launch
+ *    failure reported by the HIP runtime returns Q8_ERR_LAUNCH. Faults
+ *    inside a kernel surface at the caller's next synchronisation, like any
+ *    HIP call. Unsupported inputs are refused, never silently routed to a
+ *    slow path (topairepos memra listing: "useful failures over silent
+ *    fallbacks").
+ *  - The library runs only on gfx950; on any other device every hot-path
+ *    call returns Q8_ERR_DEVICE (memra wiki: the engine verifies at start-up
+ *    that the binary matches the device and fails early otherwise).
+ */
+#ifndef Q8GEMV_H
+#define Q8GEMV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    Q8_OK = 0,
+    Q8_ERR_NULL = -1,      /* a required pointer is NULL */
+    Q8_ERR_SHAPE = -2,     /* M, K, N, E, T or topk out of range, K % 32 != 0 */
+    Q8_ERR_ALIGN = -3,     /* a pointer or leading dimension breaks 16-byte alignment */
+    Q8_ERR_DTYPE = -4,     /* unsupported dtype code */
+    Q8_ERR_WORKSPACE = -5, /* workspace NULL, misaligned or too small */
+    Q8_ERR_DEVICE = -6,    /* current device is not gfx950, or no device */
+    Q8_ERR_LAUNCH = -7,    /* the HIP runtime rejected a launch */
+    Q8_ERR_ALIAS = -8      /* an output overlaps an input it must not */
+} q8_status;
+
+typedef enum { Q8_DT_F16 = 1, Q8_DT_F32 = 2 } q8_dtype;
+
+/* One packed Q8_0 matrix [M][K], rows = outputs, blocks along K, in the
+ * split-plane layout written by q8_pack_host: a quant plane and a scale
+ * plane, every row starting on a 16-byte boundary.
+ *   qs   [dev] int8 [M][ld_qs]: row m holds q[m][0..K-1] in K order.
+ *   d    [dev] fp16 bit patterns [M][ld_d]: row m holds the K/32 scales.
+ *   K % 32 == 0, M >= 1, ld_qs >= K and ld_qs % 16 == 0,
+ *   ld_d >= K/32 and ld_d % 8 == 0, qs and d 16-byte aligned.
+ * Any layout with these strides is accepted; e.g. one interleaved buffer
+ * per row ([K quants][K/32 scales]) is qs = base, d = base + K,
+ * ld_qs = K + K/16 bytes, ld_d = ld_qs / 2, valid when K % 256 == 0. */
+typedef struct q8_matrix {
+    const int8_t *qs;
+    const uint16_t *d;
+    int64_t M, K;
+    int64_t ld_qs; /* bytes */
+    int64_t ld_d;  /* fp16 elements */
+} q8_matrix;
+
+/* E experts of identical shape: expert e's matrix is e0 with
+ * qs + e*stride_qs and d + e*stride_d. Strides keep 16-byte alignment
+ * (stride_qs % 16 == 0, stride_d % 8 == 0). */
+typedef struct q8_bank {
+    q8_matrix e0;
+    int64_t stride_qs; /* bytes */
+    int64_t stride_d;  /* fp16 elements */
+    int32_t E;
+} q8_bank;
+
+/* Human-readable name of a status code (static string). */
+const char *q8_status_str(int status);
+
+/* Q8_OK iff HIP device `device` is a gfx950 part. */
+int q8_device_check(int device);
+
+/* ------------------------------------------------------------ packing (host)
+ * Load-time repack of GGUF Q8_0 blocks into the split-plane layout (memra
+ * wiki: "split-plane repacked matvecs"; the onboarding CLI packs models
+ * into the engine's own layout, topairepos memra listing, memra-cli row).
+ *
+ * q8_pack_layout: leading dimensions and plane sizes for an [M][K] matrix:
+ *   ld_qs = K (bytes), ld_d = round_up(K/32, 8) (fp16 elements),
+ *   qs_bytes = M*ld_qs, d_bytes = 2*M*ld_d. Any output pointer may be NULL.
+ * q8_pack_host: blocks [host] = M rows of K/32 blocks of 34 bytes
+ *   (little-endian fp16 scale, then 32 int8) -> qs [host] [M][ld_qs],
+ *   d [host] [M][ld_d]. Padding is written as zero. Byte-exact: unpacking
+ *   gives the input back.
+ * q8_unpack_host: the inverse. */
+int q8_pack_layout(int64_t M, int64_t K, int64_t *ld_qs, int64_t *ld_d,
+                   size_t *qs_bytes, size_t *d_bytes);
+int q8_pack_host(const void *blocks, int64_t M, int64_t K,
+                 int8_t *qs, int64_t ld_qs, uint16_t *d, int64_t ld_d);
+int q8_unpack_host(const int8_t *qs, int64_t ld_qs, const uint16_t *d, int64_t ld_d,
+                   int64_t M, int64_t K, void *blocks);
+
+/* ------------------------------------------------------------ dense GEMV
+ * y[n][m] = sum_k d[m][k/32]*q[m][k]*x[n][k] for n < N, m < W->M.
+ *   x [dev] [N][W->K], dtype x_dt (Q8_DT_F16 or Q8_DT_F32), contiguous,
+ *     16-byte aligned.
+ *   y [dev] [N][W->M], dtype y_dt (Q8_DT_F32, or Q8_DT_F16 rounded to
+ *     nearest even), contiguous; must not overlap x.
+ *   N >= 1. N > 8 runs as consecutive passes of at most 8 tokens; per-token
+ *   results stay bitwise identical to N = 1.
+ * Every weight byte is read once per pass of up to 8 tokens. */
+int q8_gemv(const q8_matrix *W, const void *x, int x_dt, void *y, int y_dt, int N,
+            void *stream);
+
+/* Fused pair: ya = Wa x and yb = Wb x in one launch sharing one staging of
+ * x (an MLP's gate and up projections). Wa->K == Wb->K; M may differ.
+ * ya [N][Wa->M], yb [N][Wb->M]. Results are bitwise equal to two q8_gemv
+ * calls. No activation is applied. */
+int q8_gemv_pair(const q8_matrix *Wa, const q8_matrix *Wb, const void *x, int x_dt,
+                 void *ya, void *yb, int y_dt, int N, void *stream);
+
+/* ------------------------------------------------------------ LM head
+ * logits[n][v] = W x_n (as q8_gemv with fp32 output) and
+ * ids[n] = the smallest v with logits[n][v] == max_v logits[n][v]
+ * (ties go to the lowest index; -0 and +0 compare equal). The argmax is
+ * taken over the same fp32 values that are written to logits, so ids is
+ * always consistent with logits. logits may be NULL (only ids are written:
+ * "lean logits", the caller copies back 4 bytes per token, as in the pages'
+ * graph decode; memra wiki feature list, "4 bytes/token host traffic").
+ *   x [dev] fp16 or fp32 [N][K]; logits [dev] fp32 [N][V] or NULL;
+ *   ids [dev] int32 [N]; N >= 1 (passes of up to 8 tokens).
+ *   ws [dev] workspace of at least q8_lmhead_ws_bytes(V, N) bytes,
+ *   16-byte aligned, contents need not be initialised. Concurrent calls
+ *   must use distinct workspaces. */
+size_t q8_lmhead_ws_bytes(int64_t V, int N);
+int q8_lmhead_argmax(const q8_matrix *W, const void *x, int x_dt, float *logits,
+                     int32_t *ids, int N, void *ws, size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------ routed experts
+ * Expert-major CSR batching of routed experts (memra wiki, feature list,
+ * "MoE ... expert-major CSR batching"): the routed (token, slot) pairs are
+ * grouped by expert on the device, and each active expert's weights are
+ * streamed once for all tokens routed to it. Routing never leaves the
+ * device (graph-replayable device-side lengths, memra wiki, feature list).
+ * A token's outputs never depend on which other tokens share the batch
+ * (memra performance, serving exactness arc).
+ *
+ * expert_ids [dev] int32 [T][topk]: expert of slot j of token t; the
+ *   topk ids of one token must be distinct and in [0, E). Ids are trusted
+ *   (checking them would need a synchronisation); out-of-range ids are
+ *   skipped by the kernels and their outputs are left as zero.
+ * gate_w [dev] fp32 [T][topk]: combine weights (e.g. softmax router output).
+ * Pair p = t*topk + j.
+ *
+ * Workspace layout (q8_moe_ws_layout gives byte offsets; all int32 unless
+ * noted): [0] counts[E], [1] offsets[E+1], [2] pairs[T*topk] (pair ids in
+ * expert-major order, ascending p inside an expert), [3] active[E]
+ * (experts with count > 0, ascending), [4] n_active[1], [5] h fp32
+ * [T*topk][F] (q8_moe_ffn only), [6] y_pair fp32 [T*topk][Mout].
+ * The caller may read these after the call for inspection. */
+
+/* Routed GEMV over one bank W (E experts of [M][K]):
+ *   y_pair[p] = W[e_p] x_{src(p)}, src(p) = t if x_per_pair == 0 (x is
+ *   [T][K]), else p (x is [T*topk][K]).
+ *   gate_w == NULL: y [dev] fp32 [T*topk][M] receives y_pair.
+ *   gate_w != NULL: y [dev] fp32 [T][M] receives
+ *     sum_{j ascending} gate_w[t][j] * y_pair[t*topk + j].
+ * x_dt is Q8_DT_F16 or Q8_DT_F32. ws >= q8_moe_ws_bytes(E, T, topk, 0, M). */
+size_t q8_moe_ws_bytes(int E, int T, int topk, int64_t F, int64_t M);
+int q8_moe_ws_layout(int E, int T, int topk, int64_t F, int64_t M, size_t offsets[7]);
+int q8_moe_gemv(const q8_bank *W, const int32_t *expert_ids, const float *gate_w,
+                const void *x, int x_dt, int x_per_pair, float *y, int T, int topk,
+                void *ws, size_t ws_bytes, void *stream);
+
+/* Routed SiLU-gated expert FFN (the qwen/silu MoE class of the pages,
+ * memra performance, grouped expert lane):
+ *   h_p   = silu(Wg[e_p] x_t) * (Wu[e_p] x_t)            fp32 [F]
+ *   out_t = sum_{j ascending} gate_w[t][j] * Wd[e_p] h_p  fp32 [H]
+ * with silu(z) = z / (1 + exp(-z)). gate, up: banks of [F][H]; down: bank
+ * of [H][F]; the three banks have the same E. x [dev] fp16 [T][H];
+ * out [dev] fp32 [T][H]. ws >= q8_moe_ws_bytes(E, T, topk, F, H). */
+int q8_moe_ffn(const q8_bank *gate, const q8_bank *up, const q8_bank *down,
+               const int32_t *expert_ids, const float *gate_w, const void *x, int x_dt,
+               float *out, int T, int topk, void *ws, size_t ws_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* Q8GEMV_H */

@@ -1,0 +1,382 @@
+// q8_api.cpp -- the C ABI: argument validation, device check, dispatch.
+//
+// Every entry point validates all of its arguments before touching the HIP
+// runtime, so a bad call fails synchronously with nothing enqueued (and can
+// be tested on a host without a GPU). Then it checks, once per device, that
+// the current device is gfx950 (memra wiki: fail early when the binary does
+// not match the device), and enqueues kernels on the caller's stream.
+#include <hip/hip_runtime.h>
+#include <string.h>
+
+#include <mutex>
+
+#include "../../include/q8gemv.h"
+#include "q8_internal.h"
+
+using q8::DevInfo;
+using q8::HBank;
+using q8::HMat;
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_once[kMaxDevices];
+DevInfo g_info[kMaxDevices];
+int g_info_rc[kMaxDevices];
+
+void probe(int dev) {
+  DevInfo& d = g_info[dev];
+  d.device = dev;
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+    g_info_rc[dev] = Q8_ERR_DEVICE;
+    return;
+  }
+  d.cus = prop.multiProcessorCount;
+  d.lds_per_block = prop.sharedMemPerBlock;
+  d.gfx950 = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  g_info_rc[dev] = d.gfx950 ? Q8_OK : Q8_ERR_DEVICE;
+}
+
+// Current device's cached properties; Q8_ERR_DEVICE unless it is gfx950.
+int current_device(const DevInfo** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return Q8_ERR_DEVICE;
+  std::call_once(g_once[dev], probe, dev);
+  if (g_info_rc[dev] != Q8_OK) return g_info_rc[dev];
+  *out = &g_info[dev];
+  return Q8_OK;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+size_t dt_size(int dt) { return dt == Q8_DT_F16 ? 2 : dt == Q8_DT_F32 ? 4 : 0; }
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + nb && y < x + na;
+}
+
+int check_matrix(const q8_matrix* W) {
+  if (!W || !W->qs || !W->d) return Q8_ERR_NULL;
+  if (W->M < 1 || W->M > INT32_MAX || W->K < 32 || W->K % 32 || W->K > (1LL << 24))
+    return Q8_ERR_SHAPE;
+  if (W->ld_qs < W->K || W->ld_d < W->K / 32) return Q8_ERR_SHAPE;
+  if (W->ld_qs % 16 || W->ld_d % 8 || !aligned(W->qs, 16) || !aligned(W->d, 16))
+    return Q8_ERR_ALIGN;
+  return Q8_OK;
+}
+
+int check_bank(const q8_bank* B) {
+  if (!B) return Q8_ERR_NULL;
+  int rc = check_matrix(&B->e0);
+  if (rc) return rc;
+  if (B->E < 1) return Q8_ERR_SHAPE;
+  if (B->E > 1 && (B->stride_qs < B->e0.M * B->e0.ld_qs || B->stride_d < B->e0.M * B->e0.ld_d))
+    return Q8_ERR_SHAPE;
+  if (B->stride_qs % 16 || B->stride_d % 8) return Q8_ERR_ALIGN;
+  return Q8_OK;
+}
+
+HMat to_h(const q8_matrix* W) { return HMat{W->qs, W->d, W->M, W->K, W->ld_qs, W->ld_d}; }
+
+HBank to_hb(const q8_bank* B) {
+  return HBank{to_h(&B->e0), B->stride_qs, B->stride_d, (int)B->E};
+}
+
+int launch_rc(hipError_t e) { return e == hipSuccess ? Q8_OK : Q8_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+const char* q8_status_str(int status) {
+  switch (status) {
+    case Q8_OK: return "ok";
+    case Q8_ERR_NULL: return "null pointer";
+    case Q8_ERR_SHAPE: return "bad shape";
+    case Q8_ERR_ALIGN: return "misaligned pointer or leading dimension";
+    case Q8_ERR_DTYPE: return "unsupported dtype";
+    case Q8_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case Q8_ERR_DEVICE: return "device is not gfx950 (or no device)";
+    case Q8_ERR_LAUNCH: return "kernel launch failed";
+    case Q8_ERR_ALIAS: return "output overlaps an input";
+  }
+  return "unknown status";
+}
+
+int q8_device_check(int device) {
+  if (device < 0 || device >= kMaxDevices) return Q8_ERR_DEVICE;
+  int n = 0;
+  if (hipGetDeviceCount(&n) != hipSuccess || device >= n) return Q8_ERR_DEVICE;
+  std::call_once(g_once[device], probe, device);
+  return g_info_rc[device];
+}
+
+// ------------------------------------------------------------ packing
+int q8_pack_layout(int64_t M, int64_t K, int64_t* ld_qs, int64_t* ld_d, size_t* qs_bytes,
+                   size_t* d_bytes) {
+  if (M < 1 || K < 32 || K % 32) return Q8_ERR_SHAPE;
+  const int64_t lq = K;
+  const int64_t ld = (K / 32 + 7) / 8 * 8;
+  if (ld_qs) *ld_qs = lq;
+  if (ld_d) *ld_d = ld;
+  if (qs_bytes) *qs_bytes = (size_t)M * (size_t)lq;
+  if (d_bytes) *d_bytes = (size_t)M * (size_t)ld * 2;
+  return Q8_OK;
+}
+
+int q8_pack_host(const void* blocks, int64_t M, int64_t K, int8_t* qs, int64_t ld_qs, uint16_t* d,
+                 int64_t ld_d) {
+  if (!blocks || !qs || !d) return Q8_ERR_NULL;
+  if (M < 1 || K < 32 || K % 32) return Q8_ERR_SHAPE;
+  if (ld_qs < K || ld_d < K / 32) return Q8_ERR_SHAPE;
+  if (ld_qs % 16 || ld_d % 8) return Q8_ERR_ALIGN;
+  const uint8_t* src = (const uint8_t*)blocks;
+  const int64_t nb = K / 32;
+  for (int64_t m = 0; m < M; ++m) {
+    int8_t* qrow = qs + m * ld_qs;
+    uint16_t* drow = d + m * ld_d;
+    for (int64_t b = 0; b < nb; ++b) {
+      const uint8_t* blk = src + (m * nb + b) * 34;
+      drow[b] = (uint16_t)(blk[0] | ((uint16_t)blk[1] << 8));
+      memcpy(qrow + b * 32, blk + 2, 32);
+    }
+    if (ld_qs > K) memset(qrow + K, 0, (size_t)(ld_qs - K));
+    for (int64_t b = nb; b < ld_d; ++b) drow[b] = 0;
+  }
+  return Q8_OK;
+}
+
+int q8_unpack_host(const int8_t* qs, int64_t ld_qs, const uint16_t* d, int64_t ld_d, int64_t M,
+                   int64_t K, void* blocks) {
+  if (!blocks || !qs || !d) return Q8_ERR_NULL;
+  if (M < 1 || K < 32 || K % 32) return Q8_ERR_SHAPE;
+  if (ld_qs < K || ld_d < K / 32) return Q8_ERR_SHAPE;
+  uint8_t* dst = (uint8_t*)blocks;
+  const int64_t nb = K / 32;
+  for (int64_t m = 0; m < M; ++m) {
+    for (int64_t b = 0; b < nb; ++b) {
+      uint8_t* blk = dst + (m * nb + b) * 34;
+      const uint16_t v = d[m * ld_d + b];
+      blk[0] = (uint8_t)(v & 0xff);
+      blk[1] = (uint8_t)(v >> 8);
+      memcpy(blk + 2, qs + m * ld_qs + b * 32, 32);
+    }
+  }
+  return Q8_OK;
+}
+
+// ------------------------------------------------------------ dense GEMV
+static int gemv_impl(const q8_matrix* Wa, const q8_matrix* Wb, const void* x, int x_dt, void* ya,
+                     void* yb, int y_dt, int N, void* stream) {
+  int rc = check_matrix(Wa);
+  if (rc) return rc;
+  if (Wb) {
+    rc = check_matrix(Wb);
+    if (rc) return rc;
+    if (Wb->K != Wa->K) return Q8_ERR_SHAPE;
+  }
+  if (!x || !ya || (Wb && !yb)) return Q8_ERR_NULL;
+  if (N < 1) return Q8_ERR_SHAPE;
+  const size_t xs = dt_size(x_dt), ys = dt_size(y_dt);
+  if (!xs || !ys) return Q8_ERR_DTYPE;
+  if (!aligned(x, 16) || !aligned(ya, ys) || (Wb && !aligned(yb, ys))) return Q8_ERR_ALIGN;
+  const size_t xbytes = (size_t)N * Wa->K * xs;
+  const size_t yabytes = (size_t)N * Wa->M * ys;
+  if (overlap(x, xbytes, ya, yabytes)) return Q8_ERR_ALIAS;
+  if (Wb) {
+    const size_t ybbytes = (size_t)N * Wb->M * ys;
+    if (overlap(x, xbytes, yb, ybbytes) || overlap(ya, yabytes, yb, ybbytes)) return Q8_ERR_ALIAS;
+  }
+  const DevInfo* dev = nullptr;
+  rc = current_device(&dev);
+  if (rc) return rc;
+  const bool xf = x_dt == Q8_DT_F32;
+  const int per_pass = q8::max_tokens_per_pass(*dev, Wa->K, xf);
+  if (per_pass < 1) return Q8_ERR_SHAPE;
+  const HMat A = to_h(Wa);
+  HMat B;
+  if (Wb) B = to_h(Wb);
+  for (int n0 = 0; n0 < N; n0 += per_pass) {
+    const int nt = N - n0 < per_pass ? N - n0 : per_pass;
+    const char* xp = (const char*)x + (size_t)n0 * Wa->K * xs;
+    char* yap = (char*)ya + (size_t)n0 * Wa->M * ys;
+    char* ybp = Wb ? (char*)yb + (size_t)n0 * Wb->M * ys : nullptr;
+    hipError_t e = q8::launch_gemv(*dev, A, Wb ? &B : nullptr, xp, xf, Wa->K, yap, ybp,
+                                   y_dt == Q8_DT_F16, nt, (hipStream_t)stream);
+    if (e != hipSuccess) return Q8_ERR_LAUNCH;
+  }
+  return Q8_OK;
+}
+
+int q8_gemv(const q8_matrix* W, const void* x, int x_dt, void* y, int y_dt, int N, void* stream) {
+  return gemv_impl(W, nullptr, x, x_dt, y, nullptr, y_dt, N, stream);
+}
+
+int q8_gemv_pair(const q8_matrix* Wa, const q8_matrix* Wb, const void* x, int x_dt, void* ya,
+                 void* yb, int y_dt, int N, void* stream) {
+  if (!Wb) return Q8_ERR_NULL;
+  return gemv_impl(Wa, Wb, x, x_dt, ya, yb, y_dt, N, stream);
+}
+
+// ------------------------------------------------------------ LM head
+size_t q8_lmhead_ws_bytes(int64_t V, int N) {
+  (void)V;
+  (void)N;
+  return (size_t)4096 * 8 * sizeof(uint64_t);
+}
+
+int q8_lmhead_argmax(const q8_matrix* W, const void* x, int x_dt, float* logits, int32_t* ids,
+                     int N, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_matrix(W);
+  if (rc) return rc;
+  if (!x || !ids) return Q8_ERR_NULL;
+  if (N < 1) return Q8_ERR_SHAPE;
+  const size_t xs = dt_size(x_dt);
+  if (!xs) return Q8_ERR_DTYPE;
+  if (!aligned(x, 16) || !aligned(ids, 4) || (logits && !aligned(logits, 4))) return Q8_ERR_ALIGN;
+  if (!ws || !aligned(ws, 16) || ws_bytes < q8_lmhead_ws_bytes(W->M, N)) return Q8_ERR_WORKSPACE;
+  const size_t xbytes = (size_t)N * W->K * xs;
+  const size_t lbytes = logits ? (size_t)N * W->M * 4 : 0;
+  if ((logits && overlap(x, xbytes, logits, lbytes)) || overlap(x, xbytes, ids, 4 * (size_t)N) ||
+      (logits && overlap(logits, lbytes, ids, 4 * (size_t)N)) ||
+      overlap(ws, ws_bytes, x, xbytes) || overlap(ws, ws_bytes, ids, 4 * (size_t)N) ||
+      (logits && overlap(ws, ws_bytes, logits, lbytes)))
+    return Q8_ERR_ALIAS;
+  const DevInfo* dev = nullptr;
+  rc = current_device(&dev);
+  if (rc) return rc;
+  const bool xf = x_dt == Q8_DT_F32;
+  const int per_pass = q8::max_tokens_per_pass(*dev, W->K, xf);
+  if (per_pass < 1) return Q8_ERR_SHAPE;
+  const HMat A = to_h(W);
+  for (int n0 = 0; n0 < N; n0 += per_pass) {
+    const int nt = N - n0 < per_pass ? N - n0 : per_pass;
+    const char* xp = (const char*)x + (size_t)n0 * W->K * xs;
+    float* lp = logits ? logits + (size_t)n0 * W->M : nullptr;
+    hipError_t e = q8::launch_lmhead(*dev, A, xp, xf, lp, W->M, ids + n0, (uint64_t*)ws, nt,
+                                     (hipStream_t)stream);
+    if (e != hipSuccess) return Q8_ERR_LAUNCH;
+  }
+  return Q8_OK;
+}
+
+// ------------------------------------------------------------ routed experts
+size_t q8_moe_ws_bytes(int E, int T, int topk, int64_t F, int64_t M) {
+  if (E < 1 || T < 1 || topk < 1 || F < 0 || M < 0) return 0;
+  size_t off[7];
+  return q8::moe_ws_layout(E, T, topk, F, M, off);
+}
+
+int q8_moe_ws_layout(int E, int T, int topk, int64_t F, int64_t M, size_t offsets[7]) {
+  if (!offsets) return Q8_ERR_NULL;
+  if (E < 1 || T < 1 || topk < 1 || topk > E || F < 0 || M < 0) return Q8_ERR_SHAPE;
+  q8::moe_ws_layout(E, T, topk, F, M, offsets);
+  return Q8_OK;
+}
+
+static q8::MoeWs moe_ws_ptrs(void* ws, int E, int T, int topk, int64_t F, int64_t M) {
+  size_t off[7];
+  q8::moe_ws_layout(E, T, topk, F, M, off);
+  char* b = (char*)ws;
+  q8::MoeWs w;
+  w.counts = (int32_t*)(b + off[0]);
+  w.offsets = (int32_t*)(b + off[1]);
+  w.pairs = (int32_t*)(b + off[2]);
+  w.active = (int32_t*)(b + off[3]);
+  w.n_active = (int32_t*)(b + off[4]);
+  w.h = F > 0 ? (float*)(b + off[5]) : nullptr;
+  w.y_pair = (float*)(b + off[6]);
+  return w;
+}
+
+static int check_routing(const int32_t* ids, const float* gate_w, int T, int topk, int E,
+                         bool need_gate) {
+  if (!ids || (need_gate && !gate_w)) return Q8_ERR_NULL;
+  if (T < 1 || topk < 1 || topk > E || (int64_t)T * topk > (1 << 20)) return Q8_ERR_SHAPE;
+  if (!aligned(ids, 4) || (gate_w && !aligned(gate_w, 4))) return Q8_ERR_ALIGN;
+  return Q8_OK;
+}
+
+int q8_moe_gemv(const q8_bank* W, const int32_t* expert_ids, const float* gate_w, const void* x,
+                int x_dt, int x_per_pair, float* y, int T, int topk, void* ws, size_t ws_bytes,
+                void* stream) {
+  int rc = check_bank(W);
+  if (rc) return rc;
+  if (W->E > 65535) return Q8_ERR_SHAPE;
+  rc = check_routing(expert_ids, gate_w, T, topk, W->E, false);
+  if (rc) return rc;
+  if (!x || !y) return Q8_ERR_NULL;
+  const size_t xs = dt_size(x_dt);
+  if (!xs) return Q8_ERR_DTYPE;
+  if (!aligned(x, 16) || !aligned(y, 4)) return Q8_ERR_ALIGN;
+  const int P = T * topk;
+  const int64_t M = W->e0.M, K = W->e0.K;
+  if (!ws || !aligned(ws, 16) || ws_bytes < q8_moe_ws_bytes(W->E, T, topk, 0, M))
+    return Q8_ERR_WORKSPACE;
+  const size_t xbytes = (size_t)(x_per_pair ? P : T) * K * xs;
+  const size_t ybytes = (size_t)(gate_w ? T : P) * M * 4;
+  if (overlap(x, xbytes, y, ybytes) || overlap(ws, ws_bytes, x, xbytes) ||
+      overlap(ws, ws_bytes, y, ybytes))
+    return Q8_ERR_ALIAS;
+  const DevInfo* dev = nullptr;
+  rc = current_device(&dev);
+  if (rc) return rc;
+  const bool xf = x_dt == Q8_DT_F32;
+  if (q8::max_tokens_per_pass(*dev, K, xf) < 8) return Q8_ERR_SHAPE;
+  q8::MoeWs w = moe_ws_ptrs(ws, W->E, T, topk, 0, M);
+  float* yp = gate_w ? w.y_pair : y;
+  hipStream_t s = (hipStream_t)stream;
+  if (q8::launch_moe_route(expert_ids, W->E, P, w, gate_w ? nullptr : y, M, s) != hipSuccess)
+    return Q8_ERR_LAUNCH;
+  if (q8::launch_moe_gemv(*dev, to_hb(W), w, P, topk, x, xf, x_per_pair != 0, yp, s) !=
+      hipSuccess)
+    return Q8_ERR_LAUNCH;
+  if (gate_w)
+    return launch_rc(q8::launch_moe_combine(expert_ids, W->E, gate_w, yp, y, T, topk, M, s));
+  return Q8_OK;
+}
+
+int q8_moe_ffn(const q8_bank* gate, const q8_bank* up, const q8_bank* down,
+               const int32_t* expert_ids, const float* gate_w, const void* x, int x_dt,
+               float* out, int T, int topk, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_bank(gate);
+  if (rc) return rc;
+  if ((rc = check_bank(up)) || (rc = check_bank(down))) return rc;
+  const int E = gate->E;
+  if (up->E != E || down->E != E || E > 65535) return Q8_ERR_SHAPE;
+  const int64_t F = gate->e0.M, H = gate->e0.K;
+  if (up->e0.M != F || up->e0.K != H || down->e0.M != H || down->e0.K != F) return Q8_ERR_SHAPE;
+  rc = check_routing(expert_ids, gate_w, T, topk, E, true);
+  if (rc) return rc;
+  if (!x || !out) return Q8_ERR_NULL;
+  const size_t xs = dt_size(x_dt);
+  if (!xs) return Q8_ERR_DTYPE;
+  if (!aligned(x, 16) || !aligned(out, 4)) return Q8_ERR_ALIGN;
+  if (!ws || !aligned(ws, 16) || ws_bytes < q8_moe_ws_bytes(E, T, topk, F, H))
+    return Q8_ERR_WORKSPACE;
+  const size_t xbytes = (size_t)T * H * xs, obytes = (size_t)T * H * 4;
+  if (overlap(x, xbytes, out, obytes) || overlap(ws, ws_bytes, x, xbytes) ||
+      overlap(ws, ws_bytes, out, obytes))
+    return Q8_ERR_ALIAS;
+  const DevInfo* dev = nullptr;
+  rc = current_device(&dev);
+  if (rc) return rc;
+  const bool xf = x_dt == Q8_DT_F32;
+  if (q8::max_tokens_per_pass(*dev, H, xf) < 8 || q8::max_tokens_per_pass(*dev, F, true) < 8)
+    return Q8_ERR_SHAPE;
+  const int P = T * topk;
+  q8::MoeWs w = moe_ws_ptrs(ws, E, T, topk, F, H);
+  hipStream_t s = (hipStream_t)stream;
+  if (q8::launch_moe_route(expert_ids, E, P, w, nullptr, 0, s) != hipSuccess) return Q8_ERR_LAUNCH;
+  if (q8::launch_moe_gate_up(*dev, to_hb(gate), to_hb(up), w, P, topk, x, xf, w.h, s) !=
+      hipSuccess)
+    return Q8_ERR_LAUNCH;
+  if (q8::launch_moe_gemv(*dev, to_hb(down), w, P, topk, w.h, true, true, w.y_pair, s) !=
+      hipSuccess)
+    return Q8_ERR_LAUNCH;
+  return launch_rc(q8::launch_moe_combine(expert_ids, E, gate_w, w.y_pair, out, T, topk, H, s));
+}
+
+}  // extern "C"

@@ -1,0 +1,83 @@
+// q8_internal.h -- host-side interface between the C ABI (q8_api.cpp) and
+// the kernel launchers (*.hip). Arguments here are already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace q8 {
+
+struct DevInfo {
+  int device;
+  int cus;             // compute units
+  size_t lds_per_block;  // bytes of dynamic LDS a workgroup may use
+  bool gfx950;
+};
+
+struct HMat {  // host view of one packed matrix
+  const int8_t* qs;
+  const uint16_t* d;
+  int64_t M, K, ld_qs, ld_d;
+};
+
+struct HBank {
+  HMat e0;
+  int64_t stride_qs, stride_d;
+  int E;
+};
+
+// Lanes per row team for a given K (K only: keeps per-token results
+// independent of N and of the kernel that runs the row).
+int lanes_per_row(int64_t K);
+
+// LDS bytes for x of one pass of nt tokens of K activations.
+inline size_t x_lds_bytes(int nt, int64_t K, bool x_f32) {
+  return (size_t)nt * (size_t)K * (x_f32 ? 4 : 2);
+}
+
+// Largest token count per pass that fits the LDS limit (<= 8), 0 if none.
+int max_tokens_per_pass(const DevInfo& dev, int64_t K, bool x_f32);
+
+// y[n] = A x[n] (and yb[n] = B x[n] when B != nullptr) for nt <= 8 tokens.
+hipError_t launch_gemv(const DevInfo& dev, const HMat& A, const HMat* B, const void* x,
+                       bool x_f32, int64_t ldx, void* ya, void* yb, bool y_f16, int nt,
+                       hipStream_t s);
+
+// LM head pass: logits (may be null), per-workgroup partial argmax keys into
+// keys [n_blocks][nt]; then the final reduction writes ids [nt].
+int lmhead_blocks(const DevInfo& dev, int64_t V);
+hipError_t launch_lmhead(const DevInfo& dev, const HMat& W, const void* x, bool x_f32,
+                         float* logits, int64_t ld_logits, int32_t* ids, uint64_t* keys,
+                         int nt, hipStream_t s);
+
+// Routed experts.
+struct MoeWs {
+  int32_t* counts;   // [E]
+  int32_t* offsets;  // [E+1]
+  int32_t* pairs;    // [P]
+  int32_t* active;   // [E]
+  int32_t* n_active; // [1]
+  float* h;          // [P][F] or null
+  float* y_pair;     // [P][Mout] or null
+};
+
+size_t moe_ws_layout(int E, int T, int topk, int64_t F, int64_t M, size_t off[7]);
+
+hipError_t launch_moe_route(const int32_t* ids, int E, int P, const MoeWs& ws, float* zero_rows,
+                            int64_t zero_ld, hipStream_t s);
+// Routed GEMV over a bank: y_pair[p] = W[e_p] x[src(p)]; src(p) = p / topk
+// (x_per_pair false) or p. x fp16 or fp32.
+hipError_t launch_moe_gemv(const DevInfo& dev, const HBank& W, const MoeWs& ws, int P, int topk,
+                           const void* x, bool x_f32, bool x_per_pair, float* y_pair,
+                           hipStream_t s);
+// h[p] = silu(Wg[e_p] x_t) * (Wu[e_p] x_t), x fp16 [T][H].
+hipError_t launch_moe_gate_up(const DevInfo& dev, const HBank& G, const HBank& U,
+                              const MoeWs& ws, int P, int topk, const void* x, bool x_f32,
+                              float* h, hipStream_t s);
+// out[t] = sum_j gate_w[t][j] * y_pair[t*topk + j] (slots with invalid ids skipped).
+hipError_t launch_moe_combine(const int32_t* ids, int E, const float* gate_w,
+                              const float* y_pair, float* out, int T, int topk, int64_t M,
+                              hipStream_t s);
+
+}  // namespace q8

@@ -1,0 +1,178 @@
+"""Host-side tests of the C ABI: no kernel is launched here.
+
+* the library loads and exports every function include/q8gemv.h declares;
+* the load-time packer round-trips GGUF Q8_0 blocks byte for byte and
+  writes 16-byte-aligned rows with zero padding;
+* every synchronous validation error is reachable with bad arguments (the
+  pointers are never dereferenced because validation fails first).
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import quantized_weight_gemv_q8_amd as q8
+from quantized_weight_gemv_q8_amd import synth
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
+                      "q8gemv.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(q8.LIB_PATH):
+        from quantized_weight_gemv_q8_amd import build
+        build.build()
+    return q8.lib()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(q8_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_declares_the_binding_exports():
+    assert declared_functions() == sorted(q8.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(L):
+    for name in declared_functions():
+        assert hasattr(L, name), name
+    # and they are real dynamic symbols of the shared object
+    nm = os.popen(f"nm -D --defined-only {q8.LIB_PATH}").read()
+    for name in declared_functions():
+        assert re.search(rf"\bT {name}\b", nm), name
+
+
+def test_status_strings(L):
+    for code in range(0, -9, -1):
+        s = q8.status_str(code)
+        assert s and s != "unknown status"
+    assert q8.status_str(5) == "unknown status"
+
+
+@pytest.mark.parametrize("M,K", [(1, 32), (3, 96), (17, 1024), (5, 5120), (2, 768)])
+def test_pack_roundtrip_and_layout(L, M, K):
+    c = synth.gemv_case(M, K, 1, seed=M + K)
+    c.q[0, :32] = -128  # extremes
+    c.d[0, 0] = np.float16(0.0)
+    blocks = synth.to_gguf_blocks(c.q, c.d)
+    ld_qs, ld_d, qb, db = q8.pack_layout(M, K)
+    assert ld_qs == K and ld_qs % 16 == 0
+    assert ld_d >= K // 32 and ld_d % 8 == 0 and ld_d - K // 32 < 8
+    assert qb == M * ld_qs and db == 2 * M * ld_d
+    qs, d = q8.pack_host(blocks)
+    assert np.array_equal(qs[:, :K], c.q)
+    assert np.array_equal(d[:, :K // 32], c.d.view(np.uint16))
+    assert np.all(d[:, K // 32:] == 0)
+    back = q8.unpack_host(qs, d, M, K)
+    assert back.tobytes() == blocks.tobytes()
+
+
+def _mat(qs=0x10000, d=0x20000, M=64, K=256, ld_qs=None, ld_d=None):
+    ld_d = (K // 32 + 7) // 8 * 8 if ld_d is None else ld_d
+    return q8._Matrix(qs, d, M, K, K if ld_qs is None else ld_qs, ld_d)
+
+
+def _bank(m, E):
+    return q8._Bank(m, m.M * m.ld_qs, m.M * m.ld_d, E)
+
+
+X, Y, WS = 0x100000, 0x200000, 0x300000
+
+
+def gemv_rc(L, W=None, x=X, xdt=1, y=Y, ydt=2, N=1):
+    W = _mat() if W is None else W
+    return L.q8_gemv(ctypes.byref(W), x, xdt, y, ydt, N, None)
+
+
+def test_gemv_validation(L):
+    assert L.q8_gemv(None, X, 1, Y, 2, 1, None) == -1
+    assert gemv_rc(L, W=_mat(qs=0)) == -1
+    assert gemv_rc(L, x=0) == -1
+    assert gemv_rc(L, y=0) == -1
+    assert gemv_rc(L, W=_mat(M=0)) == -2
+    assert gemv_rc(L, W=_mat(K=48, ld_qs=48, ld_d=8)) == -2
+    assert gemv_rc(L, W=_mat(K=0)) == -2
+    assert gemv_rc(L, W=_mat(ld_qs=128)) == -2
+    assert gemv_rc(L, W=_mat(ld_d=2)) == -2
+    assert gemv_rc(L, N=0) == -2
+    assert gemv_rc(L, W=_mat(ld_qs=264)) == -3
+    assert gemv_rc(L, W=_mat(ld_d=9)) == -3
+    assert gemv_rc(L, W=_mat(qs=0x10008)) == -3
+    assert gemv_rc(L, W=_mat(d=0x20002)) == -3
+    assert gemv_rc(L, x=X + 8) == -3
+    assert gemv_rc(L, y=Y + 2) == -3
+    assert gemv_rc(L, xdt=3) == -4
+    assert gemv_rc(L, ydt=0) == -4
+    assert gemv_rc(L, y=X + 64) == -8  # y inside x's [N][K] range
+    assert L.q8_gemv_pair(ctypes.byref(_mat()), None, X, 1, Y, Y + 4096, 2, 1, None) == -1
+    W2 = _mat(K=512, ld_qs=512, ld_d=16)
+    assert L.q8_gemv_pair(ctypes.byref(_mat()), ctypes.byref(W2), X, 1, Y, Y + 4096, 2, 1, None) == -2
+    assert L.q8_gemv_pair(ctypes.byref(_mat()), ctypes.byref(_mat()), X, 1, Y, Y + 16, 2, 1, None) == -8
+
+
+def test_lmhead_validation(L):
+    W = _mat()
+    n = L.q8_lmhead_ws_bytes(64, 1)
+    assert n > 0
+    ok = dict(x=X, xdt=1, logits=Y, ids=Y + 0x10000, N=1, ws=WS, nws=n)
+
+    def rc(**kw):
+        a = dict(ok, **kw)
+        return L.q8_lmhead_argmax(ctypes.byref(W), a["x"], a["xdt"], a["logits"], a["ids"], a["N"],
+                                  a["ws"], a["nws"], None)
+    assert rc(ids=0) == -1
+    assert rc(N=0) == -2
+    assert rc(xdt=7) == -4
+    assert rc(ws=0) == -5
+    assert rc(nws=n - 1) == -5
+    assert rc(ws=WS + 4) == -5
+    assert rc(ids=Y + 2) == -3
+    assert rc(ids=Y) == -8  # ids inside logits
+
+
+def test_moe_validation(L):
+    E, T, topk, F, H = 8, 4, 2, 64, 128
+    g = _bank(_mat(M=F, K=H), E)
+    u = _bank(_mat(qs=0x40000, d=0x50000, M=F, K=H), E)
+    dn = _bank(_mat(qs=0x60000, d=0x70000, M=H, K=F), E)
+    n = L.q8_moe_ws_bytes(E, T, topk, F, H)
+    assert n > 0
+    off = (ctypes.c_size_t * 7)()
+    assert L.q8_moe_ws_layout(E, T, topk, F, H, off) == 0
+    assert list(off) == sorted(off) and all(o % 256 == 0 for o in off)
+    assert L.q8_moe_ws_layout(E, T, E + 1, F, H, off) == -2
+    IDS, GW, XX, OUT = 0x800000, 0x810000, 0x820000, 0x900000
+
+    def rc(gate=g, up=u, down=dn, ids=IDS, gw=GW, x=XX, xdt=1, out=OUT, T_=T, k=topk, ws=WS, nws=n):
+        return L.q8_moe_ffn(ctypes.byref(gate), ctypes.byref(up), ctypes.byref(down), ids, gw, x, xdt,
+                            out, T_, k, ws, nws, None)
+    assert rc(ids=0) == -1
+    assert rc(gw=0) == -1
+    assert rc(k=E + 1) == -2
+    assert rc(T_=0) == -2
+    bad_down = _bank(_mat(qs=0x60000, d=0x70000, M=H, K=2 * F), E)
+    assert rc(down=bad_down) == -2
+    bad_e = _bank(_mat(qs=0x40000, d=0x50000, M=F, K=H), E - 1)
+    assert rc(up=bad_e) == -2
+    assert rc(xdt=9) == -4
+    assert rc(nws=n - 1) == -5
+    assert rc(ids=IDS + 2) == -3
+    assert rc(out=XX) == -8
+    # routed GEMV
+    n1 = L.q8_moe_ws_bytes(E, T, topk, 0, F)
+    assert L.q8_moe_gemv(ctypes.byref(g), IDS, None, XX, 1, 0, OUT, T, topk, WS, n1 - 1, None) == -5
+    assert L.q8_moe_gemv(ctypes.byref(g), IDS, None, XX, 1, 0, 0, T, topk, WS, n1, None) == -1
+    bad_stride = q8._Bank(g.e0, g.stride_qs - 16, g.stride_d, E)
+    assert L.q8_moe_gemv(ctypes.byref(bad_stride), IDS, None, XX, 1, 0, OUT, T, topk, WS, n1, None) == -2
+
+
+def test_valid_call_without_gfx950_is_refused(L):
+    if L.q8_device_check(0) == 0:
+        pytest.skip("a gfx950 device is present; this check is for hosts without one")
+    assert gemv_rc(L) == -6
+    assert L.q8_device_check(0) == -6
