@@ -294,7 +294,7 @@ static q8::MoeWs moe_ws_ptrs(void* ws, int E, int T, int topk, int64_t F, int64_
 static int check_routing(const int32_t* ids, const float* gate_w, int T, int topk, int E,
                          bool need_gate) {
   if (!ids || (need_gate && !gate_w)) return Q8_ERR_NULL;
-  if (T < 1 || topk < 1 || topk > E || (int64_t)T * topk > (1 << 20)) return Q8_ERR_SHAPE;
+  if (T < 1 || topk < 1 || topk > E || (int64_t)T * topk > 8192) return Q8_ERR_SHAPE;
   if (!aligned(ids, 4) || (gate_w && !aligned(gate_w, 4))) return Q8_ERR_ALIGN;
   return Q8_OK;
 }
@@ -304,7 +304,7 @@ int q8_moe_gemv(const q8_bank* W, const int32_t* expert_ids, const float* gate_w
                 void* stream) {
   int rc = check_bank(W);
   if (rc) return rc;
-  if (W->E > 65535) return Q8_ERR_SHAPE;
+  if (W->E > 4096) return Q8_ERR_SHAPE;
   rc = check_routing(expert_ids, gate_w, T, topk, W->E, false);
   if (rc) return rc;
   if (!x || !y) return Q8_ERR_NULL;
@@ -324,7 +324,7 @@ int q8_moe_gemv(const q8_bank* W, const int32_t* expert_ids, const float* gate_w
   rc = current_device(&dev);
   if (rc) return rc;
   const bool xf = x_dt == Q8_DT_F32;
-  if (q8::max_tokens_per_pass(*dev, K, xf) < 8) return Q8_ERR_SHAPE;
+  if (q8::max_tokens_per_pass(*dev, K, xf) < 4) return Q8_ERR_SHAPE;
   q8::MoeWs w = moe_ws_ptrs(ws, W->E, T, topk, 0, M);
   float* yp = gate_w ? w.y_pair : y;
   hipStream_t s = (hipStream_t)stream;
@@ -345,7 +345,7 @@ int q8_moe_ffn(const q8_bank* gate, const q8_bank* up, const q8_bank* down,
   if (rc) return rc;
   if ((rc = check_bank(up)) || (rc = check_bank(down))) return rc;
   const int E = gate->E;
-  if (up->E != E || down->E != E || E > 65535) return Q8_ERR_SHAPE;
+  if (up->E != E || down->E != E || E > 4096) return Q8_ERR_SHAPE;
   const int64_t F = gate->e0.M, H = gate->e0.K;
   if (up->e0.M != F || up->e0.K != H || down->e0.M != H || down->e0.K != F) return Q8_ERR_SHAPE;
   rc = check_routing(expert_ids, gate_w, T, topk, E, true);
@@ -364,7 +364,7 @@ int q8_moe_ffn(const q8_bank* gate, const q8_bank* up, const q8_bank* down,
   rc = current_device(&dev);
   if (rc) return rc;
   const bool xf = x_dt == Q8_DT_F32;
-  if (q8::max_tokens_per_pass(*dev, H, xf) < 8 || q8::max_tokens_per_pass(*dev, F, true) < 8)
+  if (q8::max_tokens_per_pass(*dev, H, xf) < 4 || q8::max_tokens_per_pass(*dev, F, true) < 4)
     return Q8_ERR_SHAPE;
   const int P = T * topk;
   q8::MoeWs w = moe_ws_ptrs(ws, E, T, topk, F, H);

@@ -6,27 +6,33 @@
 // reused from LDS for all rows (memra wiki, feature list: Q8_0 decode
 // matvecs with per-shape auto-dispatch; here the shape picks the lanes per
 // row and the token count picks the rows per team).
+#include <map>
+#include <mutex>
+#include <utility>
+
 #include "q8_engine.hpp"
 #include "q8_internal.h"
 
 namespace q8 {
 
+// Rows [0, Ma) come from matrix A, rows [Ma, Mtot) from matrix B (the pair).
+// Scalar fields and explicit selects: a struct-member select here was
+// lowered to a private-memory array.
 struct DenseMap {
-  MatDesc a, b;
+  const int8_t* qa;
+  const uint16_t* da;
+  const int8_t* qb;
+  const uint16_t* db;
+  int64_t ldqa, ldda, ldqb, lddb;
   int64_t Ma, Mtot;
   __device__ __forceinline__ bool row(int64_t i, const int8_t*& q, const uint16_t*& d) const {
-    q = a.qs;
-    d = a.d;
-    if (i >= Mtot) return false;
-    if (i < Ma) {
-      q = a.qs + i * a.ld_qs;
-      d = a.d + i * a.ld_d;
-    } else {
-      const int64_t k = i - Ma;
-      q = b.qs + k * b.ld_qs;
-      d = b.d + k * b.ld_d;
-    }
-    return true;
+    const bool second = i >= Ma;
+    const int64_t k = second ? i - Ma : i;
+    const int64_t ldq = second ? ldqb : ldqa;
+    const int64_t ldd = second ? lddb : ldda;
+    q = (second ? qb : qa) + k * ldq;
+    d = (second ? db : da) + k * ldd;
+    return i < Mtot;
   }
 };
 
@@ -55,67 +61,80 @@ struct DenseEpi {
   }
 };
 
-template <int NT>
-struct RowsPerTeam {
-  static constexpr int value = NT <= 2 ? 2 : 4;
-};
-
-template <int NT, int LPR, bool XF32>
+template <int NT, int LPR, bool XF32, bool BIG>
 __global__ __launch_bounds__(kBlock) void gemv_kernel(DenseMap map, DenseEpi epi, const char* x,
                                                       int64_t ldx_bytes, int C) {
   extern __shared__ uint4 lds_x[];
-  constexpr int R = RowsPerTeam<NT>::value;
-  constexpr int G = (kWave / LPR) * R;
-  const char* rows[NT];
-#pragma unroll
-  for (int n = 0; n < NT; ++n) rows[n] = x + n * ldx_bytes;
-  stage_x<NT, XF32>(rows, C, lds_x);
-  __syncthreads();
+  using T = Tune<NT, BIG>;
+  constexpr int G = (kWave / LPR) * T::R;
   const int64_t n_groups = (map.Mtot + G - 1) / G;
   const int wave = threadIdx.x / kWave;
-  run_rows<NT, LPR, R, 1, XF32>(map, epi, lds_x, C, n_groups,
-                                (int64_t)blockIdx.x * kWavesPerBlock + wave,
-                                (int64_t)gridDim.x * kWavesPerBlock, 0);
+  auto stage = [=]() {
+    const char* rows[NT];
+#pragma unroll
+    for (int n = 0; n < NT; ++n) rows[n] = x + n * ldx_bytes;
+    stage_x<NT, XF32>(rows, C, lds_x);
+    __syncthreads();
+  };
+  run_rows<NT, LPR, T::R, T::D, 1, XF32>(map, epi, lds_x, C, n_groups,
+                                         (int64_t)blockIdx.x * kWavesPerBlock + wave,
+                                         (int64_t)gridDim.x * kWavesPerBlock, 0, stage);
 }
 
-template <int NT, int LPR, bool XF32>
+template <int NT, int LPR, bool XF32, bool BIG>
 static hipError_t launch_t(const DevInfo& dev, DenseMap map, DenseEpi epi, const char* x,
                            int64_t ldx_bytes, int C, hipStream_t s) {
-  constexpr int R = RowsPerTeam<NT>::value;
-  constexpr int G = (kWave / LPR) * R;
+  constexpr int G = (kWave / LPR) * Tune<NT, BIG>::R;
   const size_t lds = (size_t)NT * C * 16 * XPlanes<XF32>::P;
   const int64_t n_groups = (map.Mtot + G - 1) / G;
   const int64_t need = (n_groups + kWavesPerBlock - 1) / kWavesPerBlock;
-  int64_t per_cu = lds ? (int64_t)(160 * 1024 / lds) : 4;
-  if (per_cu < 1) per_cu = 1;
-  if (per_cu > 4) per_cu = 4;
-  int64_t blocks = (int64_t)dev.cus * per_cu;
-  if (blocks > need) blocks = need;
-  if (blocks < 1) blocks = 1;
-  auto fn = gemv_kernel<NT, LPR, XF32>;
+  auto fn = gemv_kernel<NT, LPR, XF32, BIG>;
   if (lds > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize,
                                        (int)lds);
     if (e != hipSuccess) return e;
   }
+  int64_t blocks = (int64_t)dev.cus * blocks_per_cu((const void*)fn, lds);
+  if (blocks > need) blocks = need;
+  if (blocks < 1) blocks = 1;
   void* args[] = {&map, &epi, (void*)&x, &ldx_bytes, &C};
   return hipLaunchKernel((const void*)fn, dim3((unsigned)blocks), dim3(kBlock), args, lds, s);
+}
+
+template <int NT, int LPR, bool XF32>
+static hipError_t launch_sz(const DevInfo& dev, DenseMap map, DenseEpi epi, const char* x,
+                            int64_t ldx_bytes, int C, hipStream_t s) {
+  if (map.Mtot >= kBigRows) return launch_t<NT, LPR, XF32, true>(dev, map, epi, x, ldx_bytes, C, s);
+  return launch_t<NT, LPR, XF32, false>(dev, map, epi, x, ldx_bytes, C, s);
 }
 
 template <int LPR, bool XF32>
 static hipError_t launch_nt(const DevInfo& dev, int nt, DenseMap map, DenseEpi epi, const char* x,
                             int64_t ldx_bytes, int C, hipStream_t s) {
   switch (nt) {
-    case 1: return launch_t<1, LPR, XF32>(dev, map, epi, x, ldx_bytes, C, s);
-    case 2: return launch_t<2, LPR, XF32>(dev, map, epi, x, ldx_bytes, C, s);
-    case 3: return launch_t<3, LPR, XF32>(dev, map, epi, x, ldx_bytes, C, s);
-    case 4: return launch_t<4, LPR, XF32>(dev, map, epi, x, ldx_bytes, C, s);
-    case 5: return launch_t<5, LPR, XF32>(dev, map, epi, x, ldx_bytes, C, s);
-    case 6: return launch_t<6, LPR, XF32>(dev, map, epi, x, ldx_bytes, C, s);
-    case 7: return launch_t<7, LPR, XF32>(dev, map, epi, x, ldx_bytes, C, s);
-    case 8: return launch_t<8, LPR, XF32>(dev, map, epi, x, ldx_bytes, C, s);
+    case 1: return launch_sz<1, LPR, XF32>(dev, map, epi, x, ldx_bytes, C, s);
+    case 2: return launch_t<2, LPR, XF32, false>(dev, map, epi, x, ldx_bytes, C, s);
+    case 3: return launch_t<3, LPR, XF32, false>(dev, map, epi, x, ldx_bytes, C, s);
+    case 4: return launch_t<4, LPR, XF32, false>(dev, map, epi, x, ldx_bytes, C, s);
+    case 5: return launch_t<5, LPR, XF32, false>(dev, map, epi, x, ldx_bytes, C, s);
+    case 6: return launch_t<6, LPR, XF32, false>(dev, map, epi, x, ldx_bytes, C, s);
+    case 7: return launch_t<7, LPR, XF32, false>(dev, map, epi, x, ldx_bytes, C, s);
+    case 8: return launch_t<8, LPR, XF32, false>(dev, map, epi, x, ldx_bytes, C, s);
   }
   return hipErrorInvalidValue;
+}
+
+int blocks_per_cu(const void* fn, size_t lds) {
+  static std::mutex mu;
+  static std::map<std::pair<const void*, size_t>, int> cache;
+  std::lock_guard<std::mutex> lock(mu);
+  auto key = std::make_pair(fn, lds);
+  auto it = cache.find(key);
+  if (it != cache.end()) return it->second;
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, kBlock, lds) != hipSuccess || n < 1) n = 1;
+  cache[key] = n;
+  return n;
 }
 
 int lanes_per_row(int64_t K) {
@@ -140,8 +159,14 @@ hipError_t launch_gemv(const DevInfo& dev, const HMat& A, const HMat* B, const v
                        bool x_f32, int64_t ldx, void* ya, void* yb, bool y_f16, int nt,
                        hipStream_t s) {
   DenseMap map;
-  map.a = MatDesc{A.qs, A.d, A.ld_qs, A.ld_d};
-  map.b = B ? MatDesc{B->qs, B->d, B->ld_qs, B->ld_d} : map.a;
+  map.qa = A.qs;
+  map.da = A.d;
+  map.ldqa = A.ld_qs;
+  map.ldda = A.ld_d;
+  map.qb = B ? B->qs : A.qs;
+  map.db = B ? B->d : A.d;
+  map.ldqb = B ? B->ld_qs : A.ld_qs;
+  map.lddb = B ? B->ld_d : A.ld_d;
   map.Ma = A.M;
   map.Mtot = A.M + (B ? B->M : 0);
   DenseEpi epi;

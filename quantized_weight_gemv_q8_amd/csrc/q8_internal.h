@@ -31,6 +31,11 @@ struct HBank {
 // independent of N and of the kernel that runs the row).
 int lanes_per_row(int64_t K);
 
+// Resident workgroups of kernel `fn` per compute unit at `lds` bytes of
+// dynamic LDS (kBlock threads), from the runtime's occupancy calculator;
+// cached per (kernel, lds). Persistent grids launch cus * this many blocks.
+int blocks_per_cu(const void* fn, size_t lds);
+
 // LDS bytes for x of one pass of nt tokens of K activations.
 inline size_t x_lds_bytes(int nt, int64_t K, bool x_f32) {
   return (size_t)nt * (size_t)K * (x_f32 ? 4 : 2);

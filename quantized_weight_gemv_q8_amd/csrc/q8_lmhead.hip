@@ -80,22 +80,17 @@ struct LmEpi {
   }
 };
 
-template <int NT, int LPR, bool XF32>
+template <int NT, int LPR, bool XF32, bool BIG>
 __global__ __launch_bounds__(kBlock) void lmhead_kernel(LmMap map, float* logits, int64_t ld,
                                                         const char* x, int64_t ldx_bytes, int C,
                                                         uint64_t* keys) {
   extern __shared__ uint4 lds_x[];
   __shared__ uint64_t red[kWavesPerBlock][kMaxNT];
-  constexpr int R = NT <= 2 ? 2 : 4;
+  using T = Tune<NT, BIG>;
+  constexpr int R = T::R;
   constexpr int G = (kWave / LPR) * R;
   constexpr int VP = Pow2<NT * R>::value;
   constexpr int CNT = ReduceShape<LPR, VP, 1>::CNT;
-
-  const char* rows[NT];
-#pragma unroll
-  for (int n = 0; n < NT; ++n) rows[n] = x + n * ldx_bytes;
-  stage_x<NT, XF32>(rows, C, lds_x);
-  __syncthreads();
 
   LmEpi<CNT> epi;
   epi.logits = logits;
@@ -105,9 +100,16 @@ __global__ __launch_bounds__(kBlock) void lmhead_kernel(LmMap map, float* logits
   const int64_t n_groups = (map.V + G - 1) / G;
   const int wave = threadIdx.x / kWave;
   const int lane = threadIdx.x % kWave;
-  run_rows<NT, LPR, R, 1, XF32>(map, epi, lds_x, C, n_groups,
-                                (int64_t)blockIdx.x * kWavesPerBlock + wave,
-                                (int64_t)gridDim.x * kWavesPerBlock, 0);
+  auto stage = [=]() {
+    const char* rows[NT];
+#pragma unroll
+    for (int n = 0; n < NT; ++n) rows[n] = x + n * ldx_bytes;
+    stage_x<NT, XF32>(rows, C, lds_x);
+    __syncthreads();
+  };
+  run_rows<NT, LPR, R, T::D, 1, XF32>(map, epi, lds_x, C, n_groups,
+                                      (int64_t)blockIdx.x * kWavesPerBlock + wave,
+                                      (int64_t)gridDim.x * kWavesPerBlock, 0, stage);
 
 #pragma unroll
   for (int n = 0; n < NT; ++n) {
@@ -138,44 +140,45 @@ __global__ __launch_bounds__(kBlock) void lmhead_kernel(LmMap map, float* logits
   }
 }
 
-__global__ __launch_bounds__(256) void lmhead_final_kernel(const uint64_t* keys, int nblocks, int nt,
-                                                          int32_t* ids) {
-  __shared__ uint64_t red[256];
-  for (int n = 0; n < nt; ++n) {
-    uint64_t k = 0;
-    for (int b = threadIdx.x; b < nblocks; b += blockDim.x) {
-      const uint64_t o = keys[(int64_t)b * nt + n];
-      k = o > k ? o : k;
-    }
-    red[threadIdx.x] = k;
-    __syncthreads();
-    for (int s = blockDim.x / 2; s > 0; s >>= 1) {
-      if (threadIdx.x < s) {
-        const uint64_t o = red[threadIdx.x + s];
-        if (o > red[threadIdx.x]) red[threadIdx.x] = o;
-      }
-      __syncthreads();
-    }
-    if (threadIdx.x == 0) ids[n] = (int32_t)(~(uint32_t)(red[0] & 0xffffffffu));
-    __syncthreads();
-  }
-}
+// One workgroup: maximum key per token over the per-workgroup slots,
+// decoded to the row index.
+constexpr int kFinalThreads = 1024;
 
-template <int NT, int LPR, bool XF32>
-static int64_t lm_blocks_t(const DevInfo& dev, int64_t V, int C) {
-  constexpr int R = NT <= 2 ? 2 : 4;
-  constexpr int G = (kWave / LPR) * R;
-  const size_t lds = (size_t)NT * C * 16 * XPlanes<XF32>::P;
-  const int64_t n_groups = (V + G - 1) / G;
-  const int64_t need = (n_groups + kWavesPerBlock - 1) / kWavesPerBlock;
-  int64_t per_cu = lds ? (int64_t)(160 * 1024 / lds) : 4;
-  if (per_cu < 1) per_cu = 1;
-  if (per_cu > 4) per_cu = 4;
-  int64_t blocks = (int64_t)dev.cus * per_cu;
-  if (blocks > need) blocks = need;
-  if (blocks > kLmMaxBlocks) blocks = kLmMaxBlocks;
-  if (blocks < 1) blocks = 1;
-  return blocks;
+__global__ __launch_bounds__(kFinalThreads) void lmhead_final_kernel(const uint64_t* keys,
+                                                                    int nblocks, int nt,
+                                                                    int32_t* ids) {
+  __shared__ uint64_t red[kFinalThreads / kWave][kMaxNT];
+  uint64_t k[kMaxNT];
+#pragma unroll
+  for (int n = 0; n < kMaxNT; ++n) k[n] = 0;
+  for (int b = threadIdx.x; b < nblocks; b += blockDim.x) {
+#pragma unroll
+    for (int n = 0; n < kMaxNT; ++n) {
+      if (n < nt) {
+        const uint64_t o = keys[(int64_t)b * nt + n];
+        k[n] = o > k[n] ? o : k[n];
+      }
+    }
+  }
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+#pragma unroll
+  for (int n = 0; n < kMaxNT; ++n) {
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1) {
+      const uint64_t o = __shfl_xor(k[n], off, kWave);
+      k[n] = o > k[n] ? o : k[n];
+    }
+    if (lane == 0) red[wave][n] = k[n];
+  }
+  __syncthreads();
+  if (threadIdx.x < nt) {
+    uint64_t m = 0;
+    for (int w = 0; w < (int)(blockDim.x / kWave); ++w) {
+      const uint64_t o = red[w][threadIdx.x];
+      m = o > m ? o : m;
+    }
+    ids[threadIdx.x] = (int32_t)(~(uint32_t)(m & 0xffffffffu));
+  }
 }
 
 int lmhead_blocks(const DevInfo& dev, int64_t V) {
@@ -184,25 +187,32 @@ int lmhead_blocks(const DevInfo& dev, int64_t V) {
   return kLmMaxBlocks;
 }
 
-template <int NT, int LPR, bool XF32>
+template <int NT, int LPR, bool XF32, bool BIG>
 static hipError_t lm_launch_t(const DevInfo& dev, LmMap map, float* logits, int64_t ld,
                               const char* x, int64_t ldx_bytes, int C, uint64_t* keys,
                               int32_t* ids, hipStream_t s) {
+  constexpr int G = (kWave / LPR) * Tune<NT, BIG>::R;
   const size_t lds = (size_t)NT * C * 16 * XPlanes<XF32>::P;
-  const int64_t blocks = lm_blocks_t<NT, LPR, XF32>(dev, map.V, C);
-  auto fn = lmhead_kernel<NT, LPR, XF32>;
+  auto fn = lmhead_kernel<NT, LPR, XF32, BIG>;
   if (lds > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize,
                                        (int)lds);
     if (e != hipSuccess) return e;
   }
+  const int64_t n_groups = (map.V + G - 1) / G;
+  const int64_t need = (n_groups + kWavesPerBlock - 1) / kWavesPerBlock;
+  int64_t blocks = (int64_t)dev.cus * blocks_per_cu((const void*)fn, lds);
+  if (blocks > need) blocks = need;
+  if (blocks > kLmMaxBlocks) blocks = kLmMaxBlocks;
+  if (blocks < 1) blocks = 1;
   void* args[] = {&map, &logits, &ld, (void*)&x, &ldx_bytes, &C, &keys};
   hipError_t e = hipLaunchKernel((const void*)fn, dim3((unsigned)blocks), dim3(kBlock), args, lds, s);
   if (e != hipSuccess) return e;
   int nb = (int)blocks;
   int nt = NT;
   void* fargs[] = {&keys, &nb, &nt, &ids};
-  return hipLaunchKernel((const void*)lmhead_final_kernel, dim3(1), dim3(256), fargs, 0, s);
+  return hipLaunchKernel((const void*)lmhead_final_kernel, dim3(1), dim3(kFinalThreads), fargs, 0,
+                         s);
 }
 
 template <int LPR, bool XF32>
@@ -210,14 +220,17 @@ static hipError_t lm_launch_nt(const DevInfo& dev, int nt, LmMap map, float* log
                                const char* x, int64_t ldx_bytes, int C, uint64_t* keys,
                                int32_t* ids, hipStream_t s) {
   switch (nt) {
-    case 1: return lm_launch_t<1, LPR, XF32>(dev, map, logits, ld, x, ldx_bytes, C, keys, ids, s);
-    case 2: return lm_launch_t<2, LPR, XF32>(dev, map, logits, ld, x, ldx_bytes, C, keys, ids, s);
-    case 3: return lm_launch_t<3, LPR, XF32>(dev, map, logits, ld, x, ldx_bytes, C, keys, ids, s);
-    case 4: return lm_launch_t<4, LPR, XF32>(dev, map, logits, ld, x, ldx_bytes, C, keys, ids, s);
-    case 5: return lm_launch_t<5, LPR, XF32>(dev, map, logits, ld, x, ldx_bytes, C, keys, ids, s);
-    case 6: return lm_launch_t<6, LPR, XF32>(dev, map, logits, ld, x, ldx_bytes, C, keys, ids, s);
-    case 7: return lm_launch_t<7, LPR, XF32>(dev, map, logits, ld, x, ldx_bytes, C, keys, ids, s);
-    case 8: return lm_launch_t<8, LPR, XF32>(dev, map, logits, ld, x, ldx_bytes, C, keys, ids, s);
+    case 1:
+      if (map.V >= kBigRows)
+        return lm_launch_t<1, LPR, XF32, true>(dev, map, logits, ld, x, ldx_bytes, C, keys, ids, s);
+      return lm_launch_t<1, LPR, XF32, false>(dev, map, logits, ld, x, ldx_bytes, C, keys, ids, s);
+    case 2: return lm_launch_t<2, LPR, XF32, false>(dev, map, logits, ld, x, ldx_bytes, C, keys, ids, s);
+    case 3: return lm_launch_t<3, LPR, XF32, false>(dev, map, logits, ld, x, ldx_bytes, C, keys, ids, s);
+    case 4: return lm_launch_t<4, LPR, XF32, false>(dev, map, logits, ld, x, ldx_bytes, C, keys, ids, s);
+    case 5: return lm_launch_t<5, LPR, XF32, false>(dev, map, logits, ld, x, ldx_bytes, C, keys, ids, s);
+    case 6: return lm_launch_t<6, LPR, XF32, false>(dev, map, logits, ld, x, ldx_bytes, C, keys, ids, s);
+    case 7: return lm_launch_t<7, LPR, XF32, false>(dev, map, logits, ld, x, ldx_bytes, C, keys, ids, s);
+    case 8: return lm_launch_t<8, LPR, XF32, false>(dev, map, logits, ld, x, ldx_bytes, C, keys, ids, s);
   }
   return hipErrorInvalidValue;
 }

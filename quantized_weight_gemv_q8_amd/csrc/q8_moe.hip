@@ -25,47 +25,98 @@
 
 namespace q8 {
 
-__global__ __launch_bounds__(1024) void moe_route_kernel(const int32_t* ids, int E, int P,
-                                                         MoeWs ws, float* zero_rows,
-                                                         int64_t zero_ld) {
+constexpr int kRouteThreads = 1024;
+
+// Block-wide exclusive scan of one int per thread (kRouteThreads threads).
+__device__ __forceinline__ int block_exclusive_scan(int v, int* tmp, int* total) {
+  const int t = threadIdx.x;
+  tmp[t] = v;
+  __syncthreads();
+  for (int off = 1; off < kRouteThreads; off <<= 1) {
+    const int add = t >= off ? tmp[t - off] : 0;
+    __syncthreads();
+    tmp[t] += add;
+    __syncthreads();
+  }
+  const int incl = tmp[t];
+  *total = tmp[kRouteThreads - 1];
+  __syncthreads();
+  return incl - v;
+}
+
+// Expert-major CSR of the routed pairs in one workgroup: counts by LDS
+// atomics, offsets and the active list by block scans, pairs scattered by
+// atomic cursors and then put in ascending pair order inside each expert,
+// so the result does not depend on the order the atomics happened in.
+__global__ __launch_bounds__(kRouteThreads) void moe_route_kernel(const int32_t* ids, int E, int P,
+                                                                 MoeWs ws, float* zero_rows,
+                                                                 int64_t zero_ld) {
   extern __shared__ int32_t sm[];
+  __shared__ int scan_tmp[kRouteThreads];
   int32_t* cnt = sm;              // [E]
-  int32_t* off = sm + E;          // [E+1]
-  int32_t* sid = sm + 2 * E + 1;  // [P]
-  const int tid = threadIdx.x, nth = blockDim.x;
-  for (int e = tid; e < E; e += nth) cnt[e] = 0;
-  for (int p = tid; p < P; p += nth) sid[p] = ids[p];
-  __syncthreads();
-  for (int p = tid; p < P; p += nth) {
-    const int e = sid[p];
-    if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+  int32_t* off = cnt + E;         // [E+1]
+  int32_t* cur = off + E + 1;     // [E]
+  int32_t* sid = cur + E;         // [P]
+  int32_t* tmp = sid + P;         // [P]
+  const int t = threadIdx.x;
+  for (int e = t; e < E; e += kRouteThreads) cnt[e] = 0;
+  for (int p = t; p < P; p += kRouteThreads) {
+    const int e = ids[p];
+    sid[p] = (e >= 0 && e < E) ? e : -1;
   }
   __syncthreads();
-  if (tid == 0) {
-    int o = 0, na = 0;
-    for (int e = 0; e < E; ++e) {
+  for (int p = t; p < P; p += kRouteThreads)
+    if (sid[p] >= 0) atomicAdd(&cnt[sid[p]], 1);
+  __syncthreads();
+  // each thread owns a contiguous run of experts
+  const int per = (E + kRouteThreads - 1) / kRouteThreads;
+  const int e0 = t * per, e1 = e0 + per < E ? e0 + per : E;
+  int sum = 0, act = 0;
+  for (int e = e0; e < e1; ++e) {
+    sum += cnt[e];
+    act += cnt[e] > 0;
+  }
+  int total_pairs, total_active;
+  const int base = block_exclusive_scan(sum, scan_tmp, &total_pairs);
+  const int abase = block_exclusive_scan(act, scan_tmp, &total_active);
+  {
+    int o = base, a = abase;
+    for (int e = e0; e < e1; ++e) {
       off[e] = o;
+      cur[e] = o;
+      ws.counts[e] = cnt[e];
+      ws.offsets[e] = o;
+      if (cnt[e] > 0) ws.active[a++] = e;
       o += cnt[e];
-      if (cnt[e] > 0) ws.active[na++] = e;
     }
-    off[E] = o;
-    *ws.n_active = na;
+  }
+  if (t == 0) {
+    off[E] = total_pairs;
+    ws.offsets[E] = total_pairs;
+    *ws.n_active = total_active;
   }
   __syncthreads();
-  for (int e = tid; e < E; e += nth) {
-    ws.counts[e] = cnt[e];
-    ws.offsets[e] = off[e];
-  }
-  if (tid == 0) ws.offsets[E] = off[E];
-  for (int p = tid; p < P; p += nth) {
+  for (int p = t; p < P; p += kRouteThreads) {
     const int e = sid[p];
-    if (e >= 0 && e < E) {
-      int rank = 0;
-      for (int q = 0; q < p; ++q) rank += (sid[q] == e);
-      ws.pairs[off[e] + rank] = p;
+    if (e >= 0) {
+      tmp[atomicAdd(&cur[e], 1)] = p;
     } else if (zero_rows) {
       for (int64_t m = 0; m < zero_ld; ++m) zero_rows[(int64_t)p * zero_ld + m] = 0.0f;
     }
+  }
+  __syncthreads();
+  for (int e = t; e < E; e += kRouteThreads) {
+    const int lo = off[e], hi = off[e + 1];
+    for (int i = lo + 1; i < hi; ++i) {  // insertion sort: segments are short
+      const int v = tmp[i];
+      int j = i - 1;
+      while (j >= lo && tmp[j] > v) {
+        tmp[j + 1] = tmp[j];
+        --j;
+      }
+      tmp[j + 1] = v;
+    }
+    for (int i = lo; i < hi; ++i) ws.pairs[i] = tmp[i];
   }
 }
 
@@ -109,11 +160,12 @@ struct GateUpMap {
   }
 };
 
-struct PairOutEpi {  // y[pid[n]][row] = v
+struct PairOutEpi {  // y[pid[n]][row] = v for live tokens n < nt
   float* y;
   int64_t ld;
   int64_t r_end;
-  const int32_t* pid;  // LDS, [NT]
+  const int32_t* pid;  // LDS, [nt]
+  int nt;
   template <int NT, int R, int CNT>
   __device__ __forceinline__ void emit(int64_t rbase, int base, bool owner, const float* v) {
     if (!owner) return;
@@ -123,7 +175,7 @@ struct PairOutEpi {  // y[pid[n]][row] = v
       if (idx >= NT * R) continue;
       const int n = idx / R, r = idx - (idx / R) * R;
       const int64_t row = rbase + r;
-      if (row >= r_end) continue;
+      if (n >= nt || row >= r_end) continue;
       y[(int64_t)pid[n] * ld + row] = v[i];
     }
   }
@@ -133,144 +185,149 @@ struct SiluMulEpi {  // values come in (gate, up) pairs for one token
   float* h;
   int64_t ld;
   int64_t r_end;  // virtual rows
-  const int32_t* pid;
+  const int32_t* pid;  // LDS, [nt]
+  int nt;
   template <int NT, int R, int CNT>
   __device__ __forceinline__ void emit(int64_t rbase, int base, bool owner, const float* v) {
     static_assert(R == 2 && CNT == 2, "gate/up pairs");
     if (!owner) return;
     const int n = base / 2;
-    if (n >= NT || rbase >= r_end) return;
+    if (n >= nt || rbase >= r_end) return;
     const float g = v[0], u = v[1];
     const float sg = g / (1.0f + expf(-g));
     h[(int64_t)pid[n] * ld + (rbase >> 1)] = sg * u;
   }
 };
 
-template <int NT, bool XF32, class Map, class Epi, int R, int MINC, int LPR>
+// Tokens per pass for routed experts. Most experts receive one or two
+// tokens (128 pairs over ~80 active experts); capping the pass width keeps
+// the register budget of these kernels at the narrow-N level. An expert
+// with more tokens takes several passes over its tile, the later ones
+// served from L2.
+constexpr int kMoeNT = 2;
+
+template <int NT, bool XF32, int R, int D, int MINC, int LPR, class Map, class Epi>
 __device__ __forceinline__ void expert_pass(const Map& map, Epi& epi, const char* x,
                                             int64_t ldx_bytes, bool x_per_pair, int topk,
                                             const int32_t* pid_lds, int C, int64_t r_begin,
-                                            int64_t r_end, uint4* lds) {
-  const char* rows[NT];
-#pragma unroll
-  for (int n = 0; n < NT; ++n) {
-    const int p = pid_lds[n];
-    const int src = x_per_pair ? p : p / topk;
-    rows[n] = x + (int64_t)src * ldx_bytes;
-  }
-  stage_x<NT, XF32>(rows, C, lds);
-  __syncthreads();
+                                            int64_t r_end, uint4* lds, int nt) {
   constexpr int G = (kWave / LPR) * R;
   const int64_t n_groups = (r_end - r_begin + G - 1) / G;
-  run_rows<NT, LPR, R, MINC, XF32>(map, epi, lds, C, n_groups, threadIdx.x / kWave,
-                                   kWavesPerBlock, r_begin);
-  __syncthreads();
+  auto stage = [=]() {
+    const char* rows[NT];
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      const int p = n < nt ? pid_lds[n] : 0;
+      const int src = x_per_pair ? p : p / topk;
+      rows[n] = x + (int64_t)src * ldx_bytes;
+    }
+    stage_x<NT, XF32>(rows, C, lds, nt);
+    __syncthreads();
+  };
+  run_rows<NT, LPR, R, D, MINC, XF32>(map, epi, lds, C, n_groups, threadIdx.x / kWave,
+                                      kWavesPerBlock, r_begin, stage, nt);
 }
 
-// Token-count dispatch inside one workgroup (the count is per expert and
-// only known on the device).
-template <bool XF32, class Map, class Epi, int MINC, int LPR, int RFIX>
-__device__ __forceinline__ void expert_tokens(const Map& map, Epi& epi, const char* x,
-                                              int64_t ldx_bytes, bool x_per_pair, int topk,
-                                              int32_t* pid_lds, const int32_t* pairs, int ne,
-                                              int C, int64_t r_begin, int64_t r_end, uint4* lds) {
-  for (int t0 = 0; t0 < ne; t0 += kMaxNT) {
-    const int nt = ne - t0 < kMaxNT ? ne - t0 : kMaxNT;
-    if (threadIdx.x < nt) pid_lds[threadIdx.x] = pairs[t0 + threadIdx.x];
-    __syncthreads();
-    epi.pid = pid_lds;
-#define Q8_CASE(K_)                                                                        \
-  case K_:                                                                                 \
-    expert_pass<K_, XF32, Map, Epi, (RFIX ? RFIX : (K_ <= 2 ? 2 : 4)), MINC, LPR>(         \
-        map, epi, x, ldx_bytes, x_per_pair, topk, pid_lds, C, r_begin, r_end, lds);        \
-    break;
-    switch (nt) {
-      Q8_CASE(1) Q8_CASE(2) Q8_CASE(3) Q8_CASE(4) Q8_CASE(5) Q8_CASE(6) Q8_CASE(7) Q8_CASE(8)
+// Persistent loop over work items (active-expert slot, row tile); for each,
+// passes of up to kMoeNT of the expert's routed pairs.
+template <bool XF32, int MINC, int LPR, int RFIX, class MakeMap, class Epi>
+__device__ __forceinline__ void expert_items(const MoeWs& ws, int64_t tiles, int64_t rows_per_tile,
+                                             int64_t rows_total, const MakeMap& make_map, Epi& epi,
+                                             const char* x, int64_t ldx_bytes, bool x_per_pair,
+                                             int topk, int C, int32_t* pid_lds, uint4* lds) {
+  const int64_t items = (int64_t)__builtin_amdgcn_readfirstlane(*ws.n_active) * tiles;
+  for (int64_t wi = blockIdx.x; wi < items; wi += gridDim.x) {
+    const int slot = (int)(wi / tiles);
+    const int64_t tile = wi - (int64_t)slot * tiles;
+    const int e = __builtin_amdgcn_readfirstlane(ws.active[slot]);
+    const int o0 = __builtin_amdgcn_readfirstlane(ws.offsets[e]);
+    const int ne = __builtin_amdgcn_readfirstlane(ws.offsets[e + 1]) - o0;
+    const int64_t r_begin = tile * rows_per_tile;
+    const int64_t r_end = r_begin + rows_per_tile < rows_total ? r_begin + rows_per_tile : rows_total;
+    const auto map = make_map(e, r_end);
+    epi.r_end = r_end;
+    for (int t0 = 0; t0 < ne; t0 += kMoeNT) {
+      const int nt = ne - t0 < kMoeNT ? ne - t0 : kMoeNT;
+      __syncthreads();  // previous pass done with pid_lds and the LDS x image
+      if (threadIdx.x < nt) pid_lds[threadIdx.x] = ws.pairs[o0 + t0 + threadIdx.x];
+      __syncthreads();
+      epi.pid = pid_lds;
+      epi.nt = nt;
+      expert_pass<kMoeNT, XF32, (RFIX ? RFIX : Tune<kMoeNT, false>::R), Tune<kMoeNT, false>::D, MINC, LPR>(
+          map, epi, x, ldx_bytes, x_per_pair, topk, pid_lds, C, r_begin, r_end, lds, nt);
     }
-#undef Q8_CASE
   }
 }
-
-struct MoeGrid {
-  int64_t rows_per_tile;  // rows of one tile (virtual rows for gate/up)
-};
 
 template <int LPR, bool XF32>
 __global__ __launch_bounds__(kBlock) void moe_rows_kernel(HBank W, MoeWs ws, int topk,
                                                          const char* x, int64_t ldx_bytes,
-                                                         int x_per_pair, float* y,
+                                                         int x_per_pair, float* y, int64_t tiles,
                                                          int64_t rows_per_tile) {
   extern __shared__ uint4 lds_x[];
-  __shared__ int32_t pid_lds[kMaxNT];
-  const int slot = blockIdx.x;
-  if (slot >= *ws.n_active) return;
-  const int e = ws.active[slot];
-  const int o0 = ws.offsets[e];
-  const int ne = ws.offsets[e + 1] - o0;
+  __shared__ int32_t pid_lds[kMoeNT];
   const int64_t M = W.e0.M;
-  const int64_t r_begin = (int64_t)blockIdx.y * rows_per_tile;
-  if (r_begin >= M) return;
-  const int64_t r_end = r_begin + rows_per_tile < M ? r_begin + rows_per_tile : M;
-  SingleMap map;
-  map.w = expert_of(W, e);
-  map.M = M;
-  map.r_end = r_end;
   PairOutEpi epi;
   epi.y = y;
   epi.ld = M;
-  epi.r_end = r_end;
   epi.pid = pid_lds;
-  const int C = (int)(W.e0.K / 16);
-  expert_tokens<XF32, SingleMap, PairOutEpi, 1, LPR, 0>(map, epi, x, ldx_bytes, x_per_pair != 0,
-                                                         topk, pid_lds, ws.pairs + o0, ne, C,
-                                                         r_begin, r_end, lds_x);
+  auto make_map = [&](int e, int64_t r_end) {
+    SingleMap m;
+    m.w = expert_of(W, e);
+    m.M = M;
+    m.r_end = r_end;
+    return m;
+  };
+  expert_items<XF32, 1, LPR, 0>(ws, tiles, rows_per_tile, M, make_map, epi, x, ldx_bytes,
+                                x_per_pair != 0, topk, (int)(W.e0.K / 16), pid_lds, lds_x);
 }
 
 template <int LPR, bool XF32>
 __global__ __launch_bounds__(kBlock) void moe_gate_up_kernel(HBank Gb, HBank Ub, MoeWs ws,
                                                             int topk, const char* x,
                                                             int64_t ldx_bytes, float* h,
-                                                            int64_t rows_per_tile) {
+                                                            int64_t tiles, int64_t rows_per_tile) {
   extern __shared__ uint4 lds_x[];
-  __shared__ int32_t pid_lds[kMaxNT];
-  const int slot = blockIdx.x;
-  if (slot >= *ws.n_active) return;
-  const int e = ws.active[slot];
-  const int o0 = ws.offsets[e];
-  const int ne = ws.offsets[e + 1] - o0;
+  __shared__ int32_t pid_lds[kMoeNT];
   const int64_t F = Gb.e0.M;
-  const int64_t VR = 2 * F;  // virtual rows
-  const int64_t r_begin = (int64_t)blockIdx.y * rows_per_tile;
-  if (r_begin >= VR) return;
-  const int64_t r_end = r_begin + rows_per_tile < VR ? r_begin + rows_per_tile : VR;
-  GateUpMap map;
-  map.g = expert_of(Gb, e);
-  map.u = expert_of(Ub, e);
-  map.r_end = r_end;
   SiluMulEpi epi;
   epi.h = h;
   epi.ld = F;
-  epi.r_end = r_end;
   epi.pid = pid_lds;
-  const int C = (int)(Gb.e0.K / 16);
-  expert_tokens<XF32, GateUpMap, SiluMulEpi, 2, LPR, 2>(map, epi, x, ldx_bytes, false, topk,
-                                                         pid_lds, ws.pairs + o0, ne, C, r_begin,
-                                                         r_end, lds_x);
+  auto make_map = [&](int e, int64_t r_end) {
+    GateUpMap m;
+    m.g = expert_of(Gb, e);
+    m.u = expert_of(Ub, e);
+    m.r_end = r_end;
+    return m;
+  };
+  expert_items<XF32, 2, LPR, 2>(ws, tiles, rows_per_tile, 2 * F, make_map, epi, x, ldx_bytes,
+                                false, topk, (int)(Gb.e0.K / 16), pid_lds, lds_x);
 }
 
 __global__ __launch_bounds__(256) void moe_combine_kernel(const int32_t* ids, int E,
                                                          const float* gate_w, const float* yp,
                                                          float* out, int topk, int64_t M) {
   const int t = blockIdx.y;
-  const int64_t m = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (m >= M) return;
-  float acc = 0.0f;
+  const int64_t m0 = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+  if (m0 >= M) return;
+  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   for (int j = 0; j < topk; ++j) {
     const int e = ids[t * topk + j];
     if (e < 0 || e >= E) continue;
-    acc = __builtin_fmaf(gate_w[t * topk + j], yp[((int64_t)t * topk + j) * M + m], acc);
+    const float w = gate_w[t * topk + j];
+    const float* row = yp + ((int64_t)t * topk + j) * M;
+    if ((M & 3) == 0) {
+      const float4 v = *reinterpret_cast<const float4*>(row + m0);
+      acc[0] = __builtin_fmaf(w, v.x, acc[0]);
+      acc[1] = __builtin_fmaf(w, v.y, acc[1]);
+      acc[2] = __builtin_fmaf(w, v.z, acc[2]);
+      acc[3] = __builtin_fmaf(w, v.w, acc[3]);
+    } else {
+      for (int i = 0; i < 4 && m0 + i < M; ++i) acc[i] = __builtin_fmaf(w, row[m0 + i], acc[i]);
+    }
   }
-  out[(int64_t)t * M + m] = acc;
+  for (int i = 0; i < 4 && m0 + i < M; ++i) out[(int64_t)t * M + m0 + i] = acc[i];
 }
 
 // ---------------------------------------------------------------- host side
@@ -296,20 +353,30 @@ size_t moe_ws_layout(int E, int T, int topk, int64_t F, int64_t M, size_t off[7]
 
 hipError_t launch_moe_route(const int32_t* ids, int E, int P, const MoeWs& ws, float* zero_rows,
                             int64_t zero_ld, hipStream_t s) {
-  const size_t lds = 4 * (size_t)(2 * E + 1 + P);
-  int threads = 256;
-  if (P > 256 || E > 256) threads = 1024;
+  const size_t lds = 4 * (size_t)(3 * E + 1 + 2 * P);
   MoeWs w = ws;
   void* args[] = {(void*)&ids, &E, &P, &w, &zero_rows, &zero_ld};
-  return hipLaunchKernel((const void*)moe_route_kernel, dim3(1), dim3(threads), args, lds, s);
+  if (lds > 64 * 1024) {
+    hipError_t e = hipFuncSetAttribute((const void*)moe_route_kernel,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  return hipLaunchKernel((const void*)moe_route_kernel, dim3(1), dim3(kRouteThreads), args, lds, s);
 }
 
-static int64_t tiles_for(const DevInfo& dev, int slots, int64_t rows, int64_t row_quantum) {
-  int64_t tiles = (4LL * dev.cus + slots - 1) / slots;
-  if (tiles < 1) tiles = 1;
-  const int64_t max_tiles = (rows + row_quantum - 1) / row_quantum;
-  if (tiles > max_tiles) tiles = max_tiles;
-  return tiles;
+// Row tiles per expert: enough work items (active experts x tiles) to give
+// each resident workgroup several, each tile at least one group per wave.
+static void plan_tiles(int64_t blocks, int slots, int64_t rows, int64_t group_rows, int64_t* tiles,
+                       int64_t* rows_per_tile) {
+  const int64_t min_rows = group_rows * kWavesPerBlock;
+  int64_t t = (6 * blocks + slots - 1) / slots;
+  const int64_t max_t = (rows + min_rows - 1) / min_rows;
+  if (t > max_t) t = max_t;
+  if (t < 1) t = 1;
+  int64_t rpt = (rows + t - 1) / t;
+  rpt = round_up(rpt, group_rows);
+  *rows_per_tile = rpt;
+  *tiles = (rows + rpt - 1) / rpt;
 }
 
 template <int LPR, bool XF32>
@@ -318,22 +385,21 @@ static hipError_t moe_rows_t(const DevInfo& dev, const HBank& W, const MoeWs& ws
                              hipStream_t s) {
   const int slots = P < W.E ? P : W.E;
   const int64_t M = W.e0.M;
-  const int64_t quantum = (int64_t)kWavesPerBlock * (kWave / LPR) * 4;
-  const int64_t tiles = tiles_for(dev, slots, M, quantum);
-  int64_t rpt = round_up((M + tiles - 1) / tiles, (kWave / LPR) * 4);
-  const size_t lds = (size_t)kMaxNT * (W.e0.K / 16) * 16 * XPlanes<XF32>::P;
+  const size_t lds = (size_t)kMoeNT * (W.e0.K / 16) * 16 * XPlanes<XF32>::P;
   auto fn = moe_rows_kernel<LPR, XF32>;
   if (lds > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize,
                                        (int)lds);
     if (e != hipSuccess) return e;
   }
+  const int64_t blocks = (int64_t)dev.cus * blocks_per_cu((const void*)fn, lds);
+  int64_t tiles, rpt;
+  plan_tiles(blocks, slots, M, (kWave / LPR) * Tune<kMoeNT, false>::R, &tiles, &rpt);
+  int64_t grid = slots * tiles < blocks ? slots * tiles : blocks;
   HBank w = W;
   MoeWs wsv = ws;
-  void* args[] = {&w, &wsv, &topk, (void*)&x, &ldx_bytes, &x_per_pair, &y, &rpt};
-  const int64_t ty = (M + rpt - 1) / rpt;
-  return hipLaunchKernel((const void*)fn, dim3((unsigned)slots, (unsigned)ty), dim3(kBlock), args,
-                         lds, s);
+  void* args[] = {&w, &wsv, &topk, (void*)&x, &ldx_bytes, &x_per_pair, &y, &tiles, &rpt};
+  return hipLaunchKernel((const void*)fn, dim3((unsigned)grid), dim3(kBlock), args, lds, s);
 }
 
 hipError_t launch_moe_gemv(const DevInfo& dev, const HBank& W, const MoeWs& ws, int P, int topk,
@@ -359,22 +425,21 @@ static hipError_t moe_gu_t(const DevInfo& dev, const HBank& G, const HBank& U, c
                            hipStream_t s) {
   const int slots = P < G.E ? P : G.E;
   const int64_t VR = 2 * G.e0.M;
-  const int64_t quantum = (int64_t)kWavesPerBlock * (kWave / LPR) * 2;
-  const int64_t tiles = tiles_for(dev, slots, VR, quantum);
-  int64_t rpt = round_up((VR + tiles - 1) / tiles, (kWave / LPR) * 2);
-  const size_t lds = (size_t)kMaxNT * (G.e0.K / 16) * 16 * XPlanes<XF32>::P;
+  const size_t lds = (size_t)kMoeNT * (G.e0.K / 16) * 16 * XPlanes<XF32>::P;
   auto fn = moe_gate_up_kernel<LPR, XF32>;
   if (lds > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize,
                                        (int)lds);
     if (e != hipSuccess) return e;
   }
+  const int64_t blocks = (int64_t)dev.cus * blocks_per_cu((const void*)fn, lds);
+  int64_t tiles, rpt;
+  plan_tiles(blocks, slots, VR, (kWave / LPR) * 2, &tiles, &rpt);
+  int64_t grid = slots * tiles < blocks ? slots * tiles : blocks;
   HBank g = G, u = U;
   MoeWs wsv = ws;
-  void* args[] = {&g, &u, &wsv, &topk, (void*)&x, &ldx_bytes, &h, &rpt};
-  const int64_t ty = (VR + rpt - 1) / rpt;
-  return hipLaunchKernel((const void*)fn, dim3((unsigned)slots, (unsigned)ty), dim3(kBlock), args,
-                         lds, s);
+  void* args[] = {&g, &u, &wsv, &topk, (void*)&x, &ldx_bytes, &h, &tiles, &rpt};
+  return hipLaunchKernel((const void*)fn, dim3((unsigned)grid), dim3(kBlock), args, lds, s);
 }
 
 hipError_t launch_moe_gate_up(const DevInfo& dev, const HBank& G, const HBank& U,
@@ -397,7 +462,7 @@ hipError_t launch_moe_combine(const int32_t* ids, int E, const float* gate_w,
                               const float* y_pair, float* out, int T, int topk, int64_t M,
                               hipStream_t s) {
   void* args[] = {(void*)&ids, &E, (void*)&gate_w, (void*)&y_pair, &out, &topk, &M};
-  const unsigned gx = (unsigned)((M + 255) / 256);
+  const unsigned gx = (unsigned)(((M + 3) / 4 + 255) / 256);
   return hipLaunchKernel((const void*)moe_combine_kernel, dim3(gx, (unsigned)T), dim3(256), args, 0,
                          s);
 }
