@@ -10,7 +10,7 @@
 
 #include <mutex>
 
-#include "../../include/q8gemv.h"
+#include "q8gemv.h"
 #include "q8_internal.h"
 
 using q8::DevInfo;
