@@ -206,13 +206,15 @@ struct ReduceShape {
 // byte = 2*NT/R for fp16 x); D*R 16-byte loads are kept in flight per wave.
 // Neither changes the per-(row, token) arithmetic, so the choice may depend
 // on the shape (per-shape dispatch) without breaking N-invariance.
-// Measured on MI355X at N = 1 with the persistent grid at full occupancy:
-// large matrices (>= 64K rows, e.g. a 151936-row LM head) stream best with
-// R = 4, D = 1; smaller ones (5120 or 34816 rows) with R = 1, D = 1.
+// Measured on MI355X (persistent grid at full occupancy, same-process A/B):
+// a one-chunk window (D = 1) with many resident waves beats deeper windows
+// at every width; at N = 1 large matrices (>= 64K rows, e.g. a 151936-row
+// LM head) stream best with R = 4 and smaller ones with R = 1; for N >= 3,
+// R = 4 keeps the LDS reads of x per weight byte low.
 template <int NT, bool BIG>
 struct Tune {
-  static constexpr int R = NT == 1 ? (BIG ? 4 : 1) : (NT <= 4 ? 2 : 4);
-  static constexpr int D = NT == 1 ? 1 : (NT <= 4 ? 4 : 2);
+  static constexpr int R = NT == 1 ? (BIG ? 4 : 1) : (NT <= 2 ? 2 : 4);
+  static constexpr int D = 1;
 };
 constexpr int64_t kBigRows = 65536;
 

@@ -199,12 +199,13 @@ struct SiluMulEpi {  // values come in (gate, up) pairs for one token
   }
 };
 
-// Tokens per pass for routed experts. Most experts receive one or two
-// tokens (128 pairs over ~80 active experts); capping the pass width keeps
-// the register budget of these kernels at the narrow-N level. An expert
-// with more tokens takes several passes over its tile, the later ones
-// served from L2.
-constexpr int kMoeNT = 2;
+// Tokens per pass for routed experts (most experts receive one or two
+// tokens: 128 pairs over ~80 active experts). An expert with more tokens
+// takes several passes over its tile, the later ones served from L2. The
+// load window is one chunk (D = 1). Both were picked by same-process A/B
+// on MI355X for the 128-expert top-8 T=16 layer (184 -> 134 us against a
+// 2-token pass with D = 4; wider passes and other tile sizes were slower).
+constexpr int kMoeNT = 4;
 
 template <int NT, bool XF32, int R, int D, int MINC, int LPR, class Map, class Epi>
 __device__ __forceinline__ void expert_pass(const Map& map, Epi& epi, const char* x,
@@ -253,7 +254,7 @@ __device__ __forceinline__ void expert_items(const MoeWs& ws, int64_t tiles, int
       __syncthreads();
       epi.pid = pid_lds;
       epi.nt = nt;
-      expert_pass<kMoeNT, XF32, (RFIX ? RFIX : Tune<kMoeNT, false>::R), Tune<kMoeNT, false>::D, MINC, LPR>(
+      expert_pass<kMoeNT, XF32, (RFIX ? RFIX : Tune<kMoeNT, false>::R), 1, MINC, LPR>(
           map, epi, x, ldx_bytes, x_per_pair, topk, pid_lds, C, r_begin, r_end, lds, nt);
     }
   }
