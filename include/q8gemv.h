@@ -150,8 +150,12 @@ int q8_gemv_pair(const q8_matrix *Wa, const q8_matrix *Wb, const void *x, int x_
  *   x [dev] fp16 or fp32 [N][K]; logits [dev] fp32 [N][V] or NULL;
  *   ids [dev] int32 [N]; N >= 1 (passes of up to 8 tokens).
  *   ws [dev] workspace of at least q8_lmhead_ws_bytes(V, N) bytes,
- *   16-byte aligned, contents need not be initialised. Concurrent calls
- *   must use distinct workspaces. */
+ *   16-byte aligned, owned by the caller. It must be zero-filled once
+ *   before its first use: it holds the argmax slots and the counters that
+ *   let the last workgroup finish the argmax in the same launch, and every
+ *   completed call leaves it all zero again, so the same workspace can be
+ *   reused (and captured in a graph) without clearing it. Keep it for
+ *   LM-head calls only; concurrent calls must use distinct workspaces. */
 size_t q8_lmhead_ws_bytes(int64_t V, int N);
 int q8_lmhead_argmax(const q8_matrix *W, const void *x, int x_dt, float *logits,
                      int32_t *ids, int N, void *ws, size_t ws_bytes, void *stream);

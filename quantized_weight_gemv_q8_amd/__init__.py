@@ -262,7 +262,7 @@ def lmhead_argmax(W: PackedQ8, x, logits=True, ids=None, ws=None, stream=None):
         ids = torch.empty((N,), dtype=torch.int32, device=x.device)
     nws = lmhead_ws_bytes(W.M, N)
     if ws is None:
-        ws = torch.empty((nws,), dtype=torch.uint8, device=x.device)
+        ws = torch.zeros((nws,), dtype=torch.uint8, device=x.device)
     _check(lib().q8_lmhead_argmax(ctypes.byref(W.cmat()), x.data_ptr(), _dt(x),
                                   logits.data_ptr() if logits is not None else None,
                                   ids.data_ptr(), N, ws.data_ptr(), ws.numel() * ws.element_size(),

@@ -224,7 +224,7 @@ int q8_gemv_pair(const q8_matrix* Wa, const q8_matrix* Wb, const void* x, int x_
 size_t q8_lmhead_ws_bytes(int64_t V, int N) {
   (void)V;
   (void)N;
-  return (size_t)4096 * 8 * sizeof(uint64_t);
+  return q8::lmhead_ws_bytes();
 }
 
 int q8_lmhead_argmax(const q8_matrix* W, const void* x, int x_dt, float* logits, int32_t* ids,
@@ -255,7 +255,7 @@ int q8_lmhead_argmax(const q8_matrix* W, const void* x, int x_dt, float* logits,
     const int nt = N - n0 < per_pass ? N - n0 : per_pass;
     const char* xp = (const char*)x + (size_t)n0 * W->K * xs;
     float* lp = logits ? logits + (size_t)n0 * W->M : nullptr;
-    hipError_t e = q8::launch_lmhead(*dev, A, xp, xf, lp, W->M, ids + n0, (uint64_t*)ws, nt,
+    hipError_t e = q8::launch_lmhead(*dev, A, xp, xf, lp, W->M, ids + n0, (char*)ws, nt,
                                      (hipStream_t)stream);
     if (e != hipSuccess) return Q8_ERR_LAUNCH;
   }

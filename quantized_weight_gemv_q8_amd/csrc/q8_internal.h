@@ -49,11 +49,12 @@ hipError_t launch_gemv(const DevInfo& dev, const HMat& A, const HMat* B, const v
                        bool x_f32, int64_t ldx, void* ya, void* yb, bool y_f16, int nt,
                        hipStream_t s);
 
-// LM head pass: logits (may be null), per-workgroup partial argmax keys into
-// keys [n_blocks][nt]; then the final reduction writes ids [nt].
-int lmhead_blocks(const DevInfo& dev, int64_t V);
+// LM head pass: logits (may be null) and ids [nt]. The workspace holds the
+// argmax slots and counters; it must be zero before the first pass and is
+// zero again after each completed pass.
+size_t lmhead_ws_bytes();
 hipError_t launch_lmhead(const DevInfo& dev, const HMat& W, const void* x, bool x_f32,
-                         float* logits, int64_t ld_logits, int32_t* ids, uint64_t* keys,
+                         float* logits, int64_t ld_logits, int32_t* ids, char* ws,
                          int nt, hipStream_t s);
 
 // Routed experts.

@@ -6,13 +6,16 @@
 // traffic"), and greedy argmax is their correctness instrument (memra wiki,
 // gate paragraph: run-gen prints its argmax gate before any number).
 //
-// Pass structure: one persistent GEMV launch whose workgroups each fold
-// the rows they produced into one 64-bit key per token, written to a
-// per-workgroup slot (no atomics, no pre-zeroed memory, deterministic),
-// then a single-workgroup launch that takes the maximum key per token and
-// decodes the row index. Key = (order-preserving bits of the fp32 logit,
-// with -0 mapped to +0) << 32 | ~row, so the maximum key is the largest
-// logit and, among equal logits, the lowest row.
+// Pass structure: one persistent GEMV launch. Each workgroup folds the
+// rows it produced into one 64-bit key per token, merges it into a
+// per-token slot with an atomic maximum, and then takes a ticket from a
+// wrapping counter; the workgroup that draws the last ticket reads the
+// slots (resetting them to zero) and decodes the row indices. Slots and
+// counter are zero again after every completed launch, so the workspace
+// needs zero-filling only before its first use. Key = (order-preserving
+// bits of the fp32 logit, with -0 mapped to +0) << 32 | ~row, so the
+// maximum key is the largest logit and, among equal logits, the lowest
+// row; the result does not depend on the order of the workgroups.
 #include "q8_engine.hpp"
 #include "q8_internal.h"
 
@@ -27,6 +30,15 @@ __device__ __forceinline__ uint64_t argmax_key(float v, int64_t row) {
   return ((uint64_t)ord << 32) | (uint64_t)(~(uint32_t)row);
 }
 
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t k) {
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) {
+    const uint64_t o = __shfl_xor(k, off, kWave);
+    k = o > k ? o : k;
+  }
+  return k;
+}
+
 struct LmMap {
   MatDesc w;
   int64_t V;
@@ -36,6 +48,34 @@ struct LmMap {
     return i < V;
   }
 };
+
+// Workspace (zero before first use, zero again after every launch):
+// per-group slots [kLmGroups][kMaxNT] uint64 and counters, one 256-byte
+// line each, then the final slots [kMaxNT] and counter.
+constexpr int kLmGroups = 8;
+constexpr int kLmLine = 256;
+constexpr size_t kLmWsBytes = (size_t)(2 * kLmGroups + 2) * kLmLine;
+static_assert(kMaxNT * sizeof(uint64_t) <= kLmLine, "slots fit a line");
+
+struct LmWs {
+  char* base;
+  __device__ __forceinline__ uint64_t* group_slot(uint32_t g) const {
+    return (uint64_t*)(base + (size_t)g * kLmLine);
+  }
+  __device__ __forceinline__ uint32_t* group_ctr(uint32_t g) const {
+    return (uint32_t*)(base + (size_t)(kLmGroups + g) * kLmLine);
+  }
+  uint64_t* slot;
+  uint32_t* ctr;
+};
+
+__device__ __forceinline__ LmWs lm_ws(char* ws) {
+  LmWs w;
+  w.base = ws;
+  w.slot = (uint64_t*)(ws + (size_t)(2 * kLmGroups) * kLmLine);
+  w.ctr = (uint32_t*)(ws + (size_t)(2 * kLmGroups + 1) * kLmLine);
+  return w;
+}
 
 // Each lane owns a fixed set of (token, row-slot) values after the team
 // reduction (the set depends only on the lane's position), so the running
@@ -83,7 +123,7 @@ struct LmEpi {
 template <int NT, int LPR, bool XF32, bool BIG>
 __global__ __launch_bounds__(kBlock) void lmhead_kernel(LmMap map, float* logits, int64_t ld,
                                                         const char* x, int64_t ldx_bytes, int C,
-                                                        uint64_t* keys) {
+                                                        char* ws, int32_t* ids) {
   extern __shared__ uint4 lds_x[];
   __shared__ uint64_t red[kWavesPerBlock][kMaxNT];
   using T = Tune<NT, BIG>;
@@ -122,74 +162,61 @@ __global__ __launch_bounds__(kBlock) void lmhead_kernel(LmMap map, float* logits
         k = c > k ? c : k;
       }
     }
-#pragma unroll
-    for (int off = kWave / 2; off > 0; off >>= 1) {
-      const uint64_t o = __shfl_xor(k, off, kWave);
-      k = o > k ? o : k;
-    }
+    k = wave_max_u64(k);
     if (lane == 0) red[wave][n] = k;
   }
   __syncthreads();
-  if (threadIdx.x < NT) {
-    uint64_t k = 0;
-    for (int w = 0; w < kWavesPerBlock; ++w) {
-      const uint64_t o = red[w][threadIdx.x];
-      k = o > k ? o : k;
+  if (threadIdx.x == 0) {
+    // Two-level merge of the per-workgroup keys: workgroup b belongs to
+    // group b % ng. Every access to the slots and counters is an
+    // agent-scope atomic, so each location is coherent across the chip
+    // without cache write-back or invalidation, and waiting for the
+    // returned values puts a workgroup's slot updates before its ticket.
+    const LmWs w = lm_ws(ws);
+    const uint32_t ng = gridDim.x < (uint32_t)kLmGroups ? gridDim.x : (uint32_t)kLmGroups;
+    const uint32_t g = blockIdx.x % ng;
+    const uint32_t members = (gridDim.x - g + ng - 1) / ng;
+    uint64_t dep = 0;
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      uint64_t k = 0;
+      for (int wv = 0; wv < kWavesPerBlock; ++wv) {
+        const uint64_t o = red[wv][n];
+        k = o > k ? o : k;
+      }
+      dep |= __hip_atomic_fetch_max(w.group_slot(g) + n, k, __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_AGENT);
     }
-    keys[(int64_t)blockIdx.x * NT + threadIdx.x] = k;
-  }
-}
-
-// One workgroup: maximum key per token over the per-workgroup slots,
-// decoded to the row index.
-constexpr int kFinalThreads = 1024;
-
-__global__ __launch_bounds__(kFinalThreads) void lmhead_final_kernel(const uint64_t* keys,
-                                                                    int nblocks, int nt,
-                                                                    int32_t* ids) {
-  __shared__ uint64_t red[kFinalThreads / kWave][kMaxNT];
-  uint64_t k[kMaxNT];
+    asm volatile("s_waitcnt vmcnt(0)" : : "v"(dep) : "memory");
+    // A counter returns to zero when its last ticket is drawn.
+    bool last = atomicInc(w.group_ctr(g), members - 1) == members - 1;
+    if (last) {
+      // Every member of the group has merged: move the group's keys into
+      // the final slots (leaving the group slots at zero).
 #pragma unroll
-  for (int n = 0; n < kMaxNT; ++n) k[n] = 0;
-  for (int b = threadIdx.x; b < nblocks; b += blockDim.x) {
+      for (int n = 0; n < NT; ++n) {
+        const uint64_t m = __hip_atomic_exchange(w.group_slot(g) + n, (uint64_t)0,
+                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        dep |= __hip_atomic_fetch_max(w.slot + n, m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      asm volatile("s_waitcnt vmcnt(0)" : : "v"(dep) : "memory");
+      last = atomicInc(w.ctr, ng - 1) == ng - 1;
+      if (last) {
+        // Every group has merged: decode the ids, leave the slots at zero.
 #pragma unroll
-    for (int n = 0; n < kMaxNT; ++n) {
-      if (n < nt) {
-        const uint64_t o = keys[(int64_t)b * nt + n];
-        k[n] = o > k[n] ? o : k[n];
+        for (int n = 0; n < NT; ++n) {
+          const uint64_t m = __hip_atomic_exchange(w.slot + n, (uint64_t)0, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT);
+          ids[n] = (int32_t)(~(uint32_t)(m & 0xffffffffu));
+        }
       }
     }
   }
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-#pragma unroll
-  for (int n = 0; n < kMaxNT; ++n) {
-#pragma unroll
-    for (int off = kWave / 2; off > 0; off >>= 1) {
-      const uint64_t o = __shfl_xor(k[n], off, kWave);
-      k[n] = o > k[n] ? o : k[n];
-    }
-    if (lane == 0) red[wave][n] = k[n];
-  }
-  __syncthreads();
-  if (threadIdx.x < nt) {
-    uint64_t m = 0;
-    for (int w = 0; w < (int)(blockDim.x / kWave); ++w) {
-      const uint64_t o = red[w][threadIdx.x];
-      m = o > m ? o : m;
-    }
-    ids[threadIdx.x] = (int32_t)(~(uint32_t)(m & 0xffffffffu));
-  }
-}
-
-int lmhead_blocks(const DevInfo& dev, int64_t V) {
-  (void)dev;
-  (void)V;
-  return kLmMaxBlocks;
 }
 
 template <int NT, int LPR, bool XF32, bool BIG>
 static hipError_t lm_launch_t(const DevInfo& dev, LmMap map, float* logits, int64_t ld,
-                              const char* x, int64_t ldx_bytes, int C, uint64_t* keys,
+                              const char* x, int64_t ldx_bytes, int C, char* ws,
                               int32_t* ids, hipStream_t s) {
   constexpr int G = (kWave / LPR) * Tune<NT, BIG>::R;
   const size_t lds = (size_t)NT * C * 16 * XPlanes<XF32>::P;
@@ -205,38 +232,34 @@ static hipError_t lm_launch_t(const DevInfo& dev, LmMap map, float* logits, int6
   if (blocks > need) blocks = need;
   if (blocks > kLmMaxBlocks) blocks = kLmMaxBlocks;
   if (blocks < 1) blocks = 1;
-  void* args[] = {&map, &logits, &ld, (void*)&x, &ldx_bytes, &C, &keys};
-  hipError_t e = hipLaunchKernel((const void*)fn, dim3((unsigned)blocks), dim3(kBlock), args, lds, s);
-  if (e != hipSuccess) return e;
-  int nb = (int)blocks;
-  int nt = NT;
-  void* fargs[] = {&keys, &nb, &nt, &ids};
-  return hipLaunchKernel((const void*)lmhead_final_kernel, dim3(1), dim3(kFinalThreads), fargs, 0,
-                         s);
+  void* args[] = {&map, &logits, &ld, (void*)&x, &ldx_bytes, &C, &ws, &ids};
+  return hipLaunchKernel((const void*)fn, dim3((unsigned)blocks), dim3(kBlock), args, lds, s);
 }
 
 template <int LPR, bool XF32>
 static hipError_t lm_launch_nt(const DevInfo& dev, int nt, LmMap map, float* logits, int64_t ld,
-                               const char* x, int64_t ldx_bytes, int C, uint64_t* keys,
+                               const char* x, int64_t ldx_bytes, int C, char* ws,
                                int32_t* ids, hipStream_t s) {
   switch (nt) {
     case 1:
       if (map.V >= kBigRows)
-        return lm_launch_t<1, LPR, XF32, true>(dev, map, logits, ld, x, ldx_bytes, C, keys, ids, s);
-      return lm_launch_t<1, LPR, XF32, false>(dev, map, logits, ld, x, ldx_bytes, C, keys, ids, s);
-    case 2: return lm_launch_t<2, LPR, XF32, false>(dev, map, logits, ld, x, ldx_bytes, C, keys, ids, s);
-    case 3: return lm_launch_t<3, LPR, XF32, false>(dev, map, logits, ld, x, ldx_bytes, C, keys, ids, s);
-    case 4: return lm_launch_t<4, LPR, XF32, false>(dev, map, logits, ld, x, ldx_bytes, C, keys, ids, s);
-    case 5: return lm_launch_t<5, LPR, XF32, false>(dev, map, logits, ld, x, ldx_bytes, C, keys, ids, s);
-    case 6: return lm_launch_t<6, LPR, XF32, false>(dev, map, logits, ld, x, ldx_bytes, C, keys, ids, s);
-    case 7: return lm_launch_t<7, LPR, XF32, false>(dev, map, logits, ld, x, ldx_bytes, C, keys, ids, s);
-    case 8: return lm_launch_t<8, LPR, XF32, false>(dev, map, logits, ld, x, ldx_bytes, C, keys, ids, s);
+        return lm_launch_t<1, LPR, XF32, true>(dev, map, logits, ld, x, ldx_bytes, C, ws, ids, s);
+      return lm_launch_t<1, LPR, XF32, false>(dev, map, logits, ld, x, ldx_bytes, C, ws, ids, s);
+    case 2: return lm_launch_t<2, LPR, XF32, false>(dev, map, logits, ld, x, ldx_bytes, C, ws, ids, s);
+    case 3: return lm_launch_t<3, LPR, XF32, false>(dev, map, logits, ld, x, ldx_bytes, C, ws, ids, s);
+    case 4: return lm_launch_t<4, LPR, XF32, false>(dev, map, logits, ld, x, ldx_bytes, C, ws, ids, s);
+    case 5: return lm_launch_t<5, LPR, XF32, false>(dev, map, logits, ld, x, ldx_bytes, C, ws, ids, s);
+    case 6: return lm_launch_t<6, LPR, XF32, false>(dev, map, logits, ld, x, ldx_bytes, C, ws, ids, s);
+    case 7: return lm_launch_t<7, LPR, XF32, false>(dev, map, logits, ld, x, ldx_bytes, C, ws, ids, s);
+    case 8: return lm_launch_t<8, LPR, XF32, false>(dev, map, logits, ld, x, ldx_bytes, C, ws, ids, s);
   }
   return hipErrorInvalidValue;
 }
 
+size_t lmhead_ws_bytes() { return kLmWsBytes; }
+
 hipError_t launch_lmhead(const DevInfo& dev, const HMat& W, const void* x, bool x_f32,
-                         float* logits, int64_t ld_logits, int32_t* ids, uint64_t* keys, int nt,
+                         float* logits, int64_t ld_logits, int32_t* ids, char* ws, int nt,
                          hipStream_t s) {
   LmMap map;
   map.w = MatDesc{W.qs, W.d, W.ld_qs, W.ld_d};
@@ -246,13 +269,13 @@ hipError_t launch_lmhead(const DevInfo& dev, const HMat& W, const void* x, bool 
   const char* xp = (const char*)x;
   const int lpr = lanes_per_row(W.K);
   if (x_f32) {
-    if (lpr == 64) return lm_launch_nt<64, true>(dev, nt, map, logits, ld_logits, xp, ldx_bytes, C, keys, ids, s);
-    if (lpr == 32) return lm_launch_nt<32, true>(dev, nt, map, logits, ld_logits, xp, ldx_bytes, C, keys, ids, s);
-    return lm_launch_nt<16, true>(dev, nt, map, logits, ld_logits, xp, ldx_bytes, C, keys, ids, s);
+    if (lpr == 64) return lm_launch_nt<64, true>(dev, nt, map, logits, ld_logits, xp, ldx_bytes, C, ws, ids, s);
+    if (lpr == 32) return lm_launch_nt<32, true>(dev, nt, map, logits, ld_logits, xp, ldx_bytes, C, ws, ids, s);
+    return lm_launch_nt<16, true>(dev, nt, map, logits, ld_logits, xp, ldx_bytes, C, ws, ids, s);
   }
-  if (lpr == 64) return lm_launch_nt<64, false>(dev, nt, map, logits, ld_logits, xp, ldx_bytes, C, keys, ids, s);
-  if (lpr == 32) return lm_launch_nt<32, false>(dev, nt, map, logits, ld_logits, xp, ldx_bytes, C, keys, ids, s);
-  return lm_launch_nt<16, false>(dev, nt, map, logits, ld_logits, xp, ldx_bytes, C, keys, ids, s);
+  if (lpr == 64) return lm_launch_nt<64, false>(dev, nt, map, logits, ld_logits, xp, ldx_bytes, C, ws, ids, s);
+  if (lpr == 32) return lm_launch_nt<32, false>(dev, nt, map, logits, ld_logits, xp, ldx_bytes, C, ws, ids, s);
+  return lm_launch_nt<16, false>(dev, nt, map, logits, ld_logits, xp, ldx_bytes, C, ws, ids, s);
 }
 
 }  // namespace q8

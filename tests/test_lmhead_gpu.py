@@ -108,3 +108,20 @@ def test_all_zero_logits_pick_row_zero():
     logits, ids = q8.lmhead_argmax(upload(q, d), dev(x))
     assert np.all(host(logits) == 0)
     assert host(ids)[0] == 0
+
+
+def test_workspace_reused_across_shapes_returns_to_zero():
+    """One zero-filled workspace serves calls whose grids differ (vocab
+    size, token count, multi-pass N): every call's ids match the oracle and
+    the whole workspace (argmax slots and counters) reads zero after each
+    call, ready for the next one."""
+    ws = torch.zeros((q8.lmhead_ws_bytes(1, 1),), dtype=torch.uint8, device="cuda")
+    for i, (V, K, N) in enumerate([(4096, 1024, 1), (333, 96, 11), (20000, 512, 4), (1, 32, 1),
+                                   (9, 64, 2), (4096, 1024, 8)]):
+        note(f"lmhead ws reuse V={V} K={K} N={N}")
+        c = synth.lmhead_case(V, K, min(N, V), seed=100 + i)
+        if N > V:
+            c.x = synth.draw_x(np.random.default_rng(i), N, K)
+        logits, ids = q8.lmhead_argmax(upload(c.q, c.d), dev(c.x), ws=ws)
+        check_lmhead(c, host(logits), host(ids))
+        assert not host(ws).any(), "workspace not returned to zero"
