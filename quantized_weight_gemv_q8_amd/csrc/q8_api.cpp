@@ -11,6 +11,8 @@
 #include <mutex>
 
 #include "q8gemv.h"
+
+#include <climits>
 #include "q8_internal.h"
 
 using q8::DevInfo;
@@ -265,19 +267,21 @@ int q8_lmhead_argmax(const q8_matrix* W, const void* x, int x_dt, float* logits,
 // ------------------------------------------------------------ routed experts
 size_t q8_moe_ws_bytes(int E, int T, int topk, int64_t F, int64_t M) {
   if (E < 1 || T < 1 || topk < 1 || F < 0 || M < 0) return 0;
-  size_t off[7];
+  size_t off[q8::kMoeWsAreas];
   return q8::moe_ws_layout(E, T, topk, F, M, off);
 }
 
 int q8_moe_ws_layout(int E, int T, int topk, int64_t F, int64_t M, size_t offsets[7]) {
   if (!offsets) return Q8_ERR_NULL;
   if (E < 1 || T < 1 || topk < 1 || topk > E || F < 0 || M < 0) return Q8_ERR_SHAPE;
-  q8::moe_ws_layout(E, T, topk, F, M, offsets);
+  size_t off[q8::kMoeWsAreas];
+  q8::moe_ws_layout(E, T, topk, F, M, off);
+  for (int i = 0; i < 7; ++i) offsets[i] = off[i];
   return Q8_OK;
 }
 
 static q8::MoeWs moe_ws_ptrs(void* ws, int E, int T, int topk, int64_t F, int64_t M) {
-  size_t off[7];
+  size_t off[q8::kMoeWsAreas];
   q8::moe_ws_layout(E, T, topk, F, M, off);
   char* b = (char*)ws;
   q8::MoeWs w;
@@ -286,8 +290,10 @@ static q8::MoeWs moe_ws_ptrs(void* ws, int E, int T, int topk, int64_t F, int64_
   w.pairs = (int32_t*)(b + off[2]);
   w.active = (int32_t*)(b + off[3]);
   w.n_active = (int32_t*)(b + off[4]);
+  w.n_vslots = w.n_active + 1;
   w.h = F > 0 ? (float*)(b + off[5]) : nullptr;
   w.y_pair = (float*)(b + off[6]);
+  w.vslots = (int32_t*)(b + off[7]);
   return w;
 }
 
@@ -313,6 +319,8 @@ int q8_moe_gemv(const q8_bank* W, const int32_t* expert_ids, const float* gate_w
   if (!aligned(x, 16) || !aligned(y, 4)) return Q8_ERR_ALIGN;
   const int P = T * topk;
   const int64_t M = W->e0.M, K = W->e0.K;
+  // the routed row space (virtual slots x rows) is indexed in 32 bits
+  if ((int64_t)q8::moe_max_vslots(W->E, P) * M > INT32_MAX) return Q8_ERR_SHAPE;
   if (!ws || !aligned(ws, 16) || ws_bytes < q8_moe_ws_bytes(W->E, T, topk, 0, M))
     return Q8_ERR_WORKSPACE;
   const size_t xbytes = (size_t)(x_per_pair ? P : T) * K * xs;
@@ -324,13 +332,13 @@ int q8_moe_gemv(const q8_bank* W, const int32_t* expert_ids, const float* gate_w
   rc = current_device(&dev);
   if (rc) return rc;
   const bool xf = x_dt == Q8_DT_F32;
-  if (q8::max_tokens_per_pass(*dev, K, xf) < 4) return Q8_ERR_SHAPE;
+  if (!q8::moe_fits(*dev, K, xf)) return Q8_ERR_SHAPE;
   q8::MoeWs w = moe_ws_ptrs(ws, W->E, T, topk, 0, M);
   float* yp = gate_w ? w.y_pair : y;
   hipStream_t s = (hipStream_t)stream;
   if (q8::launch_moe_route(expert_ids, W->E, P, w, gate_w ? nullptr : y, M, s) != hipSuccess)
     return Q8_ERR_LAUNCH;
-  if (q8::launch_moe_gemv(*dev, to_hb(W), w, P, topk, x, xf, x_per_pair != 0, yp, s) !=
+  if (q8::launch_moe_gemv(*dev, to_hb(W), w, topk, x, xf, x_per_pair != 0, yp, s) !=
       hipSuccess)
     return Q8_ERR_LAUNCH;
   if (gate_w)
@@ -350,6 +358,8 @@ int q8_moe_ffn(const q8_bank* gate, const q8_bank* up, const q8_bank* down,
   if (up->e0.M != F || up->e0.K != H || down->e0.M != H || down->e0.K != F) return Q8_ERR_SHAPE;
   rc = check_routing(expert_ids, gate_w, T, topk, E, true);
   if (rc) return rc;
+  if ((int64_t)q8::moe_max_vslots(E, T * topk) * (2 * F > H ? 2 * F : H) > INT32_MAX)
+    return Q8_ERR_SHAPE;
   if (!x || !out) return Q8_ERR_NULL;
   const size_t xs = dt_size(x_dt);
   if (!xs) return Q8_ERR_DTYPE;
@@ -364,16 +374,15 @@ int q8_moe_ffn(const q8_bank* gate, const q8_bank* up, const q8_bank* down,
   rc = current_device(&dev);
   if (rc) return rc;
   const bool xf = x_dt == Q8_DT_F32;
-  if (q8::max_tokens_per_pass(*dev, H, xf) < 4 || q8::max_tokens_per_pass(*dev, F, true) < 4)
-    return Q8_ERR_SHAPE;
+  if (!q8::moe_fits(*dev, H, xf) || !q8::moe_fits(*dev, F, true)) return Q8_ERR_SHAPE;
   const int P = T * topk;
   q8::MoeWs w = moe_ws_ptrs(ws, E, T, topk, F, H);
   hipStream_t s = (hipStream_t)stream;
   if (q8::launch_moe_route(expert_ids, E, P, w, nullptr, 0, s) != hipSuccess) return Q8_ERR_LAUNCH;
-  if (q8::launch_moe_gate_up(*dev, to_hb(gate), to_hb(up), w, P, topk, x, xf, w.h, s) !=
+  if (q8::launch_moe_gate_up(*dev, to_hb(gate), to_hb(up), w, topk, x, xf, w.h, s) !=
       hipSuccess)
     return Q8_ERR_LAUNCH;
-  if (q8::launch_moe_gemv(*dev, to_hb(down), w, P, topk, w.h, true, true, w.y_pair, s) !=
+  if (q8::launch_moe_gemv(*dev, to_hb(down), w, topk, w.h, true, true, w.y_pair, s) !=
       hipSuccess)
     return Q8_ERR_LAUNCH;
   return launch_rc(q8::launch_moe_combine(expert_ids, E, gate_w, w.y_pair, out, T, topk, H, s));

@@ -64,23 +64,31 @@ struct MoeWs {
   int32_t* pairs;    // [P]
   int32_t* active;   // [E]
   int32_t* n_active; // [1]
+  int32_t* n_vslots; // [1], after n_active
   float* h;          // [P][F] or null
   float* y_pair;     // [P][Mout] or null
+  int32_t* vslots;   // [moe_max_vslots(E, P)][8]: expert, token count, pair ids
 };
 
-size_t moe_ws_layout(int E, int T, int topk, int64_t F, int64_t M, size_t off[7]);
+// Areas of the workspace: the seven documented ones, then the slot records.
+constexpr int kMoeWsAreas = 8;
+size_t moe_ws_layout(int E, int T, int topk, int64_t F, int64_t M, size_t off[kMoeWsAreas]);
+int moe_max_vslots(int E, int P);
+// Whether a routed workgroup's LDS image of activations (the rows of the
+// tokens of the virtual slots it stages at once) fits for this K.
+bool moe_fits(const DevInfo& dev, int64_t K, bool x_f32);
 
 hipError_t launch_moe_route(const int32_t* ids, int E, int P, const MoeWs& ws, float* zero_rows,
                             int64_t zero_ld, hipStream_t s);
 // Routed GEMV over a bank: y_pair[p] = W[e_p] x[src(p)]; src(p) = p / topk
 // (x_per_pair false) or p. x fp16 or fp32.
-hipError_t launch_moe_gemv(const DevInfo& dev, const HBank& W, const MoeWs& ws, int P, int topk,
+hipError_t launch_moe_gemv(const DevInfo& dev, const HBank& W, const MoeWs& ws, int topk,
                            const void* x, bool x_f32, bool x_per_pair, float* y_pair,
                            hipStream_t s);
 // h[p] = silu(Wg[e_p] x_t) * (Wu[e_p] x_t), x fp16 [T][H].
 hipError_t launch_moe_gate_up(const DevInfo& dev, const HBank& G, const HBank& U,
-                              const MoeWs& ws, int P, int topk, const void* x, bool x_f32,
-                              float* h, hipStream_t s);
+                              const MoeWs& ws, int topk, const void* x, bool x_f32, float* h,
+                              hipStream_t s);
 // out[t] = sum_j gate_w[t][j] * y_pair[t*topk + j] (slots with invalid ids skipped).
 hipError_t launch_moe_combine(const int32_t* ids, int E, const float* gate_w,
                               const float* y_pair, float* out, int T, int topk, int64_t M,

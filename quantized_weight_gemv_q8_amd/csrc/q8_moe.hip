@@ -10,16 +10,20 @@
 //
 // Kernels:
 //  route    one workgroup: counts, offsets, expert-major pair list (stable:
-//           ascending pair id inside an expert) and the active-expert list.
-//  gate_up  grid (active-expert slot, row tile): the gate and up rows of the
-//           same output index are a team's two rows, so the epilogue has
-//           both sums in one lane and writes h = silu(g) * u.
-//  rows     grid (active-expert slot, row tile): y_pair[p] = W[e] x_p for a
-//           bank (the down projection, or a single routed GEMV).
+//           ascending pair id inside an expert), the active-expert list and
+//           the virtual slots: an active expert with up to kMoeNT of its
+//           pairs (an expert with more pairs gets several slots).
+//  gate_up  the rows of all virtual slots form one row space (a team's two
+//           rows are the gate and up rows of one output index, so the
+//           epilogue has both sums in one lane and writes h = silu(g) * u);
+//           each persistent workgroup streams one contiguous, equal slice
+//           of it, with the activations of the slots it touches staged once.
+//  rows     the same over a bank: y_pair[p] = W[e] x_p (the down
+//           projection, or a single routed GEMV).
 //  combine  out[t] = sum_j gate_w[t][j] * y_pair[t*topk + j], ascending j.
 // Per-(row, token) arithmetic is the engine's, which does not depend on
-// how many tokens an expert received, so a token's result is independent
-// of the rest of the batch.
+// how many tokens an expert received or which slot they landed in, so a
+// token's result is independent of the rest of the batch.
 #include "q8_engine.hpp"
 #include "q8_internal.h"
 
@@ -27,21 +31,55 @@ namespace q8 {
 
 constexpr int kRouteThreads = 1024;
 
-// Block-wide exclusive scan of one int per thread (kRouteThreads threads).
-__device__ __forceinline__ int block_exclusive_scan(int v, int* tmp, int* total) {
-  const int t = threadIdx.x;
-  tmp[t] = v;
-  __syncthreads();
-  for (int off = 1; off < kRouteThreads; off <<= 1) {
-    const int add = t >= off ? tmp[t - off] : 0;
-    __syncthreads();
-    tmp[t] += add;
-    __syncthreads();
+// Tokens per virtual slot. Most experts receive one or two tokens (128
+// pairs over ~90 active experts at 128 experts, top-8, 16 tokens); an
+// expert with more takes several slots, the later ones re-reading its rows.
+// Two per slot was the fastest of 1, 2, 3 and 4 in same-process A/B on
+// MI355X for that layer (95 us against 113 us for 4: the smaller
+// accumulator set raises occupancy by more than the re-reads cost).
+constexpr int kMoeNT = 2;
+// Virtual slot record: [0] expert, [1] token count, [2 .. 2+kMoeNT) pair
+// ids; 32 bytes.
+constexpr int kVSlotInts = 8;
+static_assert(2 + kMoeNT <= kVSlotInts, "slot record");
+// Slots staged together by one workgroup (a slice no longer than one
+// slot's rows touches at most two).
+constexpr int kSegV = 2;
+
+// Block-wide exclusive scan of three ints per thread (kRouteThreads
+// threads): inclusive scans inside each wave by shuffles, then the wave
+// totals from LDS. Two barriers in all.
+constexpr int kRouteWaves = kRouteThreads / kWave;
+
+__device__ __forceinline__ void block_exclusive_scan3(int v[3], int (*wtot)[3], int total[3]) {
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  int incl[3] = {v[0], v[1], v[2]};
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      const int o = __shfl_up(incl[i], off, kWave);
+      if (lane >= off) incl[i] += o;
+    }
   }
-  const int incl = tmp[t];
-  *total = tmp[kRouteThreads - 1];
+  if (lane == kWave - 1) {
+#pragma unroll
+    for (int i = 0; i < 3; ++i) wtot[wave][i] = incl[i];
+  }
   __syncthreads();
-  return incl - v;
+  int before[3] = {0, 0, 0};
+#pragma unroll
+  for (int i = 0; i < 3; ++i) total[i] = 0;
+  for (int w = 0; w < kRouteWaves; ++w) {
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      if (w < wave) before[i] += wtot[w][i];
+      total[i] += wtot[w][i];
+    }
+  }
+  __syncthreads();  // wtot may be reused
+#pragma unroll
+  for (int i = 0; i < 3; ++i) v[i] = before[i] + incl[i] - v[i];
 }
 
 // Expert-major CSR of the routed pairs in one workgroup: counts by LDS
@@ -52,7 +90,7 @@ __global__ __launch_bounds__(kRouteThreads) void moe_route_kernel(const int32_t*
                                                                  MoeWs ws, float* zero_rows,
                                                                  int64_t zero_ld) {
   extern __shared__ int32_t sm[];
-  __shared__ int scan_tmp[kRouteThreads];
+  __shared__ int wtot[kRouteWaves][3];
   int32_t* cnt = sm;              // [E]
   int32_t* off = cnt + E;         // [E+1]
   int32_t* cur = off + E + 1;     // [E]
@@ -68,19 +106,20 @@ __global__ __launch_bounds__(kRouteThreads) void moe_route_kernel(const int32_t*
   for (int p = t; p < P; p += kRouteThreads)
     if (sid[p] >= 0) atomicAdd(&cnt[sid[p]], 1);
   __syncthreads();
-  // each thread owns a contiguous run of experts
+  // Each thread owns a contiguous run of experts: its pairs, its active
+  // experts and its virtual slots are placed after those of lower runs.
   const int per = (E + kRouteThreads - 1) / kRouteThreads;
-  const int e0 = t * per, e1 = e0 + per < E ? e0 + per : E;
-  int sum = 0, act = 0;
+  const int e0 = t * per < E ? t * per : E, e1 = e0 + per < E ? e0 + per : E;
+  int v[3] = {0, 0, 0};  // pairs, active experts, virtual slots
   for (int e = e0; e < e1; ++e) {
-    sum += cnt[e];
-    act += cnt[e] > 0;
+    v[0] += cnt[e];
+    v[1] += cnt[e] > 0;
+    v[2] += (cnt[e] + kMoeNT - 1) / kMoeNT;
   }
-  int total_pairs, total_active;
-  const int base = block_exclusive_scan(sum, scan_tmp, &total_pairs);
-  const int abase = block_exclusive_scan(act, scan_tmp, &total_active);
+  int total[3];
+  block_exclusive_scan3(v, wtot, total);
   {
-    int o = base, a = abase;
+    int o = v[0], a = v[1];
     for (int e = e0; e < e1; ++e) {
       off[e] = o;
       cur[e] = o;
@@ -91,9 +130,10 @@ __global__ __launch_bounds__(kRouteThreads) void moe_route_kernel(const int32_t*
     }
   }
   if (t == 0) {
-    off[E] = total_pairs;
-    ws.offsets[E] = total_pairs;
-    *ws.n_active = total_active;
+    off[E] = total[0];
+    ws.offsets[E] = total[0];
+    *ws.n_active = total[1];
+    *ws.n_vslots = total[2];
   }
   __syncthreads();
   for (int p = t; p < P; p += kRouteThreads) {
@@ -105,18 +145,36 @@ __global__ __launch_bounds__(kRouteThreads) void moe_route_kernel(const int32_t*
     }
   }
   __syncthreads();
-  for (int e = t; e < E; e += kRouteThreads) {
+  // Ascending pair order inside each expert, so the result does not depend
+  // on the order the atomics happened in (insertion sort: segments are
+  // short). The owner of a run sorts it, then writes its pairs and slots.
+  for (int e = e0; e < e1; ++e) {
     const int lo = off[e], hi = off[e + 1];
-    for (int i = lo + 1; i < hi; ++i) {  // insertion sort: segments are short
-      const int v = tmp[i];
+    for (int i = lo + 1; i < hi; ++i) {
+      const int x = tmp[i];
       int j = i - 1;
-      while (j >= lo && tmp[j] > v) {
+      while (j >= lo && tmp[j] > x) {
         tmp[j + 1] = tmp[j];
         --j;
       }
-      tmp[j + 1] = v;
+      tmp[j + 1] = x;
     }
     for (int i = lo; i < hi; ++i) ws.pairs[i] = tmp[i];
+  }
+  int vs = v[2];
+  for (int e = e0; e < e1; ++e) {
+    for (int k = 0; k < cnt[e]; k += kMoeNT) {
+      int rec[kVSlotInts];
+      const int nt = cnt[e] - k < kMoeNT ? cnt[e] - k : kMoeNT;
+      rec[0] = e;
+      rec[1] = nt;
+#pragma unroll
+      for (int n = 0; n < kVSlotInts - 2; ++n) rec[2 + n] = n < nt ? tmp[off[e] + k + n] : -1;
+      int4* dst = reinterpret_cast<int4*>(ws.vslots + (size_t)vs * kVSlotInts);
+      dst[0] = make_int4(rec[0], rec[1], rec[2], rec[3]);
+      dst[1] = make_int4(rec[4], rec[5], rec[6], rec[7]);
+      ++vs;
+    }
   }
 }
 
@@ -135,30 +193,6 @@ __device__ __forceinline__ ExpertMat expert_of(const HBank& b, int e) {
   m.ld_d = b.e0.ld_d;
   return m;
 }
-
-struct SingleMap {
-  ExpertMat w;
-  int64_t M;      // rows of the expert matrix
-  int64_t r_end;  // end of this workgroup's row tile
-  __device__ __forceinline__ bool row(int64_t i, const int8_t*& q, const uint16_t*& d) const {
-    q = w.qs + i * w.ld_qs;
-    d = w.d + i * w.ld_d;
-    return i < r_end;
-  }
-};
-
-// virtual row i = 2*rho + s: s = 0 gate row rho, s = 1 up row rho
-struct GateUpMap {
-  ExpertMat g, u;
-  int64_t r_end;  // end (virtual rows) of this tile
-  __device__ __forceinline__ bool row(int64_t i, const int8_t*& q, const uint16_t*& d) const {
-    const int64_t rho = i >> 1;
-    const bool up = (i & 1) != 0;
-    q = up ? u.qs + rho * u.ld_qs : g.qs + rho * g.ld_qs;
-    d = up ? u.d + rho * u.ld_d : g.d + rho * g.ld_d;
-    return i < r_end;
-  }
-};
 
 struct PairOutEpi {  // y[pid[n]][row] = v for live tokens n < nt
   float* y;
@@ -199,111 +233,273 @@ struct SiluMulEpi {  // values come in (gate, up) pairs for one token
   }
 };
 
-// Tokens per pass for routed experts (most experts receive one or two
-// tokens: 128 pairs over ~80 active experts). An expert with more tokens
-// takes several passes over its tile, the later ones served from L2. The
-// load window is one chunk (D = 1). Both were picked by same-process A/B
-// on MI355X for the 128-expert top-8 T=16 layer (184 -> 134 us against a
-// 2-token pass with D = 4; wider passes and other tile sizes were slower).
-constexpr int kMoeNT = 4;
+// ---------------------------------------------------------------- routed stream
+// The row engine's inner loop, over the groups [g_begin, g_end) of the
+// virtual-slot row space (group g covers rows (g % gpv) * G .. of slot
+// g / gpv; rows at or past rpv are dead). Each group takes its expert, its
+// token count and the LDS image of its tokens from the segment tables:
+// slot v0 + j has expert seg_e[j], seg_nt[j] tokens, pair ids
+// seg_pid[j * NT ..], and its tokens' activations at LDS block j * NT.
+// Same per-lane chunk order, accumulation and team reduction as the dense
+// engine, so each (row, token) result is the dense result.
+template <int NT, int LPR, int R, int D, int MINC, bool XF32, class RowOf, class Epi, class Stage>
+__device__ __forceinline__ void run_routed(const RowOf& rowof, Epi& epi, const uint4* lds, int C,
+                                           int g_begin, int g_end, int gpv, int rpv, int v0,
+                                           const int32_t* seg_e, const int32_t* seg_nt,
+                                           const int32_t* seg_pid, Stage&& stage) {
+  constexpr int RPW = kWave / LPR;
+  constexpr int G = RPW * R;
+  constexpr int V = NT * R;
+  constexpr int VP = Pow2<V>::value;
+  using Shape = ReduceShape<LPR, VP, MINC>;
+  constexpr int P = XPlanes<XF32>::P;
+  constexpr int S = kWavesPerBlock;  // waves of the workgroup take groups in turn
 
-template <int NT, bool XF32, int R, int D, int MINC, int LPR, class Map, class Epi>
-__device__ __forceinline__ void expert_pass(const Map& map, Epi& epi, const char* x,
-                                            int64_t ldx_bytes, bool x_per_pair, int topk,
-                                            const int32_t* pid_lds, int C, int64_t r_begin,
-                                            int64_t r_end, uint4* lds, int nt) {
-  constexpr int G = (kWave / LPR) * R;
-  const int64_t n_groups = (r_end - r_begin + G - 1) / G;
-  auto stage = [=]() {
-    const char* rows[NT];
+  const int wave = threadIdx.x / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int p = lane % LPR;
+  const int team = lane / LPR;
+  const int CPL = (C + LPR - 1) / LPR;
+
+  const int g_first = g_begin + wave;
+  const int my_groups = g_first < g_end ? (g_end - g_first + S - 1) / S : 0;
+  const int total = my_groups * CPL;
+  const int padded = (total + D - 1) / D * D;
+
+  Slot<R> slot[D];
+  // issue cursor: group ig = slot iv, group il inside the slot, chunk ij
+  int ig = g_first, iv = g_first / gpv, il = g_first - (g_first / gpv) * gpv, ij = 0;
+  const int8_t* iq[R];
+  const uint16_t* id[R];
+  bool iok[R];
+  auto refresh = [&]() {
+    const bool live = ig < g_end;
+    const int e = live ? seg_e[iv - v0] : 0;
+    const int rb = il * G + team * R;
 #pragma unroll
-    for (int n = 0; n < NT; ++n) {
-      const int p = n < nt ? pid_lds[n] : 0;
-      const int src = x_per_pair ? p : p / topk;
-      rows[n] = x + (int64_t)src * ldx_bytes;
-    }
-    stage_x<NT, XF32>(rows, C, lds, nt);
-    __syncthreads();
+    for (int r = 0; r < R; ++r) iok[r] = live && rb + r < rpv && rowof(e, rb + r, iq[r], id[r]);
   };
-  run_rows<NT, LPR, R, D, MINC, XF32>(map, epi, lds, C, n_groups, threadIdx.x / kWave,
-                                      kWavesPerBlock, r_begin, stage, nt);
+  refresh();
+  auto issue = [&](Slot<R>& sl) {
+    const int c = p + LPR * ij;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      if (iok[r] && c < C) {
+        sl.q[r] = load_stream16(iq[r] + (int64_t)c * 16);
+        sl.d[r] = id[r][c >> 1];
+      } else {
+        sl.q[r] = make_uint4(0, 0, 0, 0);
+        sl.d[r] = 0;
+      }
+    }
+    if (++ij == CPL) {
+      ij = 0;
+      ig += S;
+      il += S;
+      while (il >= gpv) {
+        il -= gpv;
+        ++iv;
+      }
+      refresh();
+    }
+  };
+
+#pragma unroll
+  for (int s = 0; s < D; ++s) issue(slot[s]);
+  stage();
+
+  float acc[VP];
+#pragma unroll
+  for (int i = 0; i < VP; ++i) acc[i] = 0.0f;
+  // compute cursor and the group's token context
+  int cg = g_first, cv = iv, cl = 0, cj = 0;
+  cv = g_first / gpv;
+  cl = g_first - cv * gpv;
+  int nt = 0;
+  const uint4* xb = lds;
+  auto context = [&]() {
+    if (cg < g_end) {
+      const int j = cv - v0;
+      nt = __builtin_amdgcn_readfirstlane(seg_nt[j]);
+      xb = lds + (size_t)j * NT * P * C;
+    }
+  };
+  context();
+
+  for (int it = 0; it < padded; it += D) {
+#pragma unroll
+    for (int s = 0; s < D; ++s) {
+      const int c = p + LPR * cj;
+      if (c < C) {
+        float df[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) df[r] = half_bits_to_float((uint16_t)slot[s].d[r]);
+        if constexpr (!XF32) {
+          h2_t qh[R][8];
+#pragma unroll
+          for (int r = 0; r < R; ++r) quants_to_h2(slot[s].q[r], qh[r]);
+#pragma unroll
+          for (int n = 0; n < NT; ++n) {
+            if (n >= nt) break;
+            const uint4 xlo = xb[(n * P + 0) * C + c];
+            const uint4 xhi = xb[(n * P + 1) * C + c];
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+              const float sum = dot16_f16(qh[r], xlo, xhi);
+              acc[n * R + r] = __builtin_fmaf(df[r], sum, acc[n * R + r]);
+            }
+          }
+        } else {
+          float qf[R][16];
+#pragma unroll
+          for (int r = 0; r < R; ++r) quants_to_f32(slot[s].q[r], qf[r]);
+#pragma unroll
+          for (int n = 0; n < NT; ++n) {
+            if (n >= nt) break;
+            const float4 x0 = __builtin_bit_cast(float4, xb[(n * P + 0) * C + c]);
+            const float4 x1 = __builtin_bit_cast(float4, xb[(n * P + 1) * C + c]);
+            const float4 x2 = __builtin_bit_cast(float4, xb[(n * P + 2) * C + c]);
+            const float4 x3 = __builtin_bit_cast(float4, xb[(n * P + 3) * C + c]);
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+              const float sum = dot16_f32(qf[r], x0, x1, x2, x3);
+              acc[n * R + r] = __builtin_fmaf(df[r], sum, acc[n * R + r]);
+            }
+          }
+        }
+      }
+      issue(slot[s]);
+      if (++cj == CPL) {
+        if (cg < g_end) {
+          int base = 0;
+          TeamReduce<VP, MINC, LPR / 2>::run(acc, p, base);
+          const bool owner = (p & Shape::OWNER_MASK) == 0;
+          epi.pid = seg_pid + (cv - v0) * NT;
+          epi.nt = nt;
+          epi.template emit<NT, R, Shape::CNT>(cl * G + team * R, base, owner, acc);
+        }
+#pragma unroll
+        for (int i = 0; i < VP; ++i) acc[i] = 0.0f;
+        cj = 0;
+        cg += S;
+        cl += S;
+        while (cl >= gpv) {
+          cl -= gpv;
+          ++cv;
+        }
+        context();
+      }
+    }
+  }
 }
 
-// Persistent loop over work items (active-expert slot, row tile); for each,
-// passes of up to kMoeNT of the expert's routed pairs.
-template <bool XF32, int MINC, int LPR, int RFIX, class MakeMap, class Epi>
-__device__ __forceinline__ void expert_items(const MoeWs& ws, int64_t tiles, int64_t rows_per_tile,
-                                             int64_t rows_total, const MakeMap& make_map, Epi& epi,
-                                             const char* x, int64_t ldx_bytes, bool x_per_pair,
-                                             int topk, int C, int32_t* pid_lds, uint4* lds) {
-  const int64_t items = (int64_t)__builtin_amdgcn_readfirstlane(*ws.n_active) * tiles;
-  for (int64_t wi = blockIdx.x; wi < items; wi += gridDim.x) {
-    const int slot = (int)(wi / tiles);
-    const int64_t tile = wi - (int64_t)slot * tiles;
-    const int e = __builtin_amdgcn_readfirstlane(ws.active[slot]);
-    const int o0 = __builtin_amdgcn_readfirstlane(ws.offsets[e]);
-    const int ne = __builtin_amdgcn_readfirstlane(ws.offsets[e + 1]) - o0;
-    const int64_t r_begin = tile * rows_per_tile;
-    const int64_t r_end = r_begin + rows_per_tile < rows_total ? r_begin + rows_per_tile : rows_total;
-    const auto map = make_map(e, r_end);
-    epi.r_end = r_end;
-    for (int t0 = 0; t0 < ne; t0 += kMoeNT) {
-      const int nt = ne - t0 < kMoeNT ? ne - t0 : kMoeNT;
-      __syncthreads();  // previous pass done with pid_lds and the LDS x image
-      if (threadIdx.x < nt) pid_lds[threadIdx.x] = ws.pairs[o0 + t0 + threadIdx.x];
-      __syncthreads();
-      epi.pid = pid_lds;
-      epi.nt = nt;
-      expert_pass<kMoeNT, XF32, (RFIX ? RFIX : Tune<kMoeNT, false>::R), 1, MINC, LPR>(
-          map, epi, x, ldx_bytes, x_per_pair, topk, pid_lds, C, r_begin, r_end, lds, nt);
+// Workgroup b streams groups [b*n/grid, (b+1)*n/grid) of the n = n_vslots *
+// gpv groups, in segments of at most kSegV virtual slots: load the
+// segments' slot records, issue the first weight loads, stage the
+// activations of their tokens (x row p / topk, or p when x holds one row
+// per pair), then stream.
+template <int NT, int LPR, int R, int MINC, bool XF32, class RowOf, class Epi>
+__device__ __forceinline__ void routed_slices(const MoeWs& ws, const RowOf& rowof, Epi& epi,
+                                              const char* x, int64_t ldx_bytes, bool x_per_pair,
+                                              int topk, int C, int rpv, uint4* lds) {
+  __shared__ int32_t seg_e[kSegV], seg_nt[kSegV], seg_pid[kSegV * NT];
+  static_assert(NT == kMoeNT, "slot records hold kMoeNT pairs");
+  constexpr int G = (kWave / LPR) * R;
+  constexpr int P = XPlanes<XF32>::P;
+  const int gpv = (rpv + G - 1) / G;
+  const int nv = __builtin_amdgcn_readfirstlane(*ws.n_vslots);
+  const int n_groups = nv * gpv;
+  const int g_lo = (int)((int64_t)blockIdx.x * n_groups / gridDim.x);
+  const int g_hi = (int)((int64_t)(blockIdx.x + 1) * n_groups / gridDim.x);
+  for (int g = g_lo; g < g_hi;) {
+    const int v0 = g / gpv;
+    const int v1 = v0 + kSegV < nv ? v0 + kSegV : nv;
+    const int seg_end = g_hi < v1 * gpv ? g_hi : v1 * gpv;
+    __syncthreads();  // the previous segment is done with the tables and the LDS image
+    if (threadIdx.x < kSegV) {
+      const int j = threadIdx.x;
+      const int v = v0 + j;
+      int4 a = make_int4(0, 0, -1, -1), b = make_int4(-1, -1, -1, -1);
+      if (v < v1) {
+        const int4* rec = reinterpret_cast<const int4*>(ws.vslots + (size_t)v * kVSlotInts);
+        a = rec[0];
+        b = rec[1];
+      }
+      const int r[kVSlotInts] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+      seg_e[j] = r[0];
+      seg_nt[j] = r[1];
+#pragma unroll
+      for (int n = 0; n < NT; ++n) seg_pid[j * NT + n] = n < r[1] ? r[2 + n] : -1;
     }
+    __syncthreads();
+    auto stage = [&]() {
+      for (int i = 0; i < kSegV * NT; ++i) {
+        const int pid = seg_pid[i];
+        if (pid < 0) continue;
+        const int src = x_per_pair ? pid : pid / topk;
+        const uint4* row = reinterpret_cast<const uint4*>(x + (int64_t)src * ldx_bytes);
+        for (int k = threadIdx.x; k < C * P; k += kBlock) {
+          const int c = k / P, h = k - c * P;
+          lds[(i * P + h) * C + c] = row[k];
+        }
+      }
+      __syncthreads();
+    };
+    run_routed<NT, LPR, R, 1, MINC, XF32>(rowof, epi, lds, C, g, seg_end, gpv, rpv, v0, seg_e,
+                                          seg_nt, seg_pid, stage);
+    g = seg_end;
   }
 }
 
 template <int LPR, bool XF32>
 __global__ __launch_bounds__(kBlock) void moe_rows_kernel(HBank W, MoeWs ws, int topk,
                                                          const char* x, int64_t ldx_bytes,
-                                                         int x_per_pair, float* y, int64_t tiles,
-                                                         int64_t rows_per_tile) {
+                                                         int x_per_pair, float* y) {
   extern __shared__ uint4 lds_x[];
-  __shared__ int32_t pid_lds[kMoeNT];
-  const int64_t M = W.e0.M;
+  const int M = (int)W.e0.M;
   PairOutEpi epi;
   epi.y = y;
   epi.ld = M;
-  epi.pid = pid_lds;
-  auto make_map = [&](int e, int64_t r_end) {
-    SingleMap m;
-    m.w = expert_of(W, e);
-    m.M = M;
-    m.r_end = r_end;
-    return m;
+  epi.r_end = M;
+  epi.pid = nullptr;
+  epi.nt = 0;
+  auto rowof = [W](int e, int i, const int8_t*& q, const uint16_t*& d) {
+    q = W.e0.qs + (int64_t)e * W.stride_qs + (int64_t)i * W.e0.ld_qs;
+    d = W.e0.d + (int64_t)e * W.stride_d + (int64_t)i * W.e0.ld_d;
+    return true;
   };
-  expert_items<XF32, 1, LPR, 0>(ws, tiles, rows_per_tile, M, make_map, epi, x, ldx_bytes,
-                                x_per_pair != 0, topk, (int)(W.e0.K / 16), pid_lds, lds_x);
+  routed_slices<kMoeNT, LPR, Tune<kMoeNT, false>::R, 1, XF32>(
+      ws, rowof, epi, x, ldx_bytes, x_per_pair != 0, topk, (int)(W.e0.K / 16), M, lds_x);
 }
 
+// virtual row i = 2*rho + s: s = 0 gate row rho, s = 1 up row rho
 template <int LPR, bool XF32>
 __global__ __launch_bounds__(kBlock) void moe_gate_up_kernel(HBank Gb, HBank Ub, MoeWs ws,
                                                             int topk, const char* x,
-                                                            int64_t ldx_bytes, float* h,
-                                                            int64_t tiles, int64_t rows_per_tile) {
+                                                            int64_t ldx_bytes, float* h) {
   extern __shared__ uint4 lds_x[];
-  __shared__ int32_t pid_lds[kMoeNT];
-  const int64_t F = Gb.e0.M;
+  const int F = (int)Gb.e0.M;
   SiluMulEpi epi;
   epi.h = h;
   epi.ld = F;
-  epi.pid = pid_lds;
-  auto make_map = [&](int e, int64_t r_end) {
-    GateUpMap m;
-    m.g = expert_of(Gb, e);
-    m.u = expert_of(Ub, e);
-    m.r_end = r_end;
-    return m;
+  epi.r_end = 2 * F;
+  epi.pid = nullptr;
+  epi.nt = 0;
+  auto rowof = [Gb, Ub](int e, int i, const int8_t*& q, const uint16_t*& d) {
+    const int64_t rho = i >> 1;
+    const bool up = (i & 1) != 0;
+    const int8_t* q0 = up ? Ub.e0.qs : Gb.e0.qs;
+    const uint16_t* d0 = up ? Ub.e0.d : Gb.e0.d;
+    const int64_t sq = up ? Ub.stride_qs : Gb.stride_qs;
+    const int64_t sd = up ? Ub.stride_d : Gb.stride_d;
+    const int64_t lq = up ? Ub.e0.ld_qs : Gb.e0.ld_qs;
+    const int64_t ld = up ? Ub.e0.ld_d : Gb.e0.ld_d;
+    q = q0 + (int64_t)e * sq + rho * lq;
+    d = d0 + (int64_t)e * sd + rho * ld;
+    return true;
   };
-  expert_items<XF32, 2, LPR, 2>(ws, tiles, rows_per_tile, 2 * F, make_map, epi, x, ldx_bytes,
-                                false, topk, (int)(Gb.e0.K / 16), pid_lds, lds_x);
+  routed_slices<kMoeNT, LPR, 2, 2, XF32>(ws, rowof, epi, x, ldx_bytes, false, topk,
+                                         (int)(Gb.e0.K / 16), 2 * F, lds_x);
 }
 
 __global__ __launch_bounds__(256) void moe_combine_kernel(const int32_t* ids, int E,
@@ -334,7 +530,18 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(const int32_t* ids, in
 // ---------------------------------------------------------------- host side
 static int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
 
-size_t moe_ws_layout(int E, int T, int topk, int64_t F, int64_t M, size_t off[7]) {
+static size_t moe_lds_bytes(int64_t K, bool x_f32) {
+  return (size_t)kSegV * kMoeNT * (size_t)(K / 16) * 16 * (x_f32 ? 4 : 2);
+}
+
+// The segment tables and the engine's other static LDS take well under 1 KiB.
+bool moe_fits(const DevInfo& dev, int64_t K, bool x_f32) {
+  return moe_lds_bytes(K, x_f32) + 1024 <= dev.lds_per_block;
+}
+
+int moe_max_vslots(int E, int P) { return (E < P ? E : P) + P / kMoeNT + 1; }
+
+size_t moe_ws_layout(int E, int T, int topk, int64_t F, int64_t M, size_t off[kMoeWsAreas]) {
   const int64_t P = (int64_t)T * topk;
   size_t o = 0;
   auto take = [&](size_t bytes) {
@@ -346,9 +553,10 @@ size_t moe_ws_layout(int E, int T, int topk, int64_t F, int64_t M, size_t off[7]
   off[1] = take(4 * (size_t)(E + 1));
   off[2] = take(4 * (size_t)P);
   off[3] = take(4 * (size_t)E);
-  off[4] = take(4);
+  off[4] = take(8);  // n_active, n_vslots
   off[5] = take(F > 0 ? 4 * (size_t)P * (size_t)F : 0);
   off[6] = take(4 * (size_t)P * (size_t)M);
+  off[7] = take(4 * (size_t)kVSlotInts * (size_t)moe_max_vslots(E, (int)P));
   return o;
 }
 
@@ -365,45 +573,30 @@ hipError_t launch_moe_route(const int32_t* ids, int E, int P, const MoeWs& ws, f
   return hipLaunchKernel((const void*)moe_route_kernel, dim3(1), dim3(kRouteThreads), args, lds, s);
 }
 
-// Row tiles per expert: enough work items (active experts x tiles) to give
-// each resident workgroup several, each tile at least one group per wave.
-static void plan_tiles(int64_t blocks, int slots, int64_t rows, int64_t group_rows, int64_t* tiles,
-                       int64_t* rows_per_tile) {
-  const int64_t min_rows = group_rows * kWavesPerBlock;
-  int64_t t = (6 * blocks + slots - 1) / slots;
-  const int64_t max_t = (rows + min_rows - 1) / min_rows;
-  if (t > max_t) t = max_t;
-  if (t < 1) t = 1;
-  int64_t rpt = (rows + t - 1) / t;
-  rpt = round_up(rpt, group_rows);
-  *rows_per_tile = rpt;
-  *tiles = (rows + rpt - 1) / rpt;
-}
-
-template <int LPR, bool XF32>
-static hipError_t moe_rows_t(const DevInfo& dev, const HBank& W, const MoeWs& ws, int P, int topk,
-                             const char* x, int64_t ldx_bytes, int x_per_pair, float* y,
-                             hipStream_t s) {
-  const int slots = P < W.E ? P : W.E;
-  const int64_t M = W.e0.M;
-  const size_t lds = (size_t)kMoeNT * (W.e0.K / 16) * 16 * XPlanes<XF32>::P;
-  auto fn = moe_rows_kernel<LPR, XF32>;
+template <class Fn>
+static hipError_t moe_launch(Fn fn, size_t lds, void** args, hipStream_t s, const DevInfo& dev) {
   if (lds > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize,
                                        (int)lds);
     if (e != hipSuccess) return e;
   }
   const int64_t blocks = (int64_t)dev.cus * blocks_per_cu((const void*)fn, lds);
-  int64_t tiles, rpt;
-  plan_tiles(blocks, slots, M, (kWave / LPR) * Tune<kMoeNT, false>::R, &tiles, &rpt);
-  int64_t grid = slots * tiles < blocks ? slots * tiles : blocks;
-  HBank w = W;
-  MoeWs wsv = ws;
-  void* args[] = {&w, &wsv, &topk, (void*)&x, &ldx_bytes, &x_per_pair, &y, &tiles, &rpt};
-  return hipLaunchKernel((const void*)fn, dim3((unsigned)grid), dim3(kBlock), args, lds, s);
+  return hipLaunchKernel((const void*)fn, dim3((unsigned)(blocks > 0 ? blocks : 1)), dim3(kBlock),
+                         args, lds, s);
 }
 
-hipError_t launch_moe_gemv(const DevInfo& dev, const HBank& W, const MoeWs& ws, int P, int topk,
+template <int LPR, bool XF32>
+static hipError_t moe_rows_t(const DevInfo& dev, const HBank& W, const MoeWs& ws, int topk,
+                             const char* x, int64_t ldx_bytes, int x_per_pair, float* y,
+                             hipStream_t s) {
+  const size_t lds = moe_lds_bytes(W.e0.K, XF32);
+  HBank w = W;
+  MoeWs wsv = ws;
+  void* args[] = {&w, &wsv, &topk, (void*)&x, &ldx_bytes, &x_per_pair, &y};
+  return moe_launch(moe_rows_kernel<LPR, XF32>, lds, args, s, dev);
+}
+
+hipError_t launch_moe_gemv(const DevInfo& dev, const HBank& W, const MoeWs& ws, int topk,
                            const void* x, bool x_f32, bool x_per_pair, float* y_pair,
                            hipStream_t s) {
   const int64_t ldx_bytes = W.e0.K * (x_f32 ? 4 : 2);
@@ -411,52 +604,39 @@ hipError_t launch_moe_gemv(const DevInfo& dev, const HBank& W, const MoeWs& ws, 
   const int lpr = lanes_per_row(W.e0.K);
   const int xpp = x_per_pair ? 1 : 0;
   if (x_f32) {
-    if (lpr == 64) return moe_rows_t<64, true>(dev, W, ws, P, topk, xp, ldx_bytes, xpp, y_pair, s);
-    if (lpr == 32) return moe_rows_t<32, true>(dev, W, ws, P, topk, xp, ldx_bytes, xpp, y_pair, s);
-    return moe_rows_t<16, true>(dev, W, ws, P, topk, xp, ldx_bytes, xpp, y_pair, s);
+    if (lpr == 64) return moe_rows_t<64, true>(dev, W, ws, topk, xp, ldx_bytes, xpp, y_pair, s);
+    if (lpr == 32) return moe_rows_t<32, true>(dev, W, ws, topk, xp, ldx_bytes, xpp, y_pair, s);
+    return moe_rows_t<16, true>(dev, W, ws, topk, xp, ldx_bytes, xpp, y_pair, s);
   }
-  if (lpr == 64) return moe_rows_t<64, false>(dev, W, ws, P, topk, xp, ldx_bytes, xpp, y_pair, s);
-  if (lpr == 32) return moe_rows_t<32, false>(dev, W, ws, P, topk, xp, ldx_bytes, xpp, y_pair, s);
-  return moe_rows_t<16, false>(dev, W, ws, P, topk, xp, ldx_bytes, xpp, y_pair, s);
+  if (lpr == 64) return moe_rows_t<64, false>(dev, W, ws, topk, xp, ldx_bytes, xpp, y_pair, s);
+  if (lpr == 32) return moe_rows_t<32, false>(dev, W, ws, topk, xp, ldx_bytes, xpp, y_pair, s);
+  return moe_rows_t<16, false>(dev, W, ws, topk, xp, ldx_bytes, xpp, y_pair, s);
 }
 
 template <int LPR, bool XF32>
 static hipError_t moe_gu_t(const DevInfo& dev, const HBank& G, const HBank& U, const MoeWs& ws,
-                           int P, int topk, const char* x, int64_t ldx_bytes, float* h,
-                           hipStream_t s) {
-  const int slots = P < G.E ? P : G.E;
-  const int64_t VR = 2 * G.e0.M;
-  const size_t lds = (size_t)kMoeNT * (G.e0.K / 16) * 16 * XPlanes<XF32>::P;
-  auto fn = moe_gate_up_kernel<LPR, XF32>;
-  if (lds > 64 * 1024) {
-    hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)lds);
-    if (e != hipSuccess) return e;
-  }
-  const int64_t blocks = (int64_t)dev.cus * blocks_per_cu((const void*)fn, lds);
-  int64_t tiles, rpt;
-  plan_tiles(blocks, slots, VR, (kWave / LPR) * 2, &tiles, &rpt);
-  int64_t grid = slots * tiles < blocks ? slots * tiles : blocks;
+                           int topk, const char* x, int64_t ldx_bytes, float* h, hipStream_t s) {
+  const size_t lds = moe_lds_bytes(G.e0.K, XF32);
   HBank g = G, u = U;
   MoeWs wsv = ws;
-  void* args[] = {&g, &u, &wsv, &topk, (void*)&x, &ldx_bytes, &h, &tiles, &rpt};
-  return hipLaunchKernel((const void*)fn, dim3((unsigned)grid), dim3(kBlock), args, lds, s);
+  void* args[] = {&g, &u, &wsv, &topk, (void*)&x, &ldx_bytes, &h};
+  return moe_launch(moe_gate_up_kernel<LPR, XF32>, lds, args, s, dev);
 }
 
 hipError_t launch_moe_gate_up(const DevInfo& dev, const HBank& G, const HBank& U,
-                              const MoeWs& ws, int P, int topk, const void* x, bool x_f32,
-                              float* h, hipStream_t s) {
+                              const MoeWs& ws, int topk, const void* x, bool x_f32, float* h,
+                              hipStream_t s) {
   const int64_t ldx_bytes = G.e0.K * (x_f32 ? 4 : 2);
   const char* xp = (const char*)x;
-  const int lpr = lanes_per_row(G.e0.K);
+  // Teams of at most 32 lanes: a wave then works on two gate/up row pairs
+  // (2.5% faster than 64-lane teams at K = 2048 in same-process A/B).
+  const int lpr = lanes_per_row(G.e0.K) < 32 ? lanes_per_row(G.e0.K) : 32;
   if (x_f32) {
-    if (lpr == 64) return moe_gu_t<64, true>(dev, G, U, ws, P, topk, xp, ldx_bytes, h, s);
-    if (lpr == 32) return moe_gu_t<32, true>(dev, G, U, ws, P, topk, xp, ldx_bytes, h, s);
-    return moe_gu_t<16, true>(dev, G, U, ws, P, topk, xp, ldx_bytes, h, s);
+    if (lpr == 32) return moe_gu_t<32, true>(dev, G, U, ws, topk, xp, ldx_bytes, h, s);
+    return moe_gu_t<16, true>(dev, G, U, ws, topk, xp, ldx_bytes, h, s);
   }
-  if (lpr == 64) return moe_gu_t<64, false>(dev, G, U, ws, P, topk, xp, ldx_bytes, h, s);
-  if (lpr == 32) return moe_gu_t<32, false>(dev, G, U, ws, P, topk, xp, ldx_bytes, h, s);
-  return moe_gu_t<16, false>(dev, G, U, ws, P, topk, xp, ldx_bytes, h, s);
+  if (lpr == 32) return moe_gu_t<32, false>(dev, G, U, ws, topk, xp, ldx_bytes, h, s);
+  return moe_gu_t<16, false>(dev, G, U, ws, topk, xp, ldx_bytes, h, s);
 }
 
 hipError_t launch_moe_combine(const int32_t* ids, int E, const float* gate_w,
