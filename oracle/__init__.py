@@ -351,3 +351,54 @@ def moe_ffn(case, threads: int = 1):
     gw = np.asarray(case.gate_w, np.float64)
     b = (gw[:, :, None] * per_pair.reshape(T, topk, H)).sum(axis=1) + 1e-6 * S
     return dict(out=out, bound=b, stage1=s1, y_pair=y, A_pair=Ay)
+
+
+# ---------------------------------------------------------------- router
+def topk_softmax(logits: np.ndarray, topk: int):
+    """Router of a routed layer: per token, pick the topk experts with the
+    largest router logits and weight them by a softmax over the picked logits.
+
+    The pages route on the device with m-invariant router kernels and require
+    a token's routing not to depend on its co-arrivals (memra performance,
+    serving exactness arc). They do not spell out the router's arithmetic;
+    this is the plain reading used by the library: selection compares the
+    fp32 logits exactly, in descending order, equal logits going to the
+    lower expert index first (-0 equals +0); the weights are
+    w_j = exp(l_j - l_0) / sum_i exp(l_i - l_0) over the picked logits, in
+    fp64 (l_0 is the largest). Renormalising a softmax over all experts to
+    the picked ones gives the same weights.
+
+    Returns (ids int32 [T][topk], w float64 [T][topk], dl float64 [T][topk]
+    with dl = l_0 - l_j >= 0).
+    """
+    L = np.asarray(logits, np.float32)
+    T, E = L.shape
+    if not 1 <= topk <= E:
+        raise ValueError("need 1 <= topk <= E")
+    if not np.isfinite(L).all():
+        raise ValueError("router logits must be finite")
+    ids = np.empty((T, topk), np.int32)
+    w = np.empty((T, topk))
+    dl = np.empty((T, topk))
+    idx = np.arange(E)
+    for t in range(T):
+        v = L[t].astype(np.float64)
+        order = np.lexsort((idx, -v))[:topk]  # primary: larger logit; then lower index
+        sel = v[order]
+        z = np.exp(sel - sel[0])
+        ids[t] = order
+        w[t] = z / z.sum()
+        dl[t] = sel[0] - sel
+    return ids, w, dl
+
+
+def topk_softmax_bound(w: np.ndarray, dl: np.ndarray) -> np.ndarray:
+    """Error bound for fp32 router weights against ``topk_softmax``.
+
+    An fp32 evaluation rounds l_j - l_0 (relative 2^-24, so an absolute
+    2^-24*dl_j in the exponent), evaluates exp (a few ulps), sums topk
+    positive terms (at most (topk-1)*2^-24 relative) and divides (2^-24):
+    |dw_j| <= 2^-23 * (dl_j + 2*topk + 8) * w_j, with margin.
+    """
+    topk = w.shape[-1]
+    return 2.0 ** -23 * (dl + 2 * topk + 8) * w

@@ -237,3 +237,22 @@ WORKLOADS = {
     "lmhead_151936x5120": dict(kind="lmhead", V=151936, K=5120, Ns=(1, 4)),
     "moe_e128_top8_t16": dict(kind="moe", E=128, F=768, H=2048, T=16, topk=8),
 }
+
+
+def router_case(T: int, E: int, seed: int = 0, ties: bool = True) -> np.ndarray:
+    """Router logits fp32 [T][E] ~ N(0,1). With ``ties``, token 0 gets an
+    exact tie at its top (two experts share the largest logit) and token 1
+    a block of equal logits, so the ordering rule for equal logits is
+    exercised; a -0.0/+0.0 pair is planted where E allows."""
+    rng = rng_for(seed)
+    L = rng.normal(0.0, 1.0, size=(T, E)).astype(np.float32)
+    if ties and E >= 4:
+        L[0, E - 1] = L[0].max()
+        L[0, 1] = L[0, E - 1]
+        if T > 1:
+            L[1, : E // 2] = np.float32(0.5)
+        if T > 2:
+            L[2, :] = np.float32(-3.0)
+            L[2, E // 3] = np.float32(-0.0)
+            L[2, E // 4] = np.float32(0.0)
+    return L

@@ -390,3 +390,72 @@ def test_lmhead_planting_small():
         others = np.delete(y[n], c.planted_rows[n])
         sigma = others.std()
         assert y[n, c.planted_rows[n]] - others.max() >= 3 * sigma
+
+
+# ---------------------------------------------------------------- router
+def test_router_closed_form_weights():
+    """Logits ln 1, ln 2, ln 3, ln 6 give softmax weights 1:2:3:6 exactly
+    (up to the fp32 rounding of the logits), ordered by descending logit."""
+    L = np.log(np.array([[1.0, 2.0, 3.0, 6.0]])).astype(np.float32)
+    ids, w, dl = oracle.topk_softmax(L, 4)
+    assert list(ids[0]) == [3, 2, 1, 0]
+    assert np.allclose(w[0], np.array([6, 3, 2, 1]) / 12.0, rtol=1e-6, atol=0)
+    assert np.allclose(dl[0], np.log(6.0 / np.array([6, 3, 2, 1])), rtol=0, atol=1e-6)
+    ids2, w2, _ = oracle.topk_softmax(L, 2)  # top 2 of them: 6 and 3 -> 2/3, 1/3
+    assert list(ids2[0]) == [3, 2] and np.allclose(w2[0], [2 / 3, 1 / 3], rtol=1e-6)
+
+
+def test_router_top1_weight_is_one_and_id_is_first_argmax():
+    L = synth.router_case(9, 37, seed=3)
+    ids, w, _ = oracle.topk_softmax(L, 1)
+    assert np.all(w == 1.0)
+    assert np.array_equal(ids[:, 0], np.argmax(L, axis=1))  # numpy: first maximum
+
+
+def test_router_equal_logits_take_lowest_indices_with_equal_weights():
+    L = np.full((2, 10), np.float32(0.25))
+    L[1, 7] = np.float32(-0.0)
+    L[1, 3] = np.float32(0.0)
+    L[1, [0, 1, 2, 4, 5, 6, 8, 9]] = -1.0
+    ids, w, _ = oracle.topk_softmax(L, 4)
+    assert list(ids[0]) == [0, 1, 2, 3] and np.all(w[0] == 0.25)
+    assert list(ids[1][:2]) == [3, 7]  # -0 == +0: the lower index first
+    assert w[1][0] == w[1][1]
+
+
+def test_router_matches_renormalised_full_softmax_brute_force():
+    """A different formula: softmax over all experts, keep the picked ones,
+    renormalise; the picked set is checked against a brute-force ordering."""
+    L = synth.router_case(6, 11, seed=4)
+    for k in (1, 3, 11):
+        ids, w, _ = oracle.topk_softmax(L, k)
+        for t in range(L.shape[0]):
+            ranked = sorted(range(11), key=lambda e: (-float(L[t, e]), e))
+            assert list(ids[t]) == ranked[:k]
+            p = np.exp(L[t].astype(np.float64))
+            p = p / p.sum()
+            ref = p[ranked[:k]] / p[ranked[:k]].sum()
+            assert np.allclose(w[t], ref, rtol=1e-12, atol=0)
+
+
+def test_router_invariances():
+    """Adding a constant to every logit of a token changes nothing; permuting
+    the experts permutes the ids; each token is routed independently of the
+    other tokens of the batch."""
+    L = synth.router_case(5, 24, seed=5, ties=False)
+    ids, w, _ = oracle.topk_softmax(L, 6)
+    ids_s, w_s, _ = oracle.topk_softmax(L + np.float32(0.5), 6)
+    # fp32 rounding of the shifted logits moves the weights by ~1e-7 at most
+    assert np.array_equal(ids, ids_s) and np.allclose(w, w_s, rtol=1e-6)
+    perm = np.random.default_rng(0).permutation(24)
+    ids_p, w_p, _ = oracle.topk_softmax(L[:, perm], 6)
+    assert np.array_equal(perm[ids_p], ids) and np.allclose(w_p, w, rtol=0, atol=0)
+    ids_1, w_1, _ = oracle.topk_softmax(L[2:3], 6)
+    assert np.array_equal(ids_1[0], ids[2]) and np.array_equal(w_1[0], w[2])
+
+
+def test_router_rejects_bad_input():
+    with pytest.raises(ValueError):
+        oracle.topk_softmax(np.zeros((1, 4), np.float32), 5)
+    with pytest.raises(ValueError):
+        oracle.topk_softmax(np.array([[0.0, np.nan]], np.float32), 1)
