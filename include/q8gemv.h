@@ -207,6 +207,34 @@ int q8_moe_ffn(const q8_bank *gate, const q8_bank *up, const q8_bank *down,
                const int32_t *expert_ids, const float *gate_w, const void *x, int x_dt,
                float *out, int T, int topk, void *ws, size_t ws_bytes, void *stream);
 
+/* ------------------------------------------------------------ router
+ * The step upstream of the routed experts, kept on the device so the
+ * routed layer replays as a graph with no host round-trip (memra wiki,
+ * feature list: graph-replayable device-length counters; one graph replay
+ * per token), and computed one token at a time so a token's experts never
+ * depend on its co-arrivals (memra performance, serving exactness arc:
+ * m-invariant router kernels). The pages do not spell out the router's
+ * arithmetic; the library's reading: per token t,
+ *   expert_ids[t][0..topk) = the topk experts with the largest logits, in
+ *     descending order of logit; equal logits go to the lower expert index
+ *     first; -0 and +0 compare equal;
+ *   gate_w[t][j] = exp(l_j - l_0) / sum_i exp(l_i - l_0) over the picked
+ *     logits l_0 >= l_1 >= ... (fp32 expf; equal to a softmax over all
+ *     experts renormalised to the picked ones).
+ * logits [dev] fp32 [T][E], finite (a NaN gives an unspecified pick, no
+ * fault); expert_ids [dev] int32 [T][topk]; gate_w [dev] fp32 [T][topk];
+ * 1 <= E <= 4096, 1 <= topk <= min(E, 64); T >= 1. No workspace. The
+ * outputs feed q8_moe_gemv / q8_moe_ffn directly. */
+int q8_moe_topk_softmax(const float *logits, int T, int E, int topk, int32_t *expert_ids,
+                        float *gate_w, void *stream);
+
+/* Router from a Q8_0 router matrix Wr [E][K]: logits = Wr x (as q8_gemv
+ * with fp32 output, so bitwise independent of T), then
+ * q8_moe_topk_softmax. x [dev] [T][K] of x_dt; logits [dev] fp32 [T][E]
+ * (written, caller-owned). Two launches on the stream. */
+int q8_moe_router(const q8_matrix *Wr, const void *x, int x_dt, int T, int topk, float *logits,
+                  int32_t *expert_ids, float *gate_w, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -30,7 +30,7 @@ Q8_DT_F32 = 2
 EXPORTS = (
     "q8_status_str", "q8_device_check", "q8_pack_layout", "q8_pack_host", "q8_unpack_host",
     "q8_gemv", "q8_gemv_pair", "q8_lmhead_ws_bytes", "q8_lmhead_argmax", "q8_moe_ws_bytes",
-    "q8_moe_ws_layout", "q8_moe_gemv", "q8_moe_ffn",
+    "q8_moe_ws_layout", "q8_moe_gemv", "q8_moe_ffn", "q8_moe_topk_softmax", "q8_moe_router",
 )
 
 
@@ -77,6 +77,8 @@ def lib() -> ctypes.CDLL:
             "q8_moe_ws_layout": ([i32, i32, i32, i64, i64, vp], i32),
             "q8_moe_gemv": ([pb, vp, vp, vp, i32, i32, vp, i32, i32, vp, sz, vp], i32),
             "q8_moe_ffn": ([pb, pb, pb, vp, vp, vp, i32, vp, i32, i32, vp, sz, vp], i32),
+            "q8_moe_topk_softmax": ([vp, i32, i32, i32, vp, vp, vp], i32),
+            "q8_moe_router": ([pm, vp, i32, i32, i32, vp, vp, vp, vp], i32),
         }
         for name, (args, res) in sig.items():
             fn = getattr(L, name)
@@ -333,3 +335,37 @@ def moe_ffn(gate: PackedBank, up: PackedBank, down: PackedBank, expert_ids, gate
                             x.data_ptr(), _dt(x), out.data_ptr(), T, topk, ws.data_ptr(),
                             ws.numel(), _stream(stream)), "q8_moe_ffn")
     return out
+
+
+def moe_topk_softmax(logits, topk: int, ids=None, gate_w=None, stream=None):
+    """Router on the device: (expert_ids int32 [T][topk], gate_w fp32 [T][topk])
+    from router logits fp32 [T][E]."""
+    import torch
+    if logits.dtype != torch.float32 or logits.dim() != 2 or not logits.is_contiguous():
+        raise ValueError("logits must be a contiguous fp32 [T][E] tensor")
+    T, E = logits.shape
+    if ids is None:
+        ids = torch.empty((T, topk), dtype=torch.int32, device=logits.device)
+    if gate_w is None:
+        gate_w = torch.empty((T, topk), dtype=torch.float32, device=logits.device)
+    _check(lib().q8_moe_topk_softmax(logits.data_ptr(), T, E, topk, ids.data_ptr(),
+                                     gate_w.data_ptr(), _stream(stream)), "q8_moe_topk_softmax")
+    return ids, gate_w
+
+
+def moe_router(Wr: PackedQ8, x, topk: int, logits=None, ids=None, gate_w=None, stream=None):
+    """Router from a Q8_0 router matrix [E][K]: returns (logits fp32 [T][E],
+    expert_ids int32 [T][topk], gate_w fp32 [T][topk])."""
+    import torch
+    x = _as_2d(x, Wr.K)
+    T = x.shape[0]
+    if logits is None:
+        logits = torch.empty((T, Wr.M), dtype=torch.float32, device=x.device)
+    if ids is None:
+        ids = torch.empty((T, topk), dtype=torch.int32, device=x.device)
+    if gate_w is None:
+        gate_w = torch.empty((T, topk), dtype=torch.float32, device=x.device)
+    _check(lib().q8_moe_router(ctypes.byref(Wr.cmat()), x.data_ptr(), _dt(x), T, topk,
+                               logits.data_ptr(), ids.data_ptr(), gate_w.data_ptr(),
+                               _stream(stream)), "q8_moe_router")
+    return logits, ids, gate_w

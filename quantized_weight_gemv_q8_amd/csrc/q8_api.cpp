@@ -388,4 +388,45 @@ int q8_moe_ffn(const q8_bank* gate, const q8_bank* up, const q8_bank* down,
   return launch_rc(q8::launch_moe_combine(expert_ids, E, gate_w, w.y_pair, out, T, topk, H, s));
 }
 
+// ------------------------------------------------------------ router
+static int check_topk(const float* logits, int T, int E, int topk, const int32_t* ids,
+                      const float* gate_w) {
+  if (!logits || !ids || !gate_w) return Q8_ERR_NULL;
+  if (T < 1 || E < 1 || E > q8::kRouterMaxE || topk < 1 || topk > E || topk > q8::kRouterMaxK)
+    return Q8_ERR_SHAPE;
+  if (!aligned(logits, 4) || !aligned(ids, 4) || !aligned(gate_w, 4)) return Q8_ERR_ALIGN;
+  const size_t lb = (size_t)T * E * 4, ob = (size_t)T * topk * 4;
+  if (overlap(logits, lb, ids, ob) || overlap(logits, lb, gate_w, ob) || overlap(ids, ob, gate_w, ob))
+    return Q8_ERR_ALIAS;
+  return Q8_OK;
+}
+
+int q8_moe_topk_softmax(const float* logits, int T, int E, int topk, int32_t* expert_ids,
+                        float* gate_w, void* stream) {
+  int rc = check_topk(logits, T, E, topk, expert_ids, gate_w);
+  if (rc) return rc;
+  const DevInfo* dev = nullptr;
+  rc = current_device(&dev);
+  if (rc) return rc;
+  return launch_rc(
+      q8::launch_topk_softmax(logits, T, E, topk, expert_ids, gate_w, (hipStream_t)stream));
+}
+
+int q8_moe_router(const q8_matrix* Wr, const void* x, int x_dt, int T, int topk, float* logits,
+                  int32_t* expert_ids, float* gate_w, void* stream) {
+  int rc = check_matrix(Wr);
+  if (rc) return rc;
+  if (!x) return Q8_ERR_NULL;
+  rc = check_topk(logits, T, (int)Wr->M, topk, expert_ids, gate_w);
+  if (rc) return rc;
+  const size_t xs = dt_size(x_dt);
+  if (!xs) return Q8_ERR_DTYPE;
+  const size_t xb = (size_t)T * Wr->K * xs, ob = (size_t)T * topk * 4;
+  if (overlap(x, xb, expert_ids, ob) || overlap(x, xb, gate_w, ob)) return Q8_ERR_ALIAS;
+  rc = gemv_impl(Wr, nullptr, x, x_dt, logits, nullptr, Q8_DT_F32, T, stream);
+  if (rc) return rc;
+  return launch_rc(q8::launch_topk_softmax(logits, T, (int)Wr->M, topk, expert_ids, gate_w,
+                                           (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -130,18 +130,76 @@ struct XPlanes {
   static constexpr int P = XF32 ? 4 : 2;
 };
 
-// rows[n] points at token n's K activations (16-byte aligned); tokens
-// n >= nt are not staged.
-template <int NT, bool XF32>
+// rows[n] points at token n's K activations (16-byte aligned); rows[0]
+// must not be null. Tokens n >= nt, and tokens whose row is null, are not
+// staged. Thread t copies pieces t, t + blockDim, ... of every token. The
+// loads of a batch (up to 4 tokens x KB pieces) are issued before its LDS
+// writes, so staging costs about one memory round trip per batch rather
+// than one per token and piece (measured on MI355X: 5120 x 5120 at N = 8
+// 19.3 -> 16.8 us). Inside a batch every load is unconditional (a dead
+// slot re-reads piece 0 of rows[0] and discards it), so no branch forces a
+// wait between the loads; lanes with nothing to copy skip the batch.
+template <int NT, bool XF32, int KB>
+__device__ __forceinline__ void stage_batch(const char* const rows[NT], int C, uint4* lds, int nt,
+                                            int per_tok, int k0) {
+  constexpr int P = XPlanes<XF32>::P;
+  constexpr int TB = NT < 4 ? NT : 4;  // tokens per batch
+  typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+  const int step = (int)blockDim.x;
+  if ((int)threadIdx.x + k0 * step >= per_tok) return;
+  const v4u* r0 = reinterpret_cast<const v4u*>(rows[0]);
+#pragma unroll
+  for (int n0 = 0; n0 < NT; n0 += TB) {
+    v4u v[TB][KB];
+    int dst[TB][KB];
+#pragma unroll
+    for (int t = 0; t < TB; ++t) {
+#pragma unroll
+      for (int kk = 0; kk < KB; ++kk) {
+        const int n = n0 + t;
+        const int j = (int)threadIdx.x + (k0 + kk) * step;
+        const v4u* r = n < NT ? reinterpret_cast<const v4u*>(rows[n < NT ? n : 0]) : nullptr;
+        const bool live = n < nt && j < per_tok && r != nullptr;
+        v[t][kk] = live ? r[j] : r0[0];
+        const int c = j / P, h = j - c * P;
+        dst[t][kk] = live ? (n * P + h) * C + c : -1;
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < TB; ++t) {
+#pragma unroll
+      for (int kk = 0; kk < KB; ++kk)
+        if (dst[t][kk] >= 0) reinterpret_cast<v4u*>(lds)[dst[t][kk]] = v[t][kk];
+    }
+  }
+}
+
+// KBMAX = 1 keeps the batch (and the kernel's register count) small for
+// kernels whose rows need at most one piece per thread and token.
+template <int NT, bool XF32, int KBMAX = 2>
 __device__ __forceinline__ void stage_x(const char* const rows[NT], int C, uint4* lds, int nt = NT) {
   constexpr int P = XPlanes<XF32>::P;
   const int per_tok = C * P;
-  for (int n = 0; n < nt; ++n) {
-    const uint4* src = reinterpret_cast<const uint4*>(rows[n]);
+  if constexpr (NT == 1) {
+    // One token: the plain loop measured as fast as batching (2.98 against
+    // 3.04 us at 1024 x 1024), with fewer instructions.
+    const uint4* src = reinterpret_cast<const uint4*>(rows[0]);
     for (int i = threadIdx.x; i < per_tok; i += blockDim.x) {
       const int c = i / P, h = i - c * P;
-      lds[(n * P + h) * C + c] = src[i];
+      lds[h * C + c] = src[i];
     }
+    return;
+  }
+  const int step = (int)blockDim.x;
+  const int kc = (per_tok + step - 1) / step;  // pieces per thread per token
+  // The first batch is outside any loop (the only one for K <= 8192 at
+  // fp16), so nothing carried around a loop makes its loads wait.
+  if (KBMAX == 1 || kc == 1) {
+    stage_batch<NT, XF32, 1>(rows, C, lds, nt, per_tok, 0);
+    for (int k0 = 1; k0 < kc; ++k0) stage_batch<NT, XF32, 1>(rows, C, lds, nt, per_tok, k0);
+  } else {
+    stage_batch<NT, XF32, 2>(rows, C, lds, nt, per_tok, 0);
+    for (int k0 = 2; k0 < kc; k0 += 2) stage_batch<NT, XF32, 2>(rows, C, lds, nt, per_tok, k0);
   }
 }
 

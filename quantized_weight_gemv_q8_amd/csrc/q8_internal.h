@@ -89,6 +89,11 @@ hipError_t launch_moe_gemv(const DevInfo& dev, const HBank& W, const MoeWs& ws, 
 hipError_t launch_moe_gate_up(const DevInfo& dev, const HBank& G, const HBank& U,
                               const MoeWs& ws, int topk, const void* x, bool x_f32, float* h,
                               hipStream_t s);
+// Router: ids [T][topk] and softmax weights [T][topk] from logits [T][E].
+constexpr int kRouterMaxE = 4096;  // 64 experts per lane of the token's wave
+constexpr int kRouterMaxK = 64;    // one picked logit per lane
+hipError_t launch_topk_softmax(const float* logits, int T, int E, int topk, int32_t* ids,
+                               float* gate_w, hipStream_t s);
 // out[t] = sum_j gate_w[t][j] * y_pair[t*topk + j] (slots with invalid ids skipped).
 hipError_t launch_moe_combine(const int32_t* ids, int E, const float* gate_w,
                               const float* y_pair, float* out, int T, int topk, int64_t M,

@@ -433,16 +433,14 @@ __device__ __forceinline__ void routed_slices(const MoeWs& ws, const RowOf& rowo
     }
     __syncthreads();
     auto stage = [&]() {
+      const char* rows[kSegV * NT];
+#pragma unroll
       for (int i = 0; i < kSegV * NT; ++i) {
-        const int pid = seg_pid[i];
-        if (pid < 0) continue;
+        const int pid = __builtin_amdgcn_readfirstlane(seg_pid[i]);
         const int src = x_per_pair ? pid : pid / topk;
-        const uint4* row = reinterpret_cast<const uint4*>(x + (int64_t)src * ldx_bytes);
-        for (int k = threadIdx.x; k < C * P; k += kBlock) {
-          const int c = k / P, h = k - c * P;
-          lds[(i * P + h) * C + c] = row[k];
-        }
+        rows[i] = pid < 0 ? nullptr : x + (int64_t)src * ldx_bytes;
       }
+      stage_x<kSegV * NT, XF32, 1>(rows, C, lds);
       __syncthreads();
     };
     run_routed<NT, LPR, R, 1, MINC, XF32>(rowof, epi, lds, C, g, seg_end, gpv, rpv, v0, seg_e,
@@ -452,7 +450,7 @@ __device__ __forceinline__ void routed_slices(const MoeWs& ws, const RowOf& rowo
 }
 
 template <int LPR, bool XF32>
-__global__ __launch_bounds__(kBlock) void moe_rows_kernel(HBank W, MoeWs ws, int topk,
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(XF32 ? 4 : 6))) void moe_rows_kernel(HBank W, MoeWs ws, int topk,
                                                          const char* x, int64_t ldx_bytes,
                                                          int x_per_pair, float* y) {
   extern __shared__ uint4 lds_x[];
@@ -474,7 +472,7 @@ __global__ __launch_bounds__(kBlock) void moe_rows_kernel(HBank W, MoeWs ws, int
 
 // virtual row i = 2*rho + s: s = 0 gate row rho, s = 1 up row rho
 template <int LPR, bool XF32>
-__global__ __launch_bounds__(kBlock) void moe_gate_up_kernel(HBank Gb, HBank Ub, MoeWs ws,
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(XF32 ? 4 : 6))) void moe_gate_up_kernel(HBank Gb, HBank Ub, MoeWs ws,
                                                             int topk, const char* x,
                                                             int64_t ldx_bytes, float* h) {
   extern __shared__ uint4 lds_x[];

@@ -171,6 +171,27 @@ def test_moe_validation(L):
     assert L.q8_moe_gemv(ctypes.byref(bad_stride), IDS, None, XX, 1, 0, OUT, T, topk, WS, n1, None) == -2
 
 
+def test_router_validation(L):
+    LG, IDS, GW, XX = 0x800000, 0x900000, 0xA00000, 0xB00000
+    T, E, k = 4, 128, 8
+
+    def rc(lg=LG, T_=T, E_=E, k_=k, ids=IDS, gw=GW):
+        return L.q8_moe_topk_softmax(lg, T_, E_, k_, ids, gw, None)
+    assert rc(lg=0) == -1 and rc(ids=0) == -1 and rc(gw=0) == -1
+    assert rc(T_=0) == -2 and rc(E_=0) == -2 and rc(k_=0) == -2
+    assert rc(k_=E + 1) == -2
+    assert rc(E_=4097, k_=8) == -2  # more experts than the wave holds
+    assert rc(E_=100, k_=65) == -2  # more picks than lanes
+    assert rc(lg=LG + 2) == -3 and rc(gw=GW + 1) == -3
+    assert rc(ids=LG + 16) == -8  # ids inside the logits
+    assert rc(gw=IDS + 4) == -8  # gate_w overlaps ids
+    W = _mat(M=E, K=256)
+    assert L.q8_moe_router(ctypes.byref(W), 0, 1, T, k, LG, IDS, GW, None) == -1
+    assert L.q8_moe_router(ctypes.byref(W), XX, 7, T, k, LG, IDS, GW, None) == -4
+    assert L.q8_moe_router(ctypes.byref(W), XX, 1, T, E + 1, LG, IDS, GW, None) == -2
+    assert L.q8_moe_router(ctypes.byref(W), XX, 1, T, k, LG, XX, GW, None) == -8
+
+
 def test_valid_call_without_gfx950_is_refused(L):
     if L.q8_device_check(0) == 0:
         pytest.skip("a gfx950 device is present; this check is for hosts without one")
