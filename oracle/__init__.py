@@ -258,9 +258,11 @@ def moe_route(expert_ids: np.ndarray, E: int):
 
 
 def silu(z: np.ndarray) -> np.ndarray:
-    """silu(z) = z / (1 + exp(-z)) in fp64."""
+    """silu(z) = z / (1 + exp(-z)) in fp64, evaluated as z * e^z / (1 + e^z)
+    for z < 0 (the same function; exp(-z) would overflow below z = -709)."""
     z = np.asarray(z, np.float64)
-    return z / (1.0 + np.exp(-z))
+    ez = np.exp(np.minimum(z, 0.0))
+    return np.where(z >= 0, z / (1.0 + np.exp(-np.maximum(z, 0.0))), z * ez / (1.0 + ez))
 
 
 def moe_gate_up(case, threads: int = 1):
@@ -402,3 +404,25 @@ def topk_softmax_bound(w: np.ndarray, dl: np.ndarray) -> np.ndarray:
     """
     topk = w.shape[-1]
     return 2.0 ** -23 * (dl + 2 * topk + 8) * w
+
+
+# ---------------------------------------------------------------- dense gate/up
+def gate_up_silu(qg, dg, qu, du, x, threads: int = 1, out_dtype: str = "f32"):
+    """Dense SiLU-gated pair of an MLP: h = silu(W_gate x) * (W_up x), fp64.
+
+    The MLP step after the fused gate+up pair (memra performance, qwen/silu
+    class): silu(z) = z / (1 + exp(-z)). Bound on an fp32 (or fp16) GPU h,
+    propagated from the two GEMV bounds as in ``moe_gate_up``:
+    |dh| <= 1.1*b_g*|u| + |silu(g)|*b_u + 1.1*b_g*b_u + 1e-6*|h| (+ half an
+    fp16 ulp of h for fp16 output); 1.1 bounds |silu'|.
+    Returns dict(h, bh, g, u) of [N][M] arrays.
+    """
+    g, Ag = gemv(qg, dg, x, threads)
+    u, Au = gemv(qu, du, x, threads)
+    sg = silu(g)
+    h = sg * u
+    bg, bu = REL_TOL * Ag, REL_TOL * Au
+    bh = 1.1 * bg * np.abs(u) + np.abs(sg) * bu + 1.1 * bg * bu + 1e-6 * np.abs(h)
+    if out_dtype == "f16":
+        bh = bh + 0.5 * fp16_ulp(h)
+    return dict(h=h, bh=bh, g=g, u=u)

@@ -15,6 +15,7 @@ a mis-decoded byte) fails at least one test:
   shapes, per-block power-of-two scales equal an int64 block decomposition;
 * the floating-point bound: an fp32 emulation stays inside gamma_{K+1}*A.
 """
+import math
 import struct
 from fractions import Fraction
 
@@ -459,3 +460,39 @@ def test_router_rejects_bad_input():
         oracle.topk_softmax(np.zeros((1, 4), np.float32), 5)
     with pytest.raises(ValueError):
         oracle.topk_softmax(np.array([[0.0, np.nan]], np.float32), 1)
+
+
+# ---------------------------------------------------------------- dense gate/up + SiLU
+def test_gate_up_silu_closed_forms():
+    """Hand-built rows with d = 1 and unit quants give g and u exactly, so h
+    is silu at known points: silu(1) = 1/(1+e^-1), silu(-1) = -e^-1/(1+e^-1),
+    silu(0) = 0 whatever u is."""
+    K = 32
+    qg = np.zeros((3, K), np.int8)
+    qu = np.zeros((3, K), np.int8)
+    qg[0, 0], qu[0, 0] = 1, 2     # g = 1, u = 2
+    qg[1, 0], qu[1, 0] = -1, 3    # g = -1, u = 3
+    qg[2, 5], qu[2, 0] = 0, 7     # g = 0, u = 7
+    d = np.ones((3, 1), np.float16)
+    x = np.zeros((1, K), np.float16)
+    x[0, 0] = 1.0
+    r = oracle.gate_up_silu(qg, d, qu, d, x)
+    e = math.exp(-1.0)
+    assert r["g"][0].tolist() == [1.0, -1.0, 0.0] and r["u"][0].tolist() == [2.0, 3.0, 7.0]
+    assert math.isclose(r["h"][0, 0], 2.0 / (1.0 + e), rel_tol=1e-15)
+    assert math.isclose(r["h"][0, 1], 3.0 * (-e / (1.0 + e)), rel_tol=1e-15)
+    assert r["h"][0, 2] == 0.0
+
+
+def test_gate_up_silu_large_gate_is_identity_times_up():
+    """For large positive g, silu(g) -> g: h -> g*u; for large negative g, h -> 0."""
+    rng = np.random.default_rng(0)
+    K = 64
+    qg = np.full((2, K), 127, np.int8)
+    qg[1] = -127
+    qu = rng.integers(-127, 128, size=(2, K)).astype(np.int8)
+    d = np.full((2, 2), 1.0, np.float16)
+    x = np.ones((1, K), np.float16)
+    r = oracle.gate_up_silu(qg, d, qu, d, x)
+    assert math.isclose(r["h"][0, 0], r["g"][0, 0] * r["u"][0, 0], rel_tol=1e-12)
+    assert abs(r["h"][0, 1]) < 1e-300 * abs(r["u"][0, 1]) + 1e-300
