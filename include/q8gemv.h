@@ -139,6 +139,18 @@ int q8_gemv(const q8_matrix *W, const void *x, int x_dt, void *y, int y_dt, int 
 int q8_gemv_pair(const q8_matrix *Wa, const q8_matrix *Wb, const void *x, int x_dt,
                  void *ya, void *yb, int y_dt, int N, void *stream);
 
+/* Fused gate+up pair with the MLP activation (the SiLU-gated MLP of the
+ * pages' qwen/silu model class, memra performance):
+ *   h[n][m] = silu(g) * u,  g = (Wg x_n)[m], u = (Wu x_n)[m],
+ *   silu(z) = z / (1 + exp(-z)) in fp32 (expf).
+ * g and u are bitwise the ya and yb of q8_gemv_pair; only h is stored
+ * (fp32, or fp16 rounded to nearest even), so the MLP's down projection
+ * reads N*M values instead of 2*N*M. Wg and Wu have the same M and K.
+ * x [dev] [N][K] of x_dt; h [dev] [N][M] of h_dt, must not overlap x.
+ * N >= 1 (passes of up to 8 tokens, per-token results N-invariant). */
+int q8_gemv_pair_silu(const q8_matrix *Wg, const q8_matrix *Wu, const void *x, int x_dt,
+                      void *h, int h_dt, int N, void *stream);
+
 /* ------------------------------------------------------------ LM head
  * logits[n][v] = W x_n (as q8_gemv with fp32 output) and
  * ids[n] = the smallest v with logits[n][v] == max_v logits[n][v]

@@ -29,8 +29,9 @@ Q8_DT_F32 = 2
 # every function the header declares
 EXPORTS = (
     "q8_status_str", "q8_device_check", "q8_pack_layout", "q8_pack_host", "q8_unpack_host",
-    "q8_gemv", "q8_gemv_pair", "q8_lmhead_ws_bytes", "q8_lmhead_argmax", "q8_moe_ws_bytes",
-    "q8_moe_ws_layout", "q8_moe_gemv", "q8_moe_ffn", "q8_moe_topk_softmax", "q8_moe_router",
+    "q8_gemv", "q8_gemv_pair", "q8_gemv_pair_silu", "q8_lmhead_ws_bytes", "q8_lmhead_argmax",
+    "q8_moe_ws_bytes", "q8_moe_ws_layout", "q8_moe_gemv", "q8_moe_ffn", "q8_moe_topk_softmax",
+    "q8_moe_router",
 )
 
 
@@ -71,6 +72,7 @@ def lib() -> ctypes.CDLL:
             "q8_unpack_host": ([vp, i64, vp, i64, i64, i64, vp], i32),
             "q8_gemv": ([pm, vp, i32, vp, i32, i32, vp], i32),
             "q8_gemv_pair": ([pm, pm, vp, i32, vp, vp, i32, i32, vp], i32),
+            "q8_gemv_pair_silu": ([pm, pm, vp, i32, vp, i32, i32, vp], i32),
             "q8_lmhead_ws_bytes": ([i64, i32], sz),
             "q8_lmhead_argmax": ([pm, vp, i32, vp, vp, i32, vp, sz, vp], i32),
             "q8_moe_ws_bytes": ([i32, i32, i32, i64, i64], sz),
@@ -245,6 +247,19 @@ def gemv_pair(Wa: PackedQ8, Wb: PackedQ8, x, out_a=None, out_b=None, out_dtype=N
                               _dt(x), out_a.data_ptr(), out_b.data_ptr(), _dt(out_a), N,
                               _stream(stream)), "q8_gemv_pair")
     return out_a, out_b
+
+
+def gemv_pair_silu(Wg: PackedQ8, Wu: PackedQ8, x, out=None, out_dtype=None, stream=None):
+    """h = silu(Wg x) * (Wu x), fp32 (or fp16) [N][M]."""
+    import torch
+    x = _as_2d(x, Wg.K)
+    N = x.shape[0]
+    if out is None:
+        out = torch.empty((N, Wg.M), dtype=out_dtype or torch.float32, device=x.device)
+    _check(lib().q8_gemv_pair_silu(ctypes.byref(Wg.cmat()), ctypes.byref(Wu.cmat()), x.data_ptr(),
+                                   _dt(x), out.data_ptr(), _dt(out), N, _stream(stream)),
+           "q8_gemv_pair_silu")
+    return out
 
 
 def lmhead_ws_bytes(V: int, N: int) -> int:

@@ -222,6 +222,35 @@ int q8_gemv_pair(const q8_matrix* Wa, const q8_matrix* Wb, const void* x, int x_
   return gemv_impl(Wa, Wb, x, x_dt, ya, yb, y_dt, N, stream);
 }
 
+int q8_gemv_pair_silu(const q8_matrix* Wg, const q8_matrix* Wu, const void* x, int x_dt, void* h,
+                      int h_dt, int N, void* stream) {
+  int rc = check_matrix(Wg);
+  if (rc) return rc;
+  if ((rc = check_matrix(Wu))) return rc;
+  if (Wu->M != Wg->M || Wu->K != Wg->K) return Q8_ERR_SHAPE;
+  if (!x || !h) return Q8_ERR_NULL;
+  if (N < 1) return Q8_ERR_SHAPE;
+  const size_t xs = dt_size(x_dt), hs = dt_size(h_dt);
+  if (!xs || !hs) return Q8_ERR_DTYPE;
+  if (!aligned(x, 16) || !aligned(h, hs)) return Q8_ERR_ALIGN;
+  if (overlap(x, (size_t)N * Wg->K * xs, h, (size_t)N * Wg->M * hs)) return Q8_ERR_ALIAS;
+  const DevInfo* dev = nullptr;
+  rc = current_device(&dev);
+  if (rc) return rc;
+  const bool xf = x_dt == Q8_DT_F32;
+  const int per_pass = q8::max_tokens_per_pass(*dev, Wg->K, xf);
+  if (per_pass < 1) return Q8_ERR_SHAPE;
+  const HMat G = to_h(Wg), U = to_h(Wu);
+  for (int n0 = 0; n0 < N; n0 += per_pass) {
+    const int nt = N - n0 < per_pass ? N - n0 : per_pass;
+    hipError_t e = q8::launch_glu(*dev, G, U, (const char*)x + (size_t)n0 * Wg->K * xs, xf,
+                                  (char*)h + (size_t)n0 * Wg->M * hs, h_dt == Q8_DT_F16, nt,
+                                  (hipStream_t)stream);
+    if (e != hipSuccess) return Q8_ERR_LAUNCH;
+  }
+  return Q8_OK;
+}
+
 // ------------------------------------------------------------ LM head
 size_t q8_lmhead_ws_bytes(int64_t V, int N) {
   (void)V;

@@ -81,6 +81,143 @@ __global__ __launch_bounds__(kBlock) void gemv_kernel(DenseMap map, DenseEpi epi
                                          (int64_t)gridDim.x * kWavesPerBlock, 0, stage);
 }
 
+// ---------------------------------------------------------------- gate/up + SiLU
+// The gate and up rows of output rho are virtual rows 2*rho and 2*rho + 1,
+// so a team (an even number of rows) holds both sums of an output in one
+// lane after the reduction and the MLP activation h = silu(g) * u is
+// applied before anything is stored. Per-row arithmetic is the engine's, so
+// g and u are bitwise those of q8_gemv_pair.
+struct GluMap {
+  const int8_t* qg;
+  const uint16_t* dg;
+  const int8_t* qu;
+  const uint16_t* du;
+  int64_t ldqg, lddg, ldqu, lddu;
+  int64_t M2;  // 2 * M virtual rows
+  __device__ __forceinline__ bool row(int64_t i, const int8_t*& q, const uint16_t*& d) const {
+    const int64_t rho = i >> 1;
+    const bool up = (i & 1) != 0;
+    const int64_t ldq = up ? ldqu : ldqg;
+    const int64_t ldd = up ? lddu : lddg;
+    q = (up ? qu : qg) + rho * ldq;
+    d = (up ? du : dg) + rho * ldd;
+    return i < M2;
+  }
+};
+
+struct GluEpi {
+  char* h;
+  int64_t M;
+  bool f16;
+  template <int NT, int R, int CNT>
+  __device__ __forceinline__ void emit(int64_t rbase, int base, bool owner, const float* v) {
+    static_assert(R % 2 == 0 && CNT == 2, "gate/up pairs");
+    if (!owner || base >= NT * R) return;
+    const int n = base / R, r = base - (base / R) * R;
+    const int64_t row = rbase + r;  // the gate row of the pair (even)
+    if (row >= 2 * M) return;
+    const float g = v[0], u = v[1];
+    const float val = g / (1.0f + expf(-g)) * u;
+    const int64_t o = (int64_t)n * M + (row >> 1);
+    if (f16) reinterpret_cast<_Float16*>(h)[o] = (_Float16)val;
+    else reinterpret_cast<float*>(h)[o] = val;
+  }
+};
+
+template <int NT, bool BIG>
+struct GluTune {
+  static constexpr int R = Tune<NT, BIG>::R < 2 ? 2 : Tune<NT, BIG>::R;
+};
+
+template <int NT, int LPR, bool XF32, bool BIG>
+__global__ __launch_bounds__(kBlock) void glu_kernel(GluMap map, GluEpi epi, const char* x,
+                                                     int64_t ldx_bytes, int C) {
+  extern __shared__ uint4 lds_x[];
+  constexpr int R = GluTune<NT, BIG>::R;
+  constexpr int G = (kWave / LPR) * R;
+  const int64_t n_groups = (map.M2 + G - 1) / G;
+  const int wave = threadIdx.x / kWave;
+  auto stage = [=]() {
+    const char* rows[NT];
+#pragma unroll
+    for (int n = 0; n < NT; ++n) rows[n] = x + n * ldx_bytes;
+    stage_x<NT, XF32>(rows, C, lds_x);
+    __syncthreads();
+  };
+  run_rows<NT, LPR, R, 1, 2, XF32>(map, epi, lds_x, C, n_groups,
+                                   (int64_t)blockIdx.x * kWavesPerBlock + wave,
+                                   (int64_t)gridDim.x * kWavesPerBlock, 0, stage);
+}
+
+template <int NT, int LPR, bool XF32, bool BIG>
+static hipError_t glu_launch_t(const DevInfo& dev, GluMap map, GluEpi epi, const char* x,
+                               int64_t ldx_bytes, int C, hipStream_t s) {
+  constexpr int G = (kWave / LPR) * GluTune<NT, BIG>::R;
+  const size_t lds = (size_t)NT * C * 16 * XPlanes<XF32>::P;
+  const int64_t n_groups = (map.M2 + G - 1) / G;
+  const int64_t need = (n_groups + kWavesPerBlock - 1) / kWavesPerBlock;
+  auto fn = glu_kernel<NT, LPR, XF32, BIG>;
+  if (lds > 64 * 1024) {
+    hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  int64_t blocks = (int64_t)dev.cus * blocks_per_cu((const void*)fn, lds);
+  if (blocks > need) blocks = need;
+  if (blocks < 1) blocks = 1;
+  void* args[] = {&map, &epi, (void*)&x, &ldx_bytes, &C};
+  return hipLaunchKernel((const void*)fn, dim3((unsigned)blocks), dim3(kBlock), args, lds, s);
+}
+
+template <int LPR, bool XF32>
+static hipError_t glu_launch_nt(const DevInfo& dev, int nt, GluMap map, GluEpi epi, const char* x,
+                                int64_t ldx_bytes, int C, hipStream_t s) {
+  switch (nt) {
+    case 1:
+      if (map.M2 >= kBigRows)
+        return glu_launch_t<1, LPR, XF32, true>(dev, map, epi, x, ldx_bytes, C, s);
+      return glu_launch_t<1, LPR, XF32, false>(dev, map, epi, x, ldx_bytes, C, s);
+    case 2: return glu_launch_t<2, LPR, XF32, false>(dev, map, epi, x, ldx_bytes, C, s);
+    case 3: return glu_launch_t<3, LPR, XF32, false>(dev, map, epi, x, ldx_bytes, C, s);
+    case 4: return glu_launch_t<4, LPR, XF32, false>(dev, map, epi, x, ldx_bytes, C, s);
+    case 5: return glu_launch_t<5, LPR, XF32, false>(dev, map, epi, x, ldx_bytes, C, s);
+    case 6: return glu_launch_t<6, LPR, XF32, false>(dev, map, epi, x, ldx_bytes, C, s);
+    case 7: return glu_launch_t<7, LPR, XF32, false>(dev, map, epi, x, ldx_bytes, C, s);
+    case 8: return glu_launch_t<8, LPR, XF32, false>(dev, map, epi, x, ldx_bytes, C, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_glu(const DevInfo& dev, const HMat& Gm, const HMat& Um, const void* x,
+                      bool x_f32, void* h, bool h_f16, int nt, hipStream_t s) {
+  GluMap map;
+  map.qg = Gm.qs;
+  map.dg = Gm.d;
+  map.qu = Um.qs;
+  map.du = Um.d;
+  map.ldqg = Gm.ld_qs;
+  map.lddg = Gm.ld_d;
+  map.ldqu = Um.ld_qs;
+  map.lddu = Um.ld_d;
+  map.M2 = 2 * Gm.M;
+  GluEpi epi;
+  epi.h = (char*)h;
+  epi.M = Gm.M;
+  epi.f16 = h_f16;
+  const int C = (int)(Gm.K / 16);
+  const int64_t ldx_bytes = Gm.K * (x_f32 ? 4 : 2);
+  const char* xp = (const char*)x;
+  const int lpr = lanes_per_row(Gm.K);
+  if (x_f32) {
+    if (lpr == 64) return glu_launch_nt<64, true>(dev, nt, map, epi, xp, ldx_bytes, C, s);
+    if (lpr == 32) return glu_launch_nt<32, true>(dev, nt, map, epi, xp, ldx_bytes, C, s);
+    return glu_launch_nt<16, true>(dev, nt, map, epi, xp, ldx_bytes, C, s);
+  }
+  if (lpr == 64) return glu_launch_nt<64, false>(dev, nt, map, epi, xp, ldx_bytes, C, s);
+  if (lpr == 32) return glu_launch_nt<32, false>(dev, nt, map, epi, xp, ldx_bytes, C, s);
+  return glu_launch_nt<16, false>(dev, nt, map, epi, xp, ldx_bytes, C, s);
+}
+
 template <int NT, int LPR, bool XF32, bool BIG>
 static hipError_t launch_t(const DevInfo& dev, DenseMap map, DenseEpi epi, const char* x,
                            int64_t ldx_bytes, int C, hipStream_t s) {

@@ -89,6 +89,9 @@ hipError_t launch_moe_gemv(const DevInfo& dev, const HBank& W, const MoeWs& ws, 
 hipError_t launch_moe_gate_up(const DevInfo& dev, const HBank& G, const HBank& U,
                               const MoeWs& ws, int topk, const void* x, bool x_f32, float* h,
                               hipStream_t s);
+// h[n][m] = silu(G x_n)[m] * (U x_n)[m]; G, U of one shape; h fp32 or fp16.
+hipError_t launch_glu(const DevInfo& dev, const HMat& G, const HMat& U, const void* x,
+                      bool x_f32, void* h, bool h_f16, int nt, hipStream_t s);
 // Router: ids [T][topk] and softmax weights [T][topk] from logits [T][E].
 constexpr int kRouterMaxE = 4096;  // 64 experts per lane of the token's wave
 constexpr int kRouterMaxK = 64;    // one picked logit per lane

@@ -113,6 +113,16 @@ def test_gemv_validation(L):
     W2 = _mat(K=512, ld_qs=512, ld_d=16)
     assert L.q8_gemv_pair(ctypes.byref(_mat()), ctypes.byref(W2), X, 1, Y, Y + 4096, 2, 1, None) == -2
     assert L.q8_gemv_pair(ctypes.byref(_mat()), ctypes.byref(_mat()), X, 1, Y, Y + 16, 2, 1, None) == -8
+    # fused gate/up + SiLU
+    sl = L.q8_gemv_pair_silu
+    assert sl(ctypes.byref(_mat()), None, X, 1, Y, 2, 1, None) == -1
+    assert sl(ctypes.byref(_mat()), ctypes.byref(W2), X, 1, Y, 2, 1, None) == -2
+    assert sl(ctypes.byref(_mat()), ctypes.byref(_mat(M=32)), X, 1, Y, 2, 1, None) == -2
+    assert sl(ctypes.byref(_mat()), ctypes.byref(_mat()), X, 1, Y, 2, 0, None) == -2
+    assert sl(ctypes.byref(_mat()), ctypes.byref(_mat()), X, 1, 0, 2, 1, None) == -1
+    assert sl(ctypes.byref(_mat()), ctypes.byref(_mat()), X, 1, Y, 5, 1, None) == -4
+    assert sl(ctypes.byref(_mat()), ctypes.byref(_mat()), X, 1, Y + 2, 2, 1, None) == -3
+    assert sl(ctypes.byref(_mat()), ctypes.byref(_mat()), X, 1, X + 32, 2, 1, None) == -8
 
 
 def test_lmhead_validation(L):

@@ -80,7 +80,8 @@ def test_integer_exact_bitwise(M, K, N):
 
 
 SHAPES = [(1024, 1024, 1), (1000, 96, 3), (333, 2048, 4), (517, 768, 8), (64, 32, 2),
-          (129, 800, 5), (2050, 5120, 2), (7, 160, 9), (1, 1024, 1)]
+          (129, 800, 5), (2050, 5120, 2), (7, 160, 9), (1, 1024, 1), (600, 1024, 12),
+          (300, 2048, 16)]
 
 
 @pytest.mark.parametrize("M,K,N", SHAPES)
