@@ -426,3 +426,20 @@ def gate_up_silu(qg, dg, qu, du, x, threads: int = 1, out_dtype: str = "f32"):
     if out_dtype == "f16":
         bh = bh + 0.5 * fp16_ulp(h)
     return dict(h=h, bh=bh, g=g, u=u)
+
+
+# ---------------------------------------------------------------- masked LM head
+def argmax_masked(L_sub: np.ndarray, A_sub: np.ndarray, row_ids: np.ndarray):
+    """Argmax over a ranked subset of the vocabulary (the pages' draft LM
+    head, which reads only the rows of a chosen subset: memra wiki, MTP
+    speculative decoding with a vocab-masked draft head).
+
+    L_sub [N][S] are the logits of the subset rows in subset order, A_sub
+    their sum|d*q*x|; row_ids [S] the vocabulary id of each subset row. The
+    winner is the first maximum in subset order, reported as its vocabulary
+    id; gating as ``argmax_gate`` on the subset. Returns (ids int64 [N],
+    gated bool [N], candidate vocabulary ids per token).
+    """
+    row_ids = np.asarray(row_ids, np.int64)
+    istar, gated, cands = argmax_gate(L_sub, A_sub)
+    return row_ids[istar], gated, [row_ids[c] for c in cands]

@@ -496,3 +496,29 @@ def test_gate_up_silu_large_gate_is_identity_times_up():
     r = oracle.gate_up_silu(qg, d, qu, d, x)
     assert math.isclose(r["h"][0, 0], r["g"][0, 0] * r["u"][0, 0], rel_tol=1e-12)
     assert abs(r["h"][0, 1]) < 1e-300 * abs(r["u"][0, 1]) + 1e-300
+
+
+# ---------------------------------------------------------------- masked LM head
+def test_masked_argmax_identity_subset_equals_full():
+    c = synth.lmhead_case(600, 256, 3, seed=1)
+    L, A = oracle.gemv(c.q, c.d, c.x)
+    ids, gated, _ = oracle.argmax_masked(L, A, np.arange(600))
+    assert np.array_equal(ids, oracle.argmax_first(L)) and gated.all()
+
+
+def test_masked_argmax_maps_back_and_keeps_subset_order_for_ties():
+    """A subset holding the full argmax row returns that vocabulary id; equal
+    logits go to the earlier position in the subset, whatever their ids."""
+    c = synth.lmhead_case(600, 256, 2, seed=2)
+    L, A = oracle.gemv(c.q, c.d, c.x)
+    full = oracle.argmax_first(L)
+    rng = np.random.default_rng(0)
+    sub = rng.choice(600, 100, replace=False)
+    sub[37] = full[0]
+    sub[60] = full[1] if full[1] != full[0] else sub[60]
+    ids, gated, _ = oracle.argmax_masked(L[:, sub], A[:, sub], sub)
+    assert ids[0] == full[0]
+    # exact ties: two positions with identical logits, higher id first
+    Lt = np.array([[1.0, 3.0, 3.0, 2.0]])
+    ids, gated, cands = oracle.argmax_masked(Lt, np.zeros_like(Lt), np.array([5, 90, 7, 1]))
+    assert ids[0] == 90 and not gated[0] and set(cands[0]) == {90, 7}
