@@ -172,6 +172,21 @@ size_t q8_lmhead_ws_bytes(int64_t V, int N);
 int q8_lmhead_argmax(const q8_matrix *W, const void *x, int x_dt, float *logits,
                      int32_t *ids, int N, void *ws, size_t ws_bytes, void *stream);
 
+/* Draft LM head over a ranked subset of the vocabulary (the pages' MTP
+ * drafting reads a vocab-masked head of a few tens of thousands of rows
+ * instead of the whole vocabulary; memra wiki, feature list, MTP
+ * speculative decoding). W holds the S subset rows, packed at load time
+ * (gathered from the full head's blocks in subset order); row_ids [dev]
+ * int32 [S] is the vocabulary id of each row. As q8_lmhead_argmax over W,
+ * except ids[n] = row_ids[s*] where s* is the first maximum in subset
+ * order (equal logits go to the earlier subset position); logits, if not
+ * NULL, are [N][S] in subset order and bitwise equal to the full head's
+ * logits at those rows. row_ids values are copied, never dereferenced.
+ * Same workspace contract as q8_lmhead_argmax. */
+int q8_lmhead_argmax_rows(const q8_matrix *W, const int32_t *row_ids, const void *x, int x_dt,
+                          float *logits, int32_t *ids, int N, void *ws, size_t ws_bytes,
+                          void *stream);
+
 /* ------------------------------------------------------------ routed experts
  * Expert-major CSR batching of routed experts (memra wiki, feature list,
  * "MoE ... expert-major CSR batching"): the routed (token, slot) pairs are

@@ -30,6 +30,7 @@ Q8_DT_F32 = 2
 EXPORTS = (
     "q8_status_str", "q8_device_check", "q8_pack_layout", "q8_pack_host", "q8_unpack_host",
     "q8_gemv", "q8_gemv_pair", "q8_gemv_pair_silu", "q8_lmhead_ws_bytes", "q8_lmhead_argmax",
+    "q8_lmhead_argmax_rows",
     "q8_moe_ws_bytes", "q8_moe_ws_layout", "q8_moe_gemv", "q8_moe_ffn", "q8_moe_topk_softmax",
     "q8_moe_router",
 )
@@ -75,6 +76,7 @@ def lib() -> ctypes.CDLL:
             "q8_gemv_pair_silu": ([pm, pm, vp, i32, vp, i32, i32, vp], i32),
             "q8_lmhead_ws_bytes": ([i64, i32], sz),
             "q8_lmhead_argmax": ([pm, vp, i32, vp, vp, i32, vp, sz, vp], i32),
+            "q8_lmhead_argmax_rows": ([pm, vp, vp, i32, vp, vp, i32, vp, sz, vp], i32),
             "q8_moe_ws_bytes": ([i32, i32, i32, i64, i64], sz),
             "q8_moe_ws_layout": ([i32, i32, i32, i64, i64, vp], i32),
             "q8_moe_gemv": ([pb, vp, vp, vp, i32, i32, vp, i32, i32, vp, sz, vp], i32),
@@ -266,8 +268,10 @@ def lmhead_ws_bytes(V: int, N: int) -> int:
     return lib().q8_lmhead_ws_bytes(V, N)
 
 
-def lmhead_argmax(W: PackedQ8, x, logits=True, ids=None, ws=None, stream=None):
-    """Returns (logits fp32 [N][V] or None, ids int32 [N])."""
+def lmhead_argmax(W: PackedQ8, x, logits=True, ids=None, ws=None, stream=None, row_ids=None):
+    """Returns (logits fp32 [N][V] or None, ids int32 [N]). With ``row_ids``
+    (int32 [V] on the device) W is a draft head over a vocabulary subset and
+    ids are mapped through it."""
     import torch
     x = _as_2d(x, W.K)
     N = x.shape[0]
@@ -280,10 +284,18 @@ def lmhead_argmax(W: PackedQ8, x, logits=True, ids=None, ws=None, stream=None):
     nws = lmhead_ws_bytes(W.M, N)
     if ws is None:
         ws = torch.zeros((nws,), dtype=torch.uint8, device=x.device)
-    _check(lib().q8_lmhead_argmax(ctypes.byref(W.cmat()), x.data_ptr(), _dt(x),
-                                  logits.data_ptr() if logits is not None else None,
-                                  ids.data_ptr(), N, ws.data_ptr(), ws.numel() * ws.element_size(),
-                                  _stream(stream)), "q8_lmhead_argmax")
+    lp = logits.data_ptr() if logits is not None else None
+    nb = ws.numel() * ws.element_size()
+    if row_ids is None:
+        rc = lib().q8_lmhead_argmax(ctypes.byref(W.cmat()), x.data_ptr(), _dt(x), lp, ids.data_ptr(),
+                                    N, ws.data_ptr(), nb, _stream(stream))
+    else:
+        if row_ids.dtype != torch.int32 or row_ids.numel() != W.M:
+            raise ValueError("row_ids must be int32 with one entry per row of W")
+        rc = lib().q8_lmhead_argmax_rows(ctypes.byref(W.cmat()), row_ids.data_ptr(), x.data_ptr(),
+                                         _dt(x), lp, ids.data_ptr(), N, ws.data_ptr(), nb,
+                                         _stream(stream))
+    _check(rc, "q8_lmhead_argmax")
     return logits, ids
 
 

@@ -258,22 +258,29 @@ size_t q8_lmhead_ws_bytes(int64_t V, int N) {
   return q8::lmhead_ws_bytes();
 }
 
-int q8_lmhead_argmax(const q8_matrix* W, const void* x, int x_dt, float* logits, int32_t* ids,
-                     int N, void* ws, size_t ws_bytes, void* stream) {
+static int lmhead_impl(const q8_matrix* W, const int32_t* row_ids, const void* x, int x_dt,
+                       float* logits, int32_t* ids, int N, void* ws, size_t ws_bytes,
+                       void* stream) {
   int rc = check_matrix(W);
   if (rc) return rc;
   if (!x || !ids) return Q8_ERR_NULL;
   if (N < 1) return Q8_ERR_SHAPE;
   const size_t xs = dt_size(x_dt);
   if (!xs) return Q8_ERR_DTYPE;
-  if (!aligned(x, 16) || !aligned(ids, 4) || (logits && !aligned(logits, 4))) return Q8_ERR_ALIGN;
+  if (!aligned(x, 16) || !aligned(ids, 4) || (logits && !aligned(logits, 4)) ||
+      (row_ids && !aligned(row_ids, 4)))
+    return Q8_ERR_ALIGN;
   if (!ws || !aligned(ws, 16) || ws_bytes < q8_lmhead_ws_bytes(W->M, N)) return Q8_ERR_WORKSPACE;
   const size_t xbytes = (size_t)N * W->K * xs;
   const size_t lbytes = logits ? (size_t)N * W->M * 4 : 0;
+  const size_t rbytes = row_ids ? (size_t)W->M * 4 : 0;
   if ((logits && overlap(x, xbytes, logits, lbytes)) || overlap(x, xbytes, ids, 4 * (size_t)N) ||
       (logits && overlap(logits, lbytes, ids, 4 * (size_t)N)) ||
       overlap(ws, ws_bytes, x, xbytes) || overlap(ws, ws_bytes, ids, 4 * (size_t)N) ||
-      (logits && overlap(ws, ws_bytes, logits, lbytes)))
+      (logits && overlap(ws, ws_bytes, logits, lbytes)) ||
+      (row_ids && (overlap(row_ids, rbytes, ids, 4 * (size_t)N) ||
+                   overlap(row_ids, rbytes, ws, ws_bytes) ||
+                   (logits && overlap(row_ids, rbytes, logits, lbytes)))))
     return Q8_ERR_ALIAS;
   const DevInfo* dev = nullptr;
   rc = current_device(&dev);
@@ -286,11 +293,23 @@ int q8_lmhead_argmax(const q8_matrix* W, const void* x, int x_dt, float* logits,
     const int nt = N - n0 < per_pass ? N - n0 : per_pass;
     const char* xp = (const char*)x + (size_t)n0 * W->K * xs;
     float* lp = logits ? logits + (size_t)n0 * W->M : nullptr;
-    hipError_t e = q8::launch_lmhead(*dev, A, xp, xf, lp, W->M, ids + n0, (char*)ws, nt,
+    hipError_t e = q8::launch_lmhead(*dev, A, row_ids, xp, xf, lp, W->M, ids + n0, (char*)ws, nt,
                                      (hipStream_t)stream);
     if (e != hipSuccess) return Q8_ERR_LAUNCH;
   }
   return Q8_OK;
+}
+
+int q8_lmhead_argmax(const q8_matrix* W, const void* x, int x_dt, float* logits, int32_t* ids,
+                     int N, void* ws, size_t ws_bytes, void* stream) {
+  return lmhead_impl(W, nullptr, x, x_dt, logits, ids, N, ws, ws_bytes, stream);
+}
+
+int q8_lmhead_argmax_rows(const q8_matrix* W, const int32_t* row_ids, const void* x, int x_dt,
+                          float* logits, int32_t* ids, int N, void* ws, size_t ws_bytes,
+                          void* stream) {
+  if (!row_ids) return Q8_ERR_NULL;
+  return lmhead_impl(W, row_ids, x, x_dt, logits, ids, N, ws, ws_bytes, stream);
 }
 
 // ------------------------------------------------------------ routed experts

@@ -53,8 +53,8 @@ hipError_t launch_gemv(const DevInfo& dev, const HMat& A, const HMat* B, const v
 // argmax slots and counters; it must be zero before the first pass and is
 // zero again after each completed pass.
 size_t lmhead_ws_bytes();
-hipError_t launch_lmhead(const DevInfo& dev, const HMat& W, const void* x, bool x_f32,
-                         float* logits, int64_t ld_logits, int32_t* ids, char* ws,
+hipError_t launch_lmhead(const DevInfo& dev, const HMat& W, const int32_t* row_ids, const void* x,
+                         bool x_f32, float* logits, int64_t ld_logits, int32_t* ids, char* ws,
                          int nt, hipStream_t s);
 
 // Routed experts.

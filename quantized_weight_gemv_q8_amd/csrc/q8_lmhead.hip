@@ -15,7 +15,9 @@
 // needs zero-filling only before its first use. Key = (order-preserving
 // bits of the fp32 logit, with -0 mapped to +0) << 32 | ~row, so the
 // maximum key is the largest logit and, among equal logits, the lowest
-// row; the result does not depend on the order of the workgroups.
+// row; the result does not depend on the order of the workgroups. A draft
+// head (a packed subset of the vocabulary rows) reports the winner through
+// its row-id table.
 #include "q8_engine.hpp"
 #include "q8_internal.h"
 
@@ -42,6 +44,7 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t k) {
 struct LmMap {
   MatDesc w;
   int64_t V;
+  const int32_t* row_ids;  // null, or the vocabulary id of each row (a draft head's subset)
   __device__ __forceinline__ bool row(int64_t i, const int8_t*& q, const uint16_t*& d) const {
     q = w.qs + i * w.ld_qs;
     d = w.d + i * w.ld_d;
@@ -207,7 +210,8 @@ __global__ __launch_bounds__(kBlock) void lmhead_kernel(LmMap map, float* logits
         for (int n = 0; n < NT; ++n) {
           const uint64_t m = __hip_atomic_exchange(w.slot + n, (uint64_t)0, __ATOMIC_RELAXED,
                                                    __HIP_MEMORY_SCOPE_AGENT);
-          ids[n] = (int32_t)(~(uint32_t)(m & 0xffffffffu));
+          const uint32_t row = ~(uint32_t)(m & 0xffffffffu);
+          ids[n] = map.row_ids ? map.row_ids[row] : (int32_t)row;
         }
       }
     }
@@ -258,12 +262,13 @@ static hipError_t lm_launch_nt(const DevInfo& dev, int nt, LmMap map, float* log
 
 size_t lmhead_ws_bytes() { return kLmWsBytes; }
 
-hipError_t launch_lmhead(const DevInfo& dev, const HMat& W, const void* x, bool x_f32,
-                         float* logits, int64_t ld_logits, int32_t* ids, char* ws, int nt,
-                         hipStream_t s) {
+hipError_t launch_lmhead(const DevInfo& dev, const HMat& W, const int32_t* row_ids, const void* x,
+                         bool x_f32, float* logits, int64_t ld_logits, int32_t* ids, char* ws,
+                         int nt, hipStream_t s) {
   LmMap map;
   map.w = MatDesc{W.qs, W.d, W.ld_qs, W.ld_d};
   map.V = W.M;
+  map.row_ids = row_ids;
   const int C = (int)(W.K / 16);
   const int64_t ldx_bytes = W.K * (x_f32 ? 4 : 2);
   const char* xp = (const char*)x;

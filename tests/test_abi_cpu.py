@@ -143,6 +143,17 @@ def test_lmhead_validation(L):
     assert rc(ws=WS + 4) == -5
     assert rc(ids=Y + 2) == -3
     assert rc(ids=Y) == -8  # ids inside logits
+    RID = 0x700000
+
+    def rr(rid=RID, **kw):
+        a = dict(ok, **kw)
+        return L.q8_lmhead_argmax_rows(ctypes.byref(W), rid, a["x"], a["xdt"], a["logits"],
+                                       a["ids"], a["N"], a["ws"], a["nws"], None)
+    assert rr(rid=0) == -1
+    assert rr(rid=RID + 2) == -3
+    assert rr(rid=Y + 0x10000 - 8) == -8  # row ids overlap ids
+    assert rr(rid=WS) == -8
+    assert rr(nws=n - 1) == -5
 
 
 def test_moe_validation(L):

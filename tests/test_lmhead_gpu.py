@@ -125,3 +125,64 @@ def test_workspace_reused_across_shapes_returns_to_zero():
         logits, ids = q8.lmhead_argmax(upload(c.q, c.d), dev(c.x), ws=ws)
         check_lmhead(c, host(logits), host(ids))
         assert not host(ws).any(), "workspace not returned to zero"
+
+
+# ---------------------------------------------------------------- draft head (vocabulary subset)
+def gather(c, rows):
+    return synth.LmHeadCase(c.q[rows], c.d[rows], c.x, c.planted_rows, c.planted_target)
+
+
+@pytest.mark.parametrize("N", [1, 4])
+def test_draft_head_subset_of_full_vocab(vocab, N):
+    """A 32768-row ranked subset containing the planted rows: ids come back
+    as vocabulary ids and match the oracle on the subset; the subset's
+    logits are bitwise the full head's logits at those rows."""
+    note(f"draft head 32768 of 151936 N={N}")
+    c4, W = vocab
+    rng = np.random.default_rng(5)
+    others = np.setdiff1d(np.arange(151936), c4.planted_rows[:4])
+    rows = rng.choice(others, 32768, replace=False).astype(np.int32)
+    rows[rng.choice(32768, 4, replace=False)] = c4.planted_rows[:4]
+    assert len(np.unique(rows)) == 32768
+    sub = gather(c4, rows)
+    Ws = upload(sub.q, sub.d)
+    x = dev(c4.x[:N])
+    logits, ids = q8.lmhead_argmax(Ws, x, row_ids=dev(rows))
+    logits, ids = host(logits), host(ids)
+    L, A = oracle.gemv(sub.q, sub.d, c4.x[:N], threads())
+    assert_parity(logits, L, A, what="draft logits")
+    want, gated, cands = oracle.argmax_masked(L, A, rows)
+    for n in range(N):
+        assert ids[n] == want[n] if gated[n] else ids[n] in cands[n]
+    assert list(ids) == list(c4.planted_rows[:N])
+    full_logits, _ = q8.lmhead_argmax(W, x)
+    assert np.array_equal(host(full_logits)[:, rows].view(np.uint32), logits.view(np.uint32))
+    # lean path
+    _, ids2 = q8.lmhead_argmax(Ws, x, logits=False, row_ids=dev(rows))
+    assert np.array_equal(host(ids2), ids)
+
+
+def test_draft_head_ties_go_to_earlier_subset_position():
+    note("draft head ties")
+    K, S = 256, 900
+    rng = np.random.default_rng(3)
+    q = rng.integers(-20, 21, size=(S, K)).astype(np.int8)
+    d = np.full((S, K // 32), 2.0 ** -6, np.float16)
+    x = np.abs(rng.integers(-2, 3, size=(1, K))).astype(np.float16)  # integer data: exact logits
+    q[500] = 60
+    q[120] = q[500]  # the same winning row at an earlier position
+    rows = rng.permutation(100000)[:S].astype(np.int32)
+    rows[120], rows[500] = 99999, 3  # the earlier position has the larger vocabulary id
+    _, ids = q8.lmhead_argmax(upload(q, d), dev(x), row_ids=dev(rows))
+    assert host(ids)[0] == 99999
+
+
+def test_draft_head_identity_subset_equals_plain_head():
+    note("draft head identity subset")
+    c = synth.lmhead_case(5000, 1024, 3, seed=9)
+    W = upload(c.q, c.d)
+    x = dev(c.x)
+    l1, i1 = q8.lmhead_argmax(W, x)
+    l2, i2 = q8.lmhead_argmax(W, x, row_ids=dev(np.arange(5000, dtype=np.int32)))
+    assert np.array_equal(host(i1), host(i2))
+    assert np.array_equal(host(l1).view(np.uint32), host(l2).view(np.uint32))
