@@ -443,3 +443,24 @@ def argmax_masked(L_sub: np.ndarray, A_sub: np.ndarray, row_ids: np.ndarray):
     row_ids = np.asarray(row_ids, np.int64)
     istar, gated, cands = argmax_gate(L_sub, A_sub)
     return row_ids[istar], gated, [row_ids[c] for c in cands]
+
+
+# ---------------------------------------------------------------- Q4_0
+def decode_q4_0_blocks(blocks: np.ndarray):
+    """GGUF Q4_0 blocks [M][K/32][18] -> (q int8 [M][K] in -8..7, d float16 [M][K/32]).
+
+    The pages decode Q4_0 next to Q8_0 (memra wiki, feature list) but print
+    no bytes; this is the standard GGUF block: little-endian fp16 d, then 16
+    bytes whose low nibbles are elements 0..15 and high nibbles elements
+    16..31 of the block, each stored with +8; the weight is d * (nibble - 8).
+    The GEMV over the decoded (q, d) is then the same definition as for
+    Q8_0 (``gemv``).
+    """
+    b = np.asarray(blocks, np.uint8)
+    M, nb, _ = b.shape
+    d = (b[:, :, 0].astype(np.uint16) | (b[:, :, 1].astype(np.uint16) << 8)).view(np.float16)
+    qs = b[:, :, 2:].astype(np.int16)
+    lo = (qs & 0x0F) - 8
+    hi = (qs >> 4) - 8
+    q = np.concatenate([lo, hi], axis=2).reshape(M, nb * 32).astype(np.int8)
+    return q, d

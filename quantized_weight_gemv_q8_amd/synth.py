@@ -256,3 +256,34 @@ def router_case(T: int, E: int, seed: int = 0, ties: bool = True) -> np.ndarray:
             L[2, E // 3] = np.float32(-0.0)
             L[2, E // 4] = np.float32(0.0)
     return L
+
+
+# ---------------------------------------------------------------- Q4_0
+def draw_weights_q4_0(rng: np.random.Generator, M: int, K: int):
+    """One Q4_0 matrix [M][K]: (q int8 [M][K] uniform in -8..7, d float16
+    [M][K/32] = |N(0, 0.02)| / 8, the same weight scale as the Q8_0 draws)."""
+    q = rng.integers(-8, 8, size=(M, K), dtype=np.int8)
+    d = (np.abs(rng.normal(0.0, 0.02, size=(M, K // QK))) / 8.0).astype(np.float16)
+    return q, d
+
+
+def to_gguf_q4_0_blocks(q: np.ndarray, d: np.ndarray) -> np.ndarray:
+    """(q in -8..7 [M][K], d [M][K/32]) -> GGUF Q4_0 blocks uint8 [M][K/32][18]:
+    fp16 d little-endian, then byte j = (q[j+16] + 8) << 4 | (q[j] + 8)."""
+    M, K = q.shape
+    nb = K // QK
+    u = (q.astype(np.int16) + 8).astype(np.uint8).reshape(M, nb, 32)
+    out = np.empty((M, nb, 18), np.uint8)
+    dv = np.ascontiguousarray(d, np.float16).view(np.uint16)
+    out[:, :, 0] = (dv & 0xFF).astype(np.uint8)
+    out[:, :, 1] = (dv >> 8).astype(np.uint8)
+    out[:, :, 2:] = u[:, :, :16] | (u[:, :, 16:] << 4)
+    return out
+
+
+def q4_0_case(M: int, K: int, N: int, seed: int = 0) -> GemvCase:
+    """Q4_0 GEMV workload: weights (q in -8..7, d) then x ~ N(0,1) fp16."""
+    rng = rng_for(seed)
+    q, d = draw_weights_q4_0(rng, M, K)
+    x = draw_x(rng, N, K)
+    return GemvCase(q, d, x)

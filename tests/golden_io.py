@@ -17,8 +17,9 @@ def _expand(tokens):
     return out
 
 
-def load_handbuilt(name="q8_0_handbuilt.txt"):
-    """Yield dicts: name, M, K, N, blocks uint8 [M][K/32][34], x fp16 [N][K], y float64 [N][M]."""
+def load_handbuilt(name="q8_0_handbuilt.txt", block_bytes=34):
+    """Yield dicts: name, M, K, N, blocks uint8 [M][K/32][block_bytes], x fp16 [N][K],
+    y float64 [N][M]. block_bytes is 34 for Q8_0 and 18 for Q4_0."""
     cases, cur = [], None
     with open(os.path.join(GOLDEN, name)) as f:
         for line in f:
@@ -32,7 +33,7 @@ def load_handbuilt(name="q8_0_handbuilt.txt"):
                 cases.append(cur)
             elif key == "blocks":
                 b = np.array([int(t, 16) for t in _expand(rest.split())], np.uint8)
-                cur["blocks"] = b.reshape(cur["M"], cur["K"] // 32, 34)
+                cur["blocks"] = b.reshape(cur["M"], cur["K"] // 32, block_bytes)
             elif key == "x":
                 v = np.array([int(t, 16) for t in _expand(rest.split())], np.uint16)
                 cur["x"] = v.view(np.float16).reshape(cur["N"], cur["K"])

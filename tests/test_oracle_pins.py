@@ -522,3 +522,33 @@ def test_masked_argmax_maps_back_and_keeps_subset_order_for_ties():
     Lt = np.array([[1.0, 3.0, 3.0, 2.0]])
     ids, gated, cands = oracle.argmax_masked(Lt, np.zeros_like(Lt), np.array([5, 90, 7, 1]))
     assert ids[0] == 90 and not gated[0] and set(cands[0]) == {90, 7}
+
+
+# ---------------------------------------------------------------- Q4_0
+@pytest.mark.parametrize("case", load_handbuilt("q4_0_handbuilt.txt", 18), ids=lambda c: c["name"])
+def test_q4_0_handbuilt_fixtures(case):
+    q, d = oracle.decode_q4_0_blocks(case["blocks"])
+    y, _ = oracle.gemv(q, d, case["x"])
+    assert np.array_equal(y, case["y"]), case["why"]
+
+
+def test_q4_0_decode_every_nibble_position():
+    """Each nibble lands on its own element: a block whose byte j holds
+    (a_j, b_j) in (low, high) nibbles decodes to a_j - 8 at j and b_j - 8 at
+    j + 16, for every j and every nibble value."""
+    for v in range(16):
+        blk = np.full((1, 1, 18), 0x88, np.uint8)
+        blk[0, 0, :2] = (0x00, 0x3C)
+        for j in range(16):
+            blk[0, 0, 2 + j] = ((15 - v) << 4) | v
+        q, d = oracle.decode_q4_0_blocks(blk)
+        assert d[0, 0] == 1.0
+        assert np.all(q[0, :16] == v - 8) and np.all(q[0, 16:] == 7 - v)
+
+
+def test_q4_0_synth_roundtrip():
+    rng = np.random.default_rng(0)
+    q, d = synth.draw_weights_q4_0(rng, 7, 96)
+    assert q.min() >= -8 and q.max() <= 7
+    q2, d2 = oracle.decode_q4_0_blocks(synth.to_gguf_q4_0_blocks(q, d))
+    assert np.array_equal(q2, q) and np.array_equal(d2.view(np.uint16), d.view(np.uint16))
