@@ -151,6 +151,31 @@ int q8_gemv_pair(const q8_matrix *Wa, const q8_matrix *Wb, const void *x, int x_
 int q8_gemv_pair_silu(const q8_matrix *Wg, const q8_matrix *Wu, const void *x, int x_dt,
                       void *h, int h_dt, int N, void *stream);
 
+/* ------------------------------------------------------------ Q4_0
+ * The same GEMV family over GGUF Q4_0 weights (memra wiki, feature list:
+ * "NVFP4 / Q4_0 / Q8_0 decode ... split-plane repacked matvecs"). A Q4_0
+ * block is 18 bytes: little-endian fp16 d, then 16 bytes whose low nibbles
+ * are elements 0..15 and high nibbles elements 16..31, each stored as
+ * q + 8 (q in [-8, 7]); the weight is d * q. The packed matrix is a
+ * q8_matrix whose qs is the nibble plane: the 16 data bytes of each block,
+ * in GGUF order, rows of ld_qs >= K/2 bytes (a multiple of 16), 16-byte
+ * aligned; d is the scale plane as for Q8_0.
+ *
+ * q8_pack_q4_0_layout / q8_pack_q4_0_host / q8_unpack_q4_0_host: as the
+ * Q8_0 packer (ld_qs = K/2, ld_d = K/32 rounded up to 8, padding zeroed,
+ * byte-exact round trip), for blocks [host] of 18 bytes.
+ * q8_gemv_q4_0: y[n][m] = sum_k d[m][k/32] * q[m][k] * x[n][k], with the
+ * same arguments, dtypes, pass structure, N-invariance and errors as
+ * q8_gemv. */
+int q8_pack_q4_0_layout(int64_t M, int64_t K, int64_t *ld_qs, int64_t *ld_d, size_t *qs_bytes,
+                        size_t *d_bytes);
+int q8_pack_q4_0_host(const void *blocks, int64_t M, int64_t K, uint8_t *qs, int64_t ld_qs,
+                      uint16_t *d, int64_t ld_d);
+int q8_unpack_q4_0_host(const uint8_t *qs, int64_t ld_qs, const uint16_t *d, int64_t ld_d,
+                        int64_t M, int64_t K, void *blocks);
+int q8_gemv_q4_0(const q8_matrix *W, const void *x, int x_dt, void *y, int y_dt, int N,
+                 void *stream);
+
 /* ------------------------------------------------------------ LM head
  * logits[n][v] = W x_n (as q8_gemv with fp32 output) and
  * ids[n] = the smallest v with logits[n][v] == max_v logits[n][v]

@@ -29,6 +29,7 @@ Q8_DT_F32 = 2
 # every function the header declares
 EXPORTS = (
     "q8_status_str", "q8_device_check", "q8_pack_layout", "q8_pack_host", "q8_unpack_host",
+    "q8_pack_q4_0_layout", "q8_pack_q4_0_host", "q8_unpack_q4_0_host", "q8_gemv_q4_0",
     "q8_gemv", "q8_gemv_pair", "q8_gemv_pair_silu", "q8_lmhead_ws_bytes", "q8_lmhead_argmax",
     "q8_lmhead_argmax_rows",
     "q8_moe_ws_bytes", "q8_moe_ws_layout", "q8_moe_gemv", "q8_moe_ffn", "q8_moe_topk_softmax",
@@ -71,6 +72,10 @@ def lib() -> ctypes.CDLL:
             "q8_pack_layout": ([i64, i64, vp, vp, vp, vp], i32),
             "q8_pack_host": ([vp, i64, i64, vp, i64, vp, i64], i32),
             "q8_unpack_host": ([vp, i64, vp, i64, i64, i64, vp], i32),
+            "q8_pack_q4_0_layout": ([i64, i64, vp, vp, vp, vp], i32),
+            "q8_pack_q4_0_host": ([vp, i64, i64, vp, i64, vp, i64], i32),
+            "q8_unpack_q4_0_host": ([vp, i64, vp, i64, i64, i64, vp], i32),
+            "q8_gemv_q4_0": ([pm, vp, i32, vp, i32, i32, vp], i32),
             "q8_gemv": ([pm, vp, i32, vp, i32, i32, vp], i32),
             "q8_gemv_pair": ([pm, pm, vp, i32, vp, vp, i32, i32, vp], i32),
             "q8_gemv_pair_silu": ([pm, pm, vp, i32, vp, i32, i32, vp], i32),
@@ -197,6 +202,50 @@ def unpack(W: PackedQ8) -> np.ndarray:
     return unpack_host(W.qs.cpu().numpy(), W.d.cpu().numpy().view(np.uint16), W.M, W.K)
 
 
+# ---------------------------------------------------------------- Q4_0 packing
+def pack_q4_0_layout(M: int, K: int):
+    ld_qs, ld_d = ctypes.c_int64(), ctypes.c_int64()
+    qb, db = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(lib().q8_pack_q4_0_layout(M, K, ctypes.byref(ld_qs), ctypes.byref(ld_d),
+                                     ctypes.byref(qb), ctypes.byref(db)), "q8_pack_q4_0_layout")
+    return ld_qs.value, ld_d.value, qb.value, db.value
+
+
+def pack_q4_0_host(blocks: np.ndarray):
+    """GGUF Q4_0 blocks uint8 [M][K/32][18] -> host planes (nibbles uint8
+    [M][ld_qs], d uint16 [M][ld_d])."""
+    blocks = np.ascontiguousarray(blocks, np.uint8)
+    M, nb, bb = blocks.shape
+    if bb != 18:
+        raise ValueError("Q4_0 blocks are 18 bytes")
+    K = nb * 32
+    ld_qs, ld_d, _, _ = pack_q4_0_layout(M, K)
+    qs = np.empty((M, ld_qs), np.uint8)
+    d = np.empty((M, ld_d), np.uint16)
+    _check(lib().q8_pack_q4_0_host(blocks.ctypes.data, M, K, qs.ctypes.data, ld_qs, d.ctypes.data,
+                                   ld_d), "q8_pack_q4_0_host")
+    return qs, d
+
+
+def unpack_q4_0_host(qs: np.ndarray, d: np.ndarray, M: int, K: int) -> np.ndarray:
+    qs = np.ascontiguousarray(qs, np.uint8)
+    d = np.ascontiguousarray(d, np.uint16)
+    out = np.empty((M, K // 32, 18), np.uint8)
+    _check(lib().q8_unpack_q4_0_host(qs.ctypes.data, qs.shape[1], d.ctypes.data, d.shape[1], M, K,
+                                     out.ctypes.data), "q8_unpack_q4_0_host")
+    return out
+
+
+def pack_q4_0(blocks: np.ndarray, device="cuda") -> PackedQ8:
+    """Repack GGUF Q4_0 blocks [M][K/32][18] and upload them (qs holds the
+    nibble plane)."""
+    import torch
+    qs, d = pack_q4_0_host(blocks)
+    M, K = blocks.shape[0], blocks.shape[1] * 32
+    return PackedQ8(torch.from_numpy(qs.view(np.int8)).to(device),
+                    torch.from_numpy(d.view(np.int16)).to(device), M, K)
+
+
 # ---------------------------------------------------------------- hot path
 def _dt(t) -> int:
     import torch
@@ -230,6 +279,18 @@ def gemv(W: PackedQ8, x, out=None, out_dtype=None, stream=None):
         out = torch.empty((N, W.M), dtype=out_dtype or torch.float32, device=x.device)
     _check(lib().q8_gemv(ctypes.byref(W.cmat()), x.data_ptr(), _dt(x), out.data_ptr(), _dt(out), N,
                          _stream(stream)), "q8_gemv")
+    return out
+
+
+def gemv_q4_0(W: PackedQ8, x, out=None, out_dtype=None, stream=None):
+    """Q4_0 GEMV (W from pack_q4_0): y [N][M] fp32 (or fp16)."""
+    import torch
+    x = _as_2d(x, W.K)
+    N = x.shape[0]
+    if out is None:
+        out = torch.empty((N, W.M), dtype=out_dtype or torch.float32, device=x.device)
+    _check(lib().q8_gemv_q4_0(ctypes.byref(W.cmat()), x.data_ptr(), _dt(x), out.data_ptr(),
+                              _dt(out), N, _stream(stream)), "q8_gemv_q4_0")
     return out
 
 

@@ -80,6 +80,16 @@ int check_bank(const q8_bank* B) {
   return Q8_OK;
 }
 
+int check_matrix_q4(const q8_matrix* W) {
+  if (!W || !W->qs || !W->d) return Q8_ERR_NULL;
+  if (W->M < 1 || W->M > INT32_MAX || W->K < 32 || W->K % 32 || W->K > (1LL << 24))
+    return Q8_ERR_SHAPE;
+  if (W->ld_qs < W->K / 2 || W->ld_d < W->K / 32) return Q8_ERR_SHAPE;
+  if (W->ld_qs % 16 || W->ld_d % 8 || !aligned(W->qs, 16) || !aligned(W->d, 16))
+    return Q8_ERR_ALIGN;
+  return Q8_OK;
+}
+
 HMat to_h(const q8_matrix* W) { return HMat{W->qs, W->d, W->M, W->K, W->ld_qs, W->ld_d}; }
 
 HBank to_hb(const q8_bank* B) {
@@ -169,6 +179,60 @@ int q8_unpack_host(const int8_t* qs, int64_t ld_qs, const uint16_t* d, int64_t l
   return Q8_OK;
 }
 
+// ------------------------------------------------------------ Q4_0 packing
+int q8_pack_q4_0_layout(int64_t M, int64_t K, int64_t* ld_qs, int64_t* ld_d, size_t* qs_bytes,
+                        size_t* d_bytes) {
+  if (M < 1 || K < 32 || K % 32) return Q8_ERR_SHAPE;
+  const int64_t lq = K / 2;
+  const int64_t ld = (K / 32 + 7) / 8 * 8;
+  if (ld_qs) *ld_qs = lq;
+  if (ld_d) *ld_d = ld;
+  if (qs_bytes) *qs_bytes = (size_t)M * (size_t)lq;
+  if (d_bytes) *d_bytes = (size_t)M * (size_t)ld * 2;
+  return Q8_OK;
+}
+
+int q8_pack_q4_0_host(const void* blocks, int64_t M, int64_t K, uint8_t* qs, int64_t ld_qs,
+                      uint16_t* d, int64_t ld_d) {
+  if (!blocks || !qs || !d) return Q8_ERR_NULL;
+  if (M < 1 || K < 32 || K % 32) return Q8_ERR_SHAPE;
+  if (ld_qs < K / 2 || ld_d < K / 32) return Q8_ERR_SHAPE;
+  if (ld_qs % 16 || ld_d % 8) return Q8_ERR_ALIGN;
+  const uint8_t* src = (const uint8_t*)blocks;
+  const int64_t nb = K / 32;
+  for (int64_t m = 0; m < M; ++m) {
+    uint8_t* qrow = qs + m * ld_qs;
+    uint16_t* drow = d + m * ld_d;
+    for (int64_t b = 0; b < nb; ++b) {
+      const uint8_t* blk = src + (m * nb + b) * 18;
+      drow[b] = (uint16_t)(blk[0] | ((uint16_t)blk[1] << 8));
+      memcpy(qrow + b * 16, blk + 2, 16);
+    }
+    if (ld_qs > K / 2) memset(qrow + K / 2, 0, (size_t)(ld_qs - K / 2));
+    for (int64_t b = nb; b < ld_d; ++b) drow[b] = 0;
+  }
+  return Q8_OK;
+}
+
+int q8_unpack_q4_0_host(const uint8_t* qs, int64_t ld_qs, const uint16_t* d, int64_t ld_d,
+                        int64_t M, int64_t K, void* blocks) {
+  if (!blocks || !qs || !d) return Q8_ERR_NULL;
+  if (M < 1 || K < 32 || K % 32) return Q8_ERR_SHAPE;
+  if (ld_qs < K / 2 || ld_d < K / 32) return Q8_ERR_SHAPE;
+  uint8_t* dst = (uint8_t*)blocks;
+  const int64_t nb = K / 32;
+  for (int64_t m = 0; m < M; ++m) {
+    for (int64_t b = 0; b < nb; ++b) {
+      uint8_t* blk = dst + (m * nb + b) * 18;
+      const uint16_t v = d[m * ld_d + b];
+      blk[0] = (uint8_t)(v & 0xff);
+      blk[1] = (uint8_t)(v >> 8);
+      memcpy(blk + 2, qs + m * ld_qs + b * 16, 16);
+    }
+  }
+  return Q8_OK;
+}
+
 // ------------------------------------------------------------ dense GEMV
 static int gemv_impl(const q8_matrix* Wa, const q8_matrix* Wb, const void* x, int x_dt, void* ya,
                      void* yb, int y_dt, int N, void* stream) {
@@ -246,6 +310,33 @@ int q8_gemv_pair_silu(const q8_matrix* Wg, const q8_matrix* Wu, const void* x, i
     hipError_t e = q8::launch_glu(*dev, G, U, (const char*)x + (size_t)n0 * Wg->K * xs, xf,
                                   (char*)h + (size_t)n0 * Wg->M * hs, h_dt == Q8_DT_F16, nt,
                                   (hipStream_t)stream);
+    if (e != hipSuccess) return Q8_ERR_LAUNCH;
+  }
+  return Q8_OK;
+}
+
+int q8_gemv_q4_0(const q8_matrix* W, const void* x, int x_dt, void* y, int y_dt, int N,
+                 void* stream) {
+  int rc = check_matrix_q4(W);
+  if (rc) return rc;
+  if (!x || !y) return Q8_ERR_NULL;
+  if (N < 1) return Q8_ERR_SHAPE;
+  const size_t xs = dt_size(x_dt), ys = dt_size(y_dt);
+  if (!xs || !ys) return Q8_ERR_DTYPE;
+  if (!aligned(x, 16) || !aligned(y, ys)) return Q8_ERR_ALIGN;
+  if (overlap(x, (size_t)N * W->K * xs, y, (size_t)N * W->M * ys)) return Q8_ERR_ALIAS;
+  const DevInfo* dev = nullptr;
+  rc = current_device(&dev);
+  if (rc) return rc;
+  const bool xf = x_dt == Q8_DT_F32;
+  const int per_pass = q8::max_tokens_per_pass(*dev, W->K, xf);
+  if (per_pass < 1) return Q8_ERR_SHAPE;
+  const HMat A = to_h(W);
+  for (int n0 = 0; n0 < N; n0 += per_pass) {
+    const int nt = N - n0 < per_pass ? N - n0 : per_pass;
+    hipError_t e = q8::launch_gemv_q4(*dev, A, (const char*)x + (size_t)n0 * W->K * xs, xf,
+                                      (char*)y + (size_t)n0 * W->M * ys, y_dt == Q8_DT_F16, nt,
+                                      (hipStream_t)stream);
     if (e != hipSuccess) return Q8_ERR_LAUNCH;
   }
   return Q8_OK;

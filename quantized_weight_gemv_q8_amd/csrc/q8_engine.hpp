@@ -139,10 +139,9 @@ struct XPlanes {
 // 19.3 -> 16.8 us). Inside a batch every load is unconditional (a dead
 // slot re-reads piece 0 of rows[0] and discards it), so no branch forces a
 // wait between the loads; lanes with nothing to copy skip the batch.
-template <int NT, bool XF32, int KB>
+template <int NT, int P, int KB>
 __device__ __forceinline__ void stage_batch(const char* const rows[NT], int C, uint4* lds, int nt,
                                             int per_tok, int k0) {
-  constexpr int P = XPlanes<XF32>::P;
   constexpr int TB = NT < 4 ? NT : 4;  // tokens per batch
   typedef unsigned int v4u __attribute__((ext_vector_type(4)));
   const int step = (int)blockDim.x;
@@ -175,10 +174,12 @@ __device__ __forceinline__ void stage_batch(const char* const rows[NT], int C, u
 }
 
 // KBMAX = 1 keeps the batch (and the kernel's register count) small for
-// kernels whose rows need at most one piece per thread and token.
-template <int NT, bool XF32, int KBMAX = 2>
-__device__ __forceinline__ void stage_x(const char* const rows[NT], int C, uint4* lds, int nt = NT) {
-  constexpr int P = XPlanes<XF32>::P;
+// kernels whose rows need at most one piece per thread and token. P is the
+// number of 16-byte pieces of x per chunk (stage_x picks it from the x
+// type for 16-quant chunks; other chunk widths call stage_planes).
+template <int NT, int P, int KBMAX = 2>
+__device__ __forceinline__ void stage_planes(const char* const rows[NT], int C, uint4* lds,
+                                             int nt = NT) {
   const int per_tok = C * P;
   if constexpr (NT == 1) {
     // One token: the plain loop measured as fast as batching (2.98 against
@@ -195,12 +196,17 @@ __device__ __forceinline__ void stage_x(const char* const rows[NT], int C, uint4
   // The first batch is outside any loop (the only one for K <= 8192 at
   // fp16), so nothing carried around a loop makes its loads wait.
   if (KBMAX == 1 || kc == 1) {
-    stage_batch<NT, XF32, 1>(rows, C, lds, nt, per_tok, 0);
-    for (int k0 = 1; k0 < kc; ++k0) stage_batch<NT, XF32, 1>(rows, C, lds, nt, per_tok, k0);
+    stage_batch<NT, P, 1>(rows, C, lds, nt, per_tok, 0);
+    for (int k0 = 1; k0 < kc; ++k0) stage_batch<NT, P, 1>(rows, C, lds, nt, per_tok, k0);
   } else {
-    stage_batch<NT, XF32, 2>(rows, C, lds, nt, per_tok, 0);
-    for (int k0 = 2; k0 < kc; k0 += 2) stage_batch<NT, XF32, 2>(rows, C, lds, nt, per_tok, k0);
+    stage_batch<NT, P, 2>(rows, C, lds, nt, per_tok, 0);
+    for (int k0 = 2; k0 < kc; k0 += 2) stage_batch<NT, P, 2>(rows, C, lds, nt, per_tok, k0);
   }
+}
+
+template <int NT, bool XF32, int KBMAX = 2>
+__device__ __forceinline__ void stage_x(const char* const rows[NT], int C, uint4* lds, int nt = NT) {
+  stage_planes<NT, XPlanes<XF32>::P, KBMAX>(rows, C, lds, nt);
 }
 
 // ---------------------------------------------------------------- team reduction

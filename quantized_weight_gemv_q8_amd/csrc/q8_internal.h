@@ -92,6 +92,10 @@ hipError_t launch_moe_gate_up(const DevInfo& dev, const HBank& G, const HBank& U
 // h[n][m] = silu(G x_n)[m] * (U x_n)[m]; G, U of one shape; h fp32 or fp16.
 hipError_t launch_glu(const DevInfo& dev, const HMat& G, const HMat& U, const void* x,
                       bool x_f32, void* h, bool h_f16, int nt, hipStream_t s);
+// Q4_0 GEMV: W.qs is the nibble plane (16-byte blocks, row stride ld_qs
+// bytes >= K/2), W.d the fp16 scales; y [nt][M] fp32 or fp16.
+hipError_t launch_gemv_q4(const DevInfo& dev, const HMat& W, const void* x, bool x_f32, void* y,
+                          bool y_f16, int nt, hipStream_t s);
 // Router: ids [T][topk] and softmax weights [T][topk] from logits [T][E].
 constexpr int kRouterMaxE = 4096;  // 64 experts per lane of the token's wave
 constexpr int kRouterMaxK = 64;    // one picked logit per lane

@@ -89,6 +89,33 @@ def gemv_rc(L, W=None, x=X, xdt=1, y=Y, ydt=2, N=1):
     return L.q8_gemv(ctypes.byref(W), x, xdt, y, ydt, N, None)
 
 
+@pytest.mark.parametrize("M,K", [(1, 32), (3, 96), (17, 1024), (5, 5120)])
+def test_q4_0_pack_roundtrip_and_layout(L, M, K):
+    rng = np.random.default_rng(M + K)
+    q, d = synth.draw_weights_q4_0(rng, M, K)
+    blocks = synth.to_gguf_q4_0_blocks(q, d)
+    ld_qs, ld_d, qb, db = q8.pack_q4_0_layout(M, K)
+    assert ld_qs == K // 2 and ld_qs % 16 == 0 and ld_d % 8 == 0 and ld_d >= K // 32
+    qs, dd = q8.pack_q4_0_host(blocks)
+    assert qs.shape == (M, ld_qs) and dd.shape == (M, ld_d)
+    # the nibble plane holds each block's 16 data bytes in GGUF order
+    assert np.array_equal(qs[:, :K // 2].reshape(M, K // 32, 16), blocks[:, :, 2:])
+    assert np.all(dd[:, K // 32:] == 0)
+    assert np.array_equal(q8.unpack_q4_0_host(qs, dd, M, K), blocks)
+
+
+def test_q4_0_validation(L):
+    W = _mat(K=256, ld_qs=128)
+    assert L.q8_gemv_q4_0(ctypes.byref(W), X, 1, Y, 2, 1, None) in (0, -6)  # valid shape
+    assert L.q8_gemv_q4_0(ctypes.byref(_mat(K=256, ld_qs=112)), X, 1, Y, 2, 1, None) == -2
+    assert L.q8_gemv_q4_0(ctypes.byref(_mat(K=256, ld_qs=136)), X, 1, Y, 2, 1, None) == -3
+    assert L.q8_gemv_q4_0(ctypes.byref(W), 0, 1, Y, 2, 1, None) == -1
+    assert L.q8_gemv_q4_0(ctypes.byref(W), X, 1, Y, 2, 0, None) == -2
+    assert L.q8_gemv_q4_0(ctypes.byref(W), X, 9, Y, 2, 1, None) == -4
+    assert L.q8_gemv_q4_0(ctypes.byref(W), X, 1, X + 64, 2, 1, None) == -8
+    assert L.q8_pack_q4_0_layout(4, 48, None, None, None, None) == -2
+
+
 def test_gemv_validation(L):
     assert L.q8_gemv(None, X, 1, Y, 2, 1, None) == -1
     assert gemv_rc(L, W=_mat(qs=0)) == -1
