@@ -209,6 +209,37 @@ __device__ __forceinline__ void stage_x(const char* const rows[NT], int C, uint4
   stage_planes<NT, XPlanes<XF32>::P, KBMAX>(rows, C, lds, nt);
 }
 
+// ---------------------------------------------------------------- wave maximum
+// Maximum of a 64-bit key over the 64 lanes, returned in every lane. DPP
+// moves inside each 16-lane row (quad permutes [1,0,3,2] and [2,3,0,1],
+// then the half-row and row mirrors) leave every lane with its row's
+// maximum; the four row maxima are read with readlane and combined in
+// scalar registers. Exact (moves and integer compares only) and about a
+// tenth of the latency of a shuffle butterfly through the LDS crossbar.
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+  const uint32_t lo = __builtin_amdgcn_update_dpp(0u, (uint32_t)v, CTRL, 0xF, 0xF, false);
+  const uint32_t hi = __builtin_amdgcn_update_dpp(0u, (uint32_t)(v >> 32), CTRL, 0xF, 0xF, false);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t k) {
+  k = umax64(k, dpp_u64<0xB1>(k));   // quad_perm [1,0,3,2]
+  k = umax64(k, dpp_u64<0x4E>(k));   // quad_perm [2,3,0,1]
+  k = umax64(k, dpp_u64<0x141>(k));  // row_half_mirror
+  k = umax64(k, dpp_u64<0x140>(k));  // row_mirror
+  uint64_t m = 0;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)k, 16 * r);
+    const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(k >> 32), 16 * r);
+    m = umax64(m, ((uint64_t)hi << 32) | lo);
+  }
+  return m;
+}
+
 // ---------------------------------------------------------------- team reduction
 // Butterfly over the LPR lanes of a team, xor distances LPR/2, LPR/4, ..., 1.
 // While a lane carries more than MINC values, each level halves them
@@ -281,6 +312,17 @@ struct Tune {
   static constexpr int D = 1;
 };
 constexpr int64_t kBigRows = 65536;
+
+// Shape modes of the dense GEMV: 0 as Tune<NT, false>, 1 as Tune<NT, true>
+// (>= 64K rows at N = 1), 2 for matrices too small to give every CU a row
+// group (a router, a small projection): one row per team and two chunk
+// loads in flight, so the few waves there are each issue their whole row
+// at once. R and D never change the arithmetic of a (row, token).
+template <int NT, int MODE>
+struct TuneM {
+  static constexpr int R = MODE == 2 ? 1 : Tune<NT, MODE == 1>::R;
+  static constexpr int D = MODE == 2 ? 2 : Tune<NT, MODE == 1>::D;
+};
 
 // ---------------------------------------------------------------- row sources
 struct MatDesc {

@@ -61,11 +61,11 @@ struct DenseEpi {
   }
 };
 
-template <int NT, int LPR, bool XF32, bool BIG>
+template <int NT, int LPR, bool XF32, int MODE>
 __global__ __launch_bounds__(kBlock) void gemv_kernel(DenseMap map, DenseEpi epi, const char* x,
                                                       int64_t ldx_bytes, int C) {
   extern __shared__ uint4 lds_x[];
-  using T = Tune<NT, BIG>;
+  using T = TuneM<NT, MODE>;
   constexpr int G = (kWave / LPR) * T::R;
   const int64_t n_groups = (map.Mtot + G - 1) / G;
   const int wave = threadIdx.x / kWave;
@@ -218,14 +218,14 @@ hipError_t launch_glu(const DevInfo& dev, const HMat& Gm, const HMat& Um, const 
   return glu_launch_nt<16, false>(dev, nt, map, epi, xp, ldx_bytes, C, s);
 }
 
-template <int NT, int LPR, bool XF32, bool BIG>
+template <int NT, int LPR, bool XF32, int MODE>
 static hipError_t launch_t(const DevInfo& dev, DenseMap map, DenseEpi epi, const char* x,
                            int64_t ldx_bytes, int C, hipStream_t s) {
-  constexpr int G = (kWave / LPR) * Tune<NT, BIG>::R;
+  constexpr int G = (kWave / LPR) * TuneM<NT, MODE>::R;
   const size_t lds = (size_t)NT * C * 16 * XPlanes<XF32>::P;
   const int64_t n_groups = (map.Mtot + G - 1) / G;
   const int64_t need = (n_groups + kWavesPerBlock - 1) / kWavesPerBlock;
-  auto fn = gemv_kernel<NT, LPR, XF32, BIG>;
+  auto fn = gemv_kernel<NT, LPR, XF32, MODE>;
   if (lds > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize,
                                        (int)lds);
@@ -241,8 +241,12 @@ static hipError_t launch_t(const DevInfo& dev, DenseMap map, DenseEpi epi, const
 template <int NT, int LPR, bool XF32>
 static hipError_t launch_sz(const DevInfo& dev, DenseMap map, DenseEpi epi, const char* x,
                             int64_t ldx_bytes, int C, hipStream_t s) {
-  if (map.Mtot >= kBigRows) return launch_t<NT, LPR, XF32, true>(dev, map, epi, x, ldx_bytes, C, s);
-  return launch_t<NT, LPR, XF32, false>(dev, map, epi, x, ldx_bytes, C, s);
+  if (NT == 1 && map.Mtot >= kBigRows)
+    return launch_t<NT, LPR, XF32, 1>(dev, map, epi, x, ldx_bytes, C, s);
+  constexpr int G0 = (kWave / LPR) * TuneM<NT, 0>::R;
+  if ((map.Mtot + G0 - 1) / G0 < dev.cus)  // fewer row groups than CUs
+    return launch_t<NT, LPR, XF32, 2>(dev, map, epi, x, ldx_bytes, C, s);
+  return launch_t<NT, LPR, XF32, 0>(dev, map, epi, x, ldx_bytes, C, s);
 }
 
 template <int LPR, bool XF32>
@@ -250,13 +254,13 @@ static hipError_t launch_nt(const DevInfo& dev, int nt, DenseMap map, DenseEpi e
                             int64_t ldx_bytes, int C, hipStream_t s) {
   switch (nt) {
     case 1: return launch_sz<1, LPR, XF32>(dev, map, epi, x, ldx_bytes, C, s);
-    case 2: return launch_t<2, LPR, XF32, false>(dev, map, epi, x, ldx_bytes, C, s);
-    case 3: return launch_t<3, LPR, XF32, false>(dev, map, epi, x, ldx_bytes, C, s);
-    case 4: return launch_t<4, LPR, XF32, false>(dev, map, epi, x, ldx_bytes, C, s);
-    case 5: return launch_t<5, LPR, XF32, false>(dev, map, epi, x, ldx_bytes, C, s);
-    case 6: return launch_t<6, LPR, XF32, false>(dev, map, epi, x, ldx_bytes, C, s);
-    case 7: return launch_t<7, LPR, XF32, false>(dev, map, epi, x, ldx_bytes, C, s);
-    case 8: return launch_t<8, LPR, XF32, false>(dev, map, epi, x, ldx_bytes, C, s);
+    case 2: return launch_sz<2, LPR, XF32>(dev, map, epi, x, ldx_bytes, C, s);
+    case 3: return launch_sz<3, LPR, XF32>(dev, map, epi, x, ldx_bytes, C, s);
+    case 4: return launch_sz<4, LPR, XF32>(dev, map, epi, x, ldx_bytes, C, s);
+    case 5: return launch_sz<5, LPR, XF32>(dev, map, epi, x, ldx_bytes, C, s);
+    case 6: return launch_sz<6, LPR, XF32>(dev, map, epi, x, ldx_bytes, C, s);
+    case 7: return launch_sz<7, LPR, XF32>(dev, map, epi, x, ldx_bytes, C, s);
+    case 8: return launch_sz<8, LPR, XF32>(dev, map, epi, x, ldx_bytes, C, s);
   }
   return hipErrorInvalidValue;
 }

@@ -32,15 +32,6 @@ __device__ __forceinline__ uint64_t argmax_key(float v, int64_t row) {
   return ((uint64_t)ord << 32) | (uint64_t)(~(uint32_t)row);
 }
 
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t k) {
-#pragma unroll
-  for (int off = kWave / 2; off > 0; off >>= 1) {
-    const uint64_t o = __shfl_xor(k, off, kWave);
-    k = o > k ? o : k;
-  }
-  return k;
-}
-
 struct LmMap {
   MatDesc w;
   int64_t V;

@@ -14,7 +14,8 @@
 // logit and, among equal logits, the lowest expert. Each lane keeps the
 // best key of its own experts (expert e belongs to lane e % 64); a pick is
 // a wave maximum, after which only the owner of the picked expert rescans
-// its (at most 64) experts.
+// its (at most 64) experts. The wave maximum runs on DPP moves and
+// readlanes (wave_max_u64), not on shuffles through the LDS crossbar.
 #include "q8_engine.hpp"
 #include "q8_internal.h"
 
@@ -51,12 +52,7 @@ __global__ __launch_bounds__(kWave) void topk_softmax_kernel(const float* logits
   uint64_t taken = 0;  // bit i: this lane's expert lane + 64 i has been picked
   float mine = 0.0f;   // lane j holds the j-th picked logit
   for (int j = 0; j < topk; ++j) {
-    uint64_t m = best;
-#pragma unroll
-    for (int off = kWave / 2; off > 0; off >>= 1) {
-      const uint64_t o = __shfl_xor(m, off, kWave);
-      m = o > m ? o : m;
-    }
+    const uint64_t m = wave_max_u64(best);
     const int e = (int)(~(uint32_t)m);
     if (lane == j) mine = router_value((uint32_t)(m >> 32));
     if (lane == 0) ids[(int64_t)t * topk + j] = e;
