@@ -240,12 +240,37 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t k) {
   return m;
 }
 
+// ---------------------------------------------------------------- lane exchange
+// The value of lane (lane ^ DELTA), without the LDS crossbar where the
+// hardware has a direct path: DPP quad permutes for 1 and 2, ds_swizzle in
+// xor mode for 4, 8 and 16 (within 32 lanes), and the gfx950 permlane32
+// swap for 32 (each half of the wave reads the other half). Every lane of
+// the wave must be active.
+template <int DELTA>
+__device__ __forceinline__ float xor_lane(float v) {
+  const unsigned u = __builtin_bit_cast(unsigned, v);
+  unsigned r;
+  if constexpr (DELTA == 1) {
+    r = __builtin_amdgcn_update_dpp(0u, u, 0xB1, 0xF, 0xF, false);  // quad_perm [1,0,3,2]
+  } else if constexpr (DELTA == 2) {
+    r = __builtin_amdgcn_update_dpp(0u, u, 0x4E, 0xF, 0xF, false);  // quad_perm [2,3,0,1]
+  } else if constexpr (DELTA == 4 || DELTA == 8 || DELTA == 16) {
+    r = (unsigned)__builtin_amdgcn_ds_swizzle((int)u, 0x1F | (DELTA << 10));
+  } else {
+    static_assert(DELTA == 32, "xor distance within a wave");
+    const auto sw = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    r = (threadIdx.x & 32) ? sw[0] : sw[1];
+  }
+  return __builtin_bit_cast(float, r);
+}
+
 // ---------------------------------------------------------------- team reduction
 // Butterfly over the LPR lanes of a team, xor distances LPR/2, LPR/4, ..., 1.
 // While a lane carries more than MINC values, each level halves them
 // (the lane keeps the half selected by its distance bit and receives the
 // partner's copy of that half), so R*NT sums cost about R*NT shuffles
-// instead of log2(LPR) each. Every value is summed over the same pairing
+// instead of log2(LPR) each (the exchanges use xor_lane). Every value is
+// summed over the same pairing
 // tree (partners differing in bit LPR/2, then LPR/4, ...), whatever the
 // number of values carried, so the result of each (row, token) does not
 // depend on R or NT. fp32 addition is commutative, so the side a value
@@ -263,7 +288,7 @@ struct TeamReduce {
       for (int i = 0; i < H; ++i) {
         const float send = hi ? v[i] : v[i + H];
         const float keep = hi ? v[i + H] : v[i];
-        nv[i] = keep + __shfl_xor(send, DELTA, kWave);
+        nv[i] = keep + xor_lane<DELTA>(send);
       }
 #pragma unroll
       for (int i = 0; i < H; ++i) v[i] = nv[i];
@@ -271,7 +296,7 @@ struct TeamReduce {
       TeamReduce<H, MINC, DELTA / 2>::run(v, p, base);
     } else {
 #pragma unroll
-      for (int i = 0; i < CNT; ++i) v[i] = v[i] + __shfl_xor(v[i], DELTA, kWave);
+      for (int i = 0; i < CNT; ++i) v[i] = v[i] + xor_lane<DELTA>(v[i]);
       TeamReduce<CNT, MINC, DELTA / 2>::run(v, p, base);
     }
   }

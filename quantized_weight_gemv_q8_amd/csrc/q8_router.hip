@@ -69,11 +69,16 @@ __global__ __launch_bounds__(kWave) void topk_softmax_kernel(const float* logits
   // Softmax over the picked logits; the first pick is the largest. The
   // butterfly gives every lane the same sum (each level adds the same two
   // numbers on both partners).
-  const float top = __shfl(mine, 0, kWave);
+  const float top = __builtin_bit_cast(
+      float, __builtin_amdgcn_readlane(__builtin_bit_cast(unsigned, mine), 0));
   const float z = lane < topk ? expf(mine - top) : 0.0f;
   float s = z;
-#pragma unroll
-  for (int off = kWave / 2; off > 0; off >>= 1) s += __shfl_xor(s, off, kWave);
+  s += xor_lane<32>(s);
+  s += xor_lane<16>(s);
+  s += xor_lane<8>(s);
+  s += xor_lane<4>(s);
+  s += xor_lane<2>(s);
+  s += xor_lane<1>(s);
   if (lane < topk) gate_w[(int64_t)t * topk + lane] = z / s;
 }
 
