@@ -66,15 +66,24 @@ typedef enum {
 
 typedef enum { Q8_DT_F16 = 1, Q8_DT_F32 = 2 } q8_dtype;
 
-/* One packed Q8_0 matrix [M][K], rows = outputs, blocks along K, in the
- * split-plane layout written by q8_pack_host: a quant plane and a scale
- * plane, every row starting on a 16-byte boundary.
- *   qs   [dev] int8 [M][ld_qs]: row m holds q[m][0..K-1] in K order.
- *   d    [dev] fp16 bit patterns [M][ld_d]: row m holds the K/32 scales.
- *   K % 32 == 0, M >= 1, ld_qs >= K and ld_qs % 16 == 0,
- *   ld_d >= K/32 and ld_d % 8 == 0, qs and d 16-byte aligned.
- * Any layout with these strides is accepted; e.g. one interleaved buffer
- * per row ([K quants][K/32 scales]) is qs = base, d = base + K,
+/* Weight formats of a packed matrix (q8_matrix.format). */
+typedef enum { Q8_FMT_Q8_0 = 0, Q8_FMT_Q4_0 = 1 } q8_format;
+
+/* One packed matrix [M][K], rows = outputs, blocks of 32 weights along K,
+ * in the split-plane layout written by the packers: a quant plane and a
+ * scale plane, every row starting on a 16-byte boundary.
+ *   format Q8_FMT_Q8_0 (q8_pack_host): qs [dev] int8 [M][ld_qs], row m
+ *     holds q[m][0..K-1] in K order; ld_qs >= K.
+ *   format Q8_FMT_Q4_0 (q8_pack_q4_0_host): qs [dev] bytes [M][ld_qs], row
+ *     m holds the 16 data bytes of each GGUF Q4_0 block in K order;
+ *     ld_qs >= K/2.
+ *   d [dev] fp16 bit patterns [M][ld_d]: row m holds the K/32 scales.
+ *   K % 32 == 0, M >= 1, ld_qs % 16 == 0, ld_d >= K/32 and ld_d % 8 == 0,
+ *   qs and d 16-byte aligned. A zero-initialised struct is Q8_0.
+ * Every entry point below accepts either format (matrices combined in one
+ * call, e.g. a pair, must share it); another format value is Q8_ERR_DTYPE.
+ * Any layout with these strides is accepted; e.g. one interleaved Q8_0
+ * buffer per row ([K quants][K/32 scales]) is qs = base, d = base + K,
  * ld_qs = K + K/16 bytes, ld_d = ld_qs / 2, valid when K % 256 == 0. */
 typedef struct q8_matrix {
     const int8_t *qs;
@@ -82,6 +91,7 @@ typedef struct q8_matrix {
     int64_t M, K;
     int64_t ld_qs; /* bytes */
     int64_t ld_d;  /* fp16 elements */
+    int32_t format; /* q8_format */
 } q8_matrix;
 
 /* E experts of identical shape: expert e's matrix is e0 with
@@ -164,17 +174,15 @@ int q8_gemv_pair_silu(const q8_matrix *Wg, const q8_matrix *Wu, const void *x, i
  * q8_pack_q4_0_layout / q8_pack_q4_0_host / q8_unpack_q4_0_host: as the
  * Q8_0 packer (ld_qs = K/2, ld_d = K/32 rounded up to 8, padding zeroed,
  * byte-exact round trip), for blocks [host] of 18 bytes.
- * q8_gemv_q4_0: y[n][m] = sum_k d[m][k/32] * q[m][k] * x[n][k], with the
- * same arguments, dtypes, pass structure, N-invariance and errors as
- * q8_gemv. */
+ * A Q4_0 matrix (format = Q8_FMT_Q4_0) runs through every entry point
+ * (q8_gemv, pairs, LM heads, routed experts, router) with the same
+ * arguments, pass structure, N-invariance and errors as Q8_0. */
 int q8_pack_q4_0_layout(int64_t M, int64_t K, int64_t *ld_qs, int64_t *ld_d, size_t *qs_bytes,
                         size_t *d_bytes);
 int q8_pack_q4_0_host(const void *blocks, int64_t M, int64_t K, uint8_t *qs, int64_t ld_qs,
                       uint16_t *d, int64_t ld_d);
 int q8_unpack_q4_0_host(const uint8_t *qs, int64_t ld_qs, const uint16_t *d, int64_t ld_d,
                         int64_t M, int64_t K, void *blocks);
-int q8_gemv_q4_0(const q8_matrix *W, const void *x, int x_dt, void *y, int y_dt, int N,
-                 void *stream);
 
 /* ------------------------------------------------------------ LM head
  * logits[n][v] = W x_n (as q8_gemv with fp32 output) and

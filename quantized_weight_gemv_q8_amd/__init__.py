@@ -29,7 +29,7 @@ Q8_DT_F32 = 2
 # every function the header declares
 EXPORTS = (
     "q8_status_str", "q8_device_check", "q8_pack_layout", "q8_pack_host", "q8_unpack_host",
-    "q8_pack_q4_0_layout", "q8_pack_q4_0_host", "q8_unpack_q4_0_host", "q8_gemv_q4_0",
+    "q8_pack_q4_0_layout", "q8_pack_q4_0_host", "q8_unpack_q4_0_host",
     "q8_gemv", "q8_gemv_pair", "q8_gemv_pair_silu", "q8_lmhead_ws_bytes", "q8_lmhead_argmax",
     "q8_lmhead_argmax_rows",
     "q8_moe_ws_bytes", "q8_moe_ws_layout", "q8_moe_gemv", "q8_moe_ffn", "q8_moe_topk_softmax",
@@ -43,9 +43,14 @@ class Q8Error(RuntimeError):
         super().__init__(f"{where}: {status_str(status)} (status {status})")
 
 
+Q8_FMT_Q8_0 = 0
+Q8_FMT_Q4_0 = 1
+
+
 class _Matrix(ctypes.Structure):
     _fields_ = [("qs", ctypes.c_void_p), ("d", ctypes.c_void_p), ("M", ctypes.c_int64),
-                ("K", ctypes.c_int64), ("ld_qs", ctypes.c_int64), ("ld_d", ctypes.c_int64)]
+                ("K", ctypes.c_int64), ("ld_qs", ctypes.c_int64), ("ld_d", ctypes.c_int64),
+                ("format", ctypes.c_int32)]
 
 
 class _Bank(ctypes.Structure):
@@ -75,7 +80,6 @@ def lib() -> ctypes.CDLL:
             "q8_pack_q4_0_layout": ([i64, i64, vp, vp, vp, vp], i32),
             "q8_pack_q4_0_host": ([vp, i64, i64, vp, i64, vp, i64], i32),
             "q8_unpack_q4_0_host": ([vp, i64, vp, i64, i64, i64, vp], i32),
-            "q8_gemv_q4_0": ([pm, vp, i32, vp, i32, i32, vp], i32),
             "q8_gemv": ([pm, vp, i32, vp, i32, i32, vp], i32),
             "q8_gemv_pair": ([pm, pm, vp, i32, vp, vp, i32, i32, vp], i32),
             "q8_gemv_pair_silu": ([pm, pm, vp, i32, vp, i32, i32, vp], i32),
@@ -145,15 +149,17 @@ def unpack_host(qs: np.ndarray, d: np.ndarray, M: int, K: int) -> np.ndarray:
 
 @dataclasses.dataclass
 class PackedQ8:
-    """One packed Q8_0 matrix on the device (split planes, 16-byte rows)."""
+    """One packed matrix on the device (split planes, 16-byte rows): Q8_0
+    by default, or Q4_0 (fmt = Q8_FMT_Q4_0, qs holding the nibble plane)."""
     qs: "torch.Tensor"  # int8 [M][ld_qs]
     d: "torch.Tensor"   # int16 (fp16 bit patterns) [M][ld_d]
     M: int
     K: int
+    fmt: int = Q8_FMT_Q8_0
 
     def cmat(self) -> _Matrix:
         return _Matrix(self.qs.data_ptr(), self.d.data_ptr(), self.M, self.K,
-                       self.qs.stride(0), self.d.stride(0))
+                       self.qs.stride(0), self.d.stride(0), self.fmt)
 
     @property
     def nbytes(self) -> int:
@@ -162,20 +168,21 @@ class PackedQ8:
 
 @dataclasses.dataclass
 class PackedBank:
-    """E packed Q8_0 matrices of one shape: qs [E][M][ld_qs], d [E][M][ld_d]."""
+    """E packed matrices of one shape and format: qs [E][M][ld_qs], d [E][M][ld_d]."""
     qs: "torch.Tensor"
     d: "torch.Tensor"
     M: int
     K: int
     E: int
+    fmt: int = Q8_FMT_Q8_0
 
     def cbank(self) -> _Bank:
         e0 = _Matrix(self.qs.data_ptr(), self.d.data_ptr(), self.M, self.K,
-                     self.qs.stride(1), self.d.stride(1))
+                     self.qs.stride(1), self.d.stride(1), self.fmt)
         return _Bank(e0, self.qs.stride(0), self.d.stride(0), self.E)
 
     def expert(self, e: int) -> PackedQ8:
-        return PackedQ8(self.qs[e], self.d[e], self.M, self.K)
+        return PackedQ8(self.qs[e], self.d[e], self.M, self.K, self.fmt)
 
 
 def pack(blocks: np.ndarray, device="cuda") -> PackedQ8:
@@ -243,7 +250,18 @@ def pack_q4_0(blocks: np.ndarray, device="cuda") -> PackedQ8:
     qs, d = pack_q4_0_host(blocks)
     M, K = blocks.shape[0], blocks.shape[1] * 32
     return PackedQ8(torch.from_numpy(qs.view(np.int8)).to(device),
-                    torch.from_numpy(d.view(np.int16)).to(device), M, K)
+                    torch.from_numpy(d.view(np.int16)).to(device), M, K, Q8_FMT_Q4_0)
+
+
+def pack_bank_q4_0(blocks: np.ndarray, device="cuda") -> PackedBank:
+    """Q4_0 blocks uint8 [E][M][K/32][18] -> one device bank."""
+    import torch
+    E, M, nb, _ = blocks.shape
+    planes = [pack_q4_0_host(blocks[e]) for e in range(E)]
+    qs = np.stack([p[0] for p in planes]).view(np.int8)
+    d = np.stack([p[1] for p in planes]).view(np.int16)
+    return PackedBank(torch.from_numpy(qs).to(device), torch.from_numpy(d).to(device), M, nb * 32,
+                      E, Q8_FMT_Q4_0)
 
 
 # ---------------------------------------------------------------- hot path
@@ -279,18 +297,6 @@ def gemv(W: PackedQ8, x, out=None, out_dtype=None, stream=None):
         out = torch.empty((N, W.M), dtype=out_dtype or torch.float32, device=x.device)
     _check(lib().q8_gemv(ctypes.byref(W.cmat()), x.data_ptr(), _dt(x), out.data_ptr(), _dt(out), N,
                          _stream(stream)), "q8_gemv")
-    return out
-
-
-def gemv_q4_0(W: PackedQ8, x, out=None, out_dtype=None, stream=None):
-    """Q4_0 GEMV (W from pack_q4_0): y [N][M] fp32 (or fp16)."""
-    import torch
-    x = _as_2d(x, W.K)
-    N = x.shape[0]
-    if out is None:
-        out = torch.empty((N, W.M), dtype=out_dtype or torch.float32, device=x.device)
-    _check(lib().q8_gemv_q4_0(ctypes.byref(W.cmat()), x.data_ptr(), _dt(x), out.data_ptr(),
-                              _dt(out), N, _stream(stream)), "q8_gemv_q4_0")
     return out
 
 

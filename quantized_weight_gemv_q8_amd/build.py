@@ -20,8 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libq8gemv.so")
 
-SOURCES = ["q8_api.cpp", "q8_gemv.hip", "q8_lmhead.hip", "q8_moe.hip", "q8_router.hip",
-           "q8_q4.hip"]
+SOURCES = ["q8_api.cpp", "q8_gemv.hip", "q8_lmhead.hip", "q8_moe.hip", "q8_router.hip"]
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 COMMON = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-function",
           "-I", INCLUDE, "-I", CSRC]

@@ -61,9 +61,11 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
 
 int check_matrix(const q8_matrix* W) {
   if (!W || !W->qs || !W->d) return Q8_ERR_NULL;
+  if (W->format != Q8_FMT_Q8_0 && W->format != Q8_FMT_Q4_0) return Q8_ERR_DTYPE;
   if (W->M < 1 || W->M > INT32_MAX || W->K < 32 || W->K % 32 || W->K > (1LL << 24))
     return Q8_ERR_SHAPE;
-  if (W->ld_qs < W->K || W->ld_d < W->K / 32) return Q8_ERR_SHAPE;
+  const int64_t row_bytes = W->format == Q8_FMT_Q4_0 ? W->K / 2 : W->K;
+  if (W->ld_qs < row_bytes || W->ld_d < W->K / 32) return Q8_ERR_SHAPE;
   if (W->ld_qs % 16 || W->ld_d % 8 || !aligned(W->qs, 16) || !aligned(W->d, 16))
     return Q8_ERR_ALIGN;
   return Q8_OK;
@@ -80,17 +82,10 @@ int check_bank(const q8_bank* B) {
   return Q8_OK;
 }
 
-int check_matrix_q4(const q8_matrix* W) {
-  if (!W || !W->qs || !W->d) return Q8_ERR_NULL;
-  if (W->M < 1 || W->M > INT32_MAX || W->K < 32 || W->K % 32 || W->K > (1LL << 24))
-    return Q8_ERR_SHAPE;
-  if (W->ld_qs < W->K / 2 || W->ld_d < W->K / 32) return Q8_ERR_SHAPE;
-  if (W->ld_qs % 16 || W->ld_d % 8 || !aligned(W->qs, 16) || !aligned(W->d, 16))
-    return Q8_ERR_ALIGN;
-  return Q8_OK;
+HMat to_h(const q8_matrix* W) {
+  return HMat{W->qs, W->d, W->M, W->K, W->ld_qs, W->ld_d,
+              W->format == Q8_FMT_Q4_0 ? q8::kFmtQ4 : q8::kFmtQ8};
 }
-
-HMat to_h(const q8_matrix* W) { return HMat{W->qs, W->d, W->M, W->K, W->ld_qs, W->ld_d}; }
 
 HBank to_hb(const q8_bank* B) {
   return HBank{to_h(&B->e0), B->stride_qs, B->stride_d, (int)B->E};
@@ -242,6 +237,7 @@ static int gemv_impl(const q8_matrix* Wa, const q8_matrix* Wb, const void* x, in
     rc = check_matrix(Wb);
     if (rc) return rc;
     if (Wb->K != Wa->K) return Q8_ERR_SHAPE;
+    if (Wb->format != Wa->format) return Q8_ERR_DTYPE;
   }
   if (!x || !ya || (Wb && !yb)) return Q8_ERR_NULL;
   if (N < 1) return Q8_ERR_SHAPE;
@@ -292,6 +288,7 @@ int q8_gemv_pair_silu(const q8_matrix* Wg, const q8_matrix* Wu, const void* x, i
   if (rc) return rc;
   if ((rc = check_matrix(Wu))) return rc;
   if (Wu->M != Wg->M || Wu->K != Wg->K) return Q8_ERR_SHAPE;
+  if (Wu->format != Wg->format) return Q8_ERR_DTYPE;
   if (!x || !h) return Q8_ERR_NULL;
   if (N < 1) return Q8_ERR_SHAPE;
   const size_t xs = dt_size(x_dt), hs = dt_size(h_dt);
@@ -310,33 +307,6 @@ int q8_gemv_pair_silu(const q8_matrix* Wg, const q8_matrix* Wu, const void* x, i
     hipError_t e = q8::launch_glu(*dev, G, U, (const char*)x + (size_t)n0 * Wg->K * xs, xf,
                                   (char*)h + (size_t)n0 * Wg->M * hs, h_dt == Q8_DT_F16, nt,
                                   (hipStream_t)stream);
-    if (e != hipSuccess) return Q8_ERR_LAUNCH;
-  }
-  return Q8_OK;
-}
-
-int q8_gemv_q4_0(const q8_matrix* W, const void* x, int x_dt, void* y, int y_dt, int N,
-                 void* stream) {
-  int rc = check_matrix_q4(W);
-  if (rc) return rc;
-  if (!x || !y) return Q8_ERR_NULL;
-  if (N < 1) return Q8_ERR_SHAPE;
-  const size_t xs = dt_size(x_dt), ys = dt_size(y_dt);
-  if (!xs || !ys) return Q8_ERR_DTYPE;
-  if (!aligned(x, 16) || !aligned(y, ys)) return Q8_ERR_ALIGN;
-  if (overlap(x, (size_t)N * W->K * xs, y, (size_t)N * W->M * ys)) return Q8_ERR_ALIAS;
-  const DevInfo* dev = nullptr;
-  rc = current_device(&dev);
-  if (rc) return rc;
-  const bool xf = x_dt == Q8_DT_F32;
-  const int per_pass = q8::max_tokens_per_pass(*dev, W->K, xf);
-  if (per_pass < 1) return Q8_ERR_SHAPE;
-  const HMat A = to_h(W);
-  for (int n0 = 0; n0 < N; n0 += per_pass) {
-    const int nt = N - n0 < per_pass ? N - n0 : per_pass;
-    hipError_t e = q8::launch_gemv_q4(*dev, A, (const char*)x + (size_t)n0 * W->K * xs, xf,
-                                      (char*)y + (size_t)n0 * W->M * ys, y_dt == Q8_DT_F16, nt,
-                                      (hipStream_t)stream);
     if (e != hipSuccess) return Q8_ERR_LAUNCH;
   }
   return Q8_OK;
@@ -495,6 +465,7 @@ int q8_moe_ffn(const q8_bank* gate, const q8_bank* up, const q8_bank* down,
   if (up->E != E || down->E != E || E > 4096) return Q8_ERR_SHAPE;
   const int64_t F = gate->e0.M, H = gate->e0.K;
   if (up->e0.M != F || up->e0.K != H || down->e0.M != H || down->e0.K != F) return Q8_ERR_SHAPE;
+  if (up->e0.format != gate->e0.format) return Q8_ERR_DTYPE;
   rc = check_routing(expert_ids, gate_w, T, topk, E, true);
   if (rc) return rc;
   if ((int64_t)q8::moe_max_vslots(E, T * topk) * (2 * F > H ? 2 * F : H) > INT32_MAX)

@@ -34,6 +34,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "q8_format.h"
+
 namespace q8 {
 
 typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
@@ -122,6 +124,160 @@ __device__ __forceinline__ uint4 load_stream16(const int8_t* p) {
   return make_uint4(t.x, t.y, t.z, t.w);
 }
 
+// ---------------------------------------------------------------- weight formats
+// A packed row is a sequence of 16-byte chunks. Q8_0: 16 int8 quants per
+// chunk, one fp16 scale per 32-quant block (two chunks). Q4_0: one whole
+// GGUF block per chunk (16 bytes of 4-bit values stored with +8: the low
+// nibble of byte j is element j, the high nibble element j + 16) with its
+// own scale. The format decides only the per-chunk dequantisation and the
+// scale index; loads, staging, reduction and epilogues are shared.
+template <int F>
+struct Fmt;
+template <>
+struct Fmt<kFmtQ8> {
+  static constexpr int kElems = 16;      // weights per 16-byte chunk
+  static constexpr int kScaleShift = 1;  // scale index = chunk >> shift
+};
+template <>
+struct Fmt<kFmtQ4> {
+  static constexpr int kElems = 32;
+  static constexpr int kScaleShift = 0;
+};
+
+// 16-byte pieces of x per chunk in the LDS image.
+template <int F, bool XF32>
+struct ChunkPlanes {
+  static constexpr int P = Fmt<F>::kElems * (XF32 ? 4 : 2) / 16;
+};
+
+// One Q4_0 block (16 bytes) -> 16 fp16 pairs in element order: pairs 0..7
+// from the low nibbles (elements 0..15), 8..15 from the high nibbles. Each
+// nibble u = q + 8 is placed under an exponent byte of 0x64 (the fp16 value
+// 1024 + u) and 1032 is subtracted: exact, as for the int8 quants.
+__device__ __forceinline__ void nibbles_to_h2(const uint4 q, h2_t out[16]) {
+  const unsigned w[4] = {q.x, q.y, q.z, q.w};
+  const h2_t bias = {(_Float16)1032.0f, (_Float16)1032.0f};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const unsigned lo = w[i] & 0x0F0F0F0Fu;
+    const unsigned hi = (w[i] >> 4) & 0x0F0F0F0Fu;
+    out[2 * i] = __builtin_bit_cast(h2_t, __builtin_amdgcn_perm(0x64646464u, lo, 0x04010400u)) - bias;
+    out[2 * i + 1] =
+        __builtin_bit_cast(h2_t, __builtin_amdgcn_perm(0x64646464u, lo, 0x04030402u)) - bias;
+    out[8 + 2 * i] =
+        __builtin_bit_cast(h2_t, __builtin_amdgcn_perm(0x64646464u, hi, 0x04010400u)) - bias;
+    out[8 + 2 * i + 1] =
+        __builtin_bit_cast(h2_t, __builtin_amdgcn_perm(0x64646464u, hi, 0x04030402u)) - bias;
+  }
+}
+
+// sum_{i<32} q_i * x_i in fp32, sequential over the 16 pairs in K order;
+// xs[0..3] hold elements 0-7, 8-15, 16-23 and 24-31.
+__device__ __forceinline__ float dot32_f16(const h2_t q[16], const uint4 xs[4]) {
+  float s = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    s = __builtin_amdgcn_fdot2(q[4 * i + 0], __builtin_bit_cast(h2_t, xs[i].x), s, false);
+    s = __builtin_amdgcn_fdot2(q[4 * i + 1], __builtin_bit_cast(h2_t, xs[i].y), s, false);
+    s = __builtin_amdgcn_fdot2(q[4 * i + 2], __builtin_bit_cast(h2_t, xs[i].z), s, false);
+    s = __builtin_amdgcn_fdot2(q[4 * i + 3], __builtin_bit_cast(h2_t, xs[i].w), s, false);
+  }
+  return s;
+}
+
+// fp32 activations: nibble - 8 as fp32 (exact), then an FMA chain in K order.
+__device__ __forceinline__ float dot32_f32(const uint4 q, const uint4 x[8]) {
+  const unsigned w[4] = {q.x, q.y, q.z, q.w};
+  float s = 0.0f;
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float4 xv = __builtin_bit_cast(float4, x[half * 4 + i]);
+      const float xe[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int nib = (int)((w[i] >> (8 * b + 4 * half)) & 0xFu) - 8;
+        s = __builtin_fmaf((float)nib, xe[b], s);
+      }
+    }
+  }
+  return s;
+}
+
+// One chunk c of R rows (quants q[r], fp16 scale bits d[r]) against the LDS
+// image xb of the live tokens n < nt: acc[n*R + r] += fp32(d) * chunk sum.
+template <int F, int NT, int R, bool XF32>
+__device__ __forceinline__ void chunk_fma(const uint4* q, const uint32_t* d, const uint4* xb, int C,
+                                          int c, int nt, float* acc) {
+  constexpr int P = ChunkPlanes<F, XF32>::P;
+  float df[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) df[r] = half_bits_to_float((uint16_t)d[r]);
+  if constexpr (F == kFmtQ8 && !XF32) {
+    h2_t qh[R][8];
+#pragma unroll
+    for (int r = 0; r < R; ++r) quants_to_h2(q[r], qh[r]);
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      if (n >= nt) break;
+      const uint4 xlo = xb[(n * P + 0) * C + c];
+      const uint4 xhi = xb[(n * P + 1) * C + c];
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const float sum = dot16_f16(qh[r], xlo, xhi);
+        acc[n * R + r] = __builtin_fmaf(df[r], sum, acc[n * R + r]);
+      }
+    }
+  } else if constexpr (F == kFmtQ8) {
+    float qf[R][16];
+#pragma unroll
+    for (int r = 0; r < R; ++r) quants_to_f32(q[r], qf[r]);
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      if (n >= nt) break;
+      const float4 x0 = __builtin_bit_cast(float4, xb[(n * P + 0) * C + c]);
+      const float4 x1 = __builtin_bit_cast(float4, xb[(n * P + 1) * C + c]);
+      const float4 x2 = __builtin_bit_cast(float4, xb[(n * P + 2) * C + c]);
+      const float4 x3 = __builtin_bit_cast(float4, xb[(n * P + 3) * C + c]);
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const float sum = dot16_f32(qf[r], x0, x1, x2, x3);
+        acc[n * R + r] = __builtin_fmaf(df[r], sum, acc[n * R + r]);
+      }
+    }
+  } else if constexpr (!XF32) {
+    h2_t qh[R][16];
+#pragma unroll
+    for (int r = 0; r < R; ++r) nibbles_to_h2(q[r], qh[r]);
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      if (n >= nt) break;
+      uint4 xs[4];
+#pragma unroll
+      for (int h = 0; h < 4; ++h) xs[h] = xb[(n * P + h) * C + c];
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const float sum = dot32_f16(qh[r], xs);
+        acc[n * R + r] = __builtin_fmaf(df[r], sum, acc[n * R + r]);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      if (n >= nt) break;
+      uint4 xv[8];
+#pragma unroll
+      for (int h = 0; h < 8; ++h) xv[h] = xb[(n * P + h) * C + c];
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const float sum = dot32_f32(q[r], xv);
+        acc[n * R + r] = __builtin_fmaf(df[r], sum, acc[n * R + r]);
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------- x staging
 // LDS image of x for one pass: token n, plane h (16-byte piece h of a chunk:
 // 2 planes for fp16, 4 for fp32), chunk c at uint4 index (n*P + h)*C + c.
@@ -207,6 +363,13 @@ __device__ __forceinline__ void stage_planes(const char* const rows[NT], int C, 
 template <int NT, bool XF32, int KBMAX = 2>
 __device__ __forceinline__ void stage_x(const char* const rows[NT], int C, uint4* lds, int nt = NT) {
   stage_planes<NT, XPlanes<XF32>::P, KBMAX>(rows, C, lds, nt);
+}
+
+// The LDS image for chunks of format F (C chunks per row).
+template <int F, int NT, bool XF32, int KBMAX = 2>
+__device__ __forceinline__ void stage_fmt(const char* const rows[NT], int C, uint4* lds,
+                                          int nt = NT) {
+  stage_planes<NT, ChunkPlanes<F, XF32>::P, KBMAX>(rows, C, lds, nt);
 }
 
 // ---------------------------------------------------------------- wave maximum
@@ -380,7 +543,8 @@ struct Slot {
 // nt <= NT is the number of live tokens (wave-uniform); tokens n >= nt are
 // skipped, so one instantiation serves any count up to NT with the same
 // per-token arithmetic.
-template <int NT, int LPR, int R, int D, int MINC, bool XF32, class Map, class Epi, class Stage>
+template <int NT, int LPR, int R, int D, int MINC, bool XF32, int F = kFmtQ8, class Map, class Epi,
+          class Stage>
 __device__ __forceinline__ void run_rows(const Map& map, Epi& epi, const uint4* lds, int C,
                                          int64_t n_groups, int64_t g_first, int64_t g_stride,
                                          int64_t row_origin, Stage&& stage, int nt = NT) {
@@ -389,7 +553,6 @@ __device__ __forceinline__ void run_rows(const Map& map, Epi& epi, const uint4* 
   constexpr int V = NT * R;
   constexpr int VP = Pow2<V>::value;
   using Shape = ReduceShape<LPR, VP, MINC>;
-  constexpr int P = XPlanes<XF32>::P;
 
   const int lane = threadIdx.x & (kWave - 1);
   const int p = lane % LPR;
@@ -422,7 +585,7 @@ __device__ __forceinline__ void run_rows(const Map& map, Epi& epi, const uint4* 
     for (int r = 0; r < R; ++r) {
       if (iok[r] && c < C) {
         sl.q[r] = load_stream16(iq[r] + (int64_t)c * 16);
-        sl.d[r] = id[r][c >> 1];
+        sl.d[r] = id[r][c >> Fmt<F>::kScaleShift];
       } else {
         sl.q[r] = make_uint4(0, 0, 0, 0);
         sl.d[r] = 0;
@@ -449,44 +612,7 @@ __device__ __forceinline__ void run_rows(const Map& map, Epi& epi, const uint4* 
 #pragma unroll
     for (int s = 0; s < D; ++s) {
       const int c = p + LPR * cj;
-      if (c < C) {
-        float df[R];
-#pragma unroll
-        for (int r = 0; r < R; ++r) df[r] = half_bits_to_float((uint16_t)slot[s].d[r]);
-        if constexpr (!XF32) {
-          h2_t qh[R][8];
-#pragma unroll
-          for (int r = 0; r < R; ++r) quants_to_h2(slot[s].q[r], qh[r]);
-#pragma unroll
-          for (int n = 0; n < NT; ++n) {
-            if (n >= nt) break;
-            const uint4 xlo = lds[(n * P + 0) * C + c];
-            const uint4 xhi = lds[(n * P + 1) * C + c];
-#pragma unroll
-            for (int r = 0; r < R; ++r) {
-              const float sum = dot16_f16(qh[r], xlo, xhi);
-              acc[n * R + r] = __builtin_fmaf(df[r], sum, acc[n * R + r]);
-            }
-          }
-        } else {
-          float qf[R][16];
-#pragma unroll
-          for (int r = 0; r < R; ++r) quants_to_f32(slot[s].q[r], qf[r]);
-#pragma unroll
-          for (int n = 0; n < NT; ++n) {
-            if (n >= nt) break;
-            const float4 x0 = __builtin_bit_cast(float4, lds[(n * P + 0) * C + c]);
-            const float4 x1 = __builtin_bit_cast(float4, lds[(n * P + 1) * C + c]);
-            const float4 x2 = __builtin_bit_cast(float4, lds[(n * P + 2) * C + c]);
-            const float4 x3 = __builtin_bit_cast(float4, lds[(n * P + 3) * C + c]);
-#pragma unroll
-            for (int r = 0; r < R; ++r) {
-              const float sum = dot16_f32(qf[r], x0, x1, x2, x3);
-              acc[n * R + r] = __builtin_fmaf(df[r], sum, acc[n * R + r]);
-            }
-          }
-        }
-      }
+      if (c < C) chunk_fma<F, NT, R, XF32>(slot[s].q, slot[s].d, lds, C, c, nt, acc);
       issue(slot[s]);
       if (++cj == CPL) {
         if (cg < n_groups) {

@@ -61,7 +61,7 @@ struct DenseEpi {
   }
 };
 
-template <int NT, int LPR, bool XF32, int MODE>
+template <int F, int NT, int LPR, bool XF32, int MODE>
 __global__ __launch_bounds__(kBlock) void gemv_kernel(DenseMap map, DenseEpi epi, const char* x,
                                                       int64_t ldx_bytes, int C) {
   extern __shared__ uint4 lds_x[];
@@ -73,12 +73,12 @@ __global__ __launch_bounds__(kBlock) void gemv_kernel(DenseMap map, DenseEpi epi
     const char* rows[NT];
 #pragma unroll
     for (int n = 0; n < NT; ++n) rows[n] = x + n * ldx_bytes;
-    stage_x<NT, XF32>(rows, C, lds_x);
+    stage_fmt<F, NT, XF32>(rows, C, lds_x);
     __syncthreads();
   };
-  run_rows<NT, LPR, T::R, T::D, 1, XF32>(map, epi, lds_x, C, n_groups,
-                                         (int64_t)blockIdx.x * kWavesPerBlock + wave,
-                                         (int64_t)gridDim.x * kWavesPerBlock, 0, stage);
+  run_rows<NT, LPR, T::R, T::D, 1, XF32, F>(map, epi, lds_x, C, n_groups,
+                                            (int64_t)blockIdx.x * kWavesPerBlock + wave,
+                                            (int64_t)gridDim.x * kWavesPerBlock, 0, stage);
 }
 
 // ---------------------------------------------------------------- gate/up + SiLU
@@ -129,7 +129,7 @@ struct GluTune {
   static constexpr int R = Tune<NT, BIG>::R < 2 ? 2 : Tune<NT, BIG>::R;
 };
 
-template <int NT, int LPR, bool XF32, bool BIG>
+template <int F, int NT, int LPR, bool XF32, bool BIG>
 __global__ __launch_bounds__(kBlock) void glu_kernel(GluMap map, GluEpi epi, const char* x,
                                                      int64_t ldx_bytes, int C) {
   extern __shared__ uint4 lds_x[];
@@ -141,22 +141,22 @@ __global__ __launch_bounds__(kBlock) void glu_kernel(GluMap map, GluEpi epi, con
     const char* rows[NT];
 #pragma unroll
     for (int n = 0; n < NT; ++n) rows[n] = x + n * ldx_bytes;
-    stage_x<NT, XF32>(rows, C, lds_x);
+    stage_fmt<F, NT, XF32>(rows, C, lds_x);
     __syncthreads();
   };
-  run_rows<NT, LPR, R, 1, 2, XF32>(map, epi, lds_x, C, n_groups,
-                                   (int64_t)blockIdx.x * kWavesPerBlock + wave,
-                                   (int64_t)gridDim.x * kWavesPerBlock, 0, stage);
+  run_rows<NT, LPR, R, 1, 2, XF32, F>(map, epi, lds_x, C, n_groups,
+                                      (int64_t)blockIdx.x * kWavesPerBlock + wave,
+                                      (int64_t)gridDim.x * kWavesPerBlock, 0, stage);
 }
 
-template <int NT, int LPR, bool XF32, bool BIG>
+template <int F, int NT, int LPR, bool XF32, bool BIG>
 static hipError_t glu_launch_t(const DevInfo& dev, GluMap map, GluEpi epi, const char* x,
                                int64_t ldx_bytes, int C, hipStream_t s) {
   constexpr int G = (kWave / LPR) * GluTune<NT, BIG>::R;
-  const size_t lds = (size_t)NT * C * 16 * XPlanes<XF32>::P;
+  const size_t lds = (size_t)NT * C * 16 * ChunkPlanes<F, XF32>::P;
   const int64_t n_groups = (map.M2 + G - 1) / G;
   const int64_t need = (n_groups + kWavesPerBlock - 1) / kWavesPerBlock;
-  auto fn = glu_kernel<NT, LPR, XF32, BIG>;
+  auto fn = glu_kernel<F, NT, LPR, XF32, BIG>;
   if (lds > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize,
                                        (int)lds);
@@ -169,21 +169,21 @@ static hipError_t glu_launch_t(const DevInfo& dev, GluMap map, GluEpi epi, const
   return hipLaunchKernel((const void*)fn, dim3((unsigned)blocks), dim3(kBlock), args, lds, s);
 }
 
-template <int LPR, bool XF32>
+template <int F, int LPR, bool XF32>
 static hipError_t glu_launch_nt(const DevInfo& dev, int nt, GluMap map, GluEpi epi, const char* x,
                                 int64_t ldx_bytes, int C, hipStream_t s) {
   switch (nt) {
     case 1:
       if (map.M2 >= kBigRows)
-        return glu_launch_t<1, LPR, XF32, true>(dev, map, epi, x, ldx_bytes, C, s);
-      return glu_launch_t<1, LPR, XF32, false>(dev, map, epi, x, ldx_bytes, C, s);
-    case 2: return glu_launch_t<2, LPR, XF32, false>(dev, map, epi, x, ldx_bytes, C, s);
-    case 3: return glu_launch_t<3, LPR, XF32, false>(dev, map, epi, x, ldx_bytes, C, s);
-    case 4: return glu_launch_t<4, LPR, XF32, false>(dev, map, epi, x, ldx_bytes, C, s);
-    case 5: return glu_launch_t<5, LPR, XF32, false>(dev, map, epi, x, ldx_bytes, C, s);
-    case 6: return glu_launch_t<6, LPR, XF32, false>(dev, map, epi, x, ldx_bytes, C, s);
-    case 7: return glu_launch_t<7, LPR, XF32, false>(dev, map, epi, x, ldx_bytes, C, s);
-    case 8: return glu_launch_t<8, LPR, XF32, false>(dev, map, epi, x, ldx_bytes, C, s);
+        return glu_launch_t<F, 1, LPR, XF32, true>(dev, map, epi, x, ldx_bytes, C, s);
+      return glu_launch_t<F, 1, LPR, XF32, false>(dev, map, epi, x, ldx_bytes, C, s);
+    case 2: return glu_launch_t<F, 2, LPR, XF32, false>(dev, map, epi, x, ldx_bytes, C, s);
+    case 3: return glu_launch_t<F, 3, LPR, XF32, false>(dev, map, epi, x, ldx_bytes, C, s);
+    case 4: return glu_launch_t<F, 4, LPR, XF32, false>(dev, map, epi, x, ldx_bytes, C, s);
+    case 5: return glu_launch_t<F, 5, LPR, XF32, false>(dev, map, epi, x, ldx_bytes, C, s);
+    case 6: return glu_launch_t<F, 6, LPR, XF32, false>(dev, map, epi, x, ldx_bytes, C, s);
+    case 7: return glu_launch_t<F, 7, LPR, XF32, false>(dev, map, epi, x, ldx_bytes, C, s);
+    case 8: return glu_launch_t<F, 8, LPR, XF32, false>(dev, map, epi, x, ldx_bytes, C, s);
   }
   return hipErrorInvalidValue;
 }
@@ -204,28 +204,23 @@ hipError_t launch_glu(const DevInfo& dev, const HMat& Gm, const HMat& Um, const 
   epi.h = (char*)h;
   epi.M = Gm.M;
   epi.f16 = h_f16;
-  const int C = (int)(Gm.K / 16);
+  const int C = (int)chunks_per_row(Gm.fmt, Gm.K);
   const int64_t ldx_bytes = Gm.K * (x_f32 ? 4 : 2);
   const char* xp = (const char*)x;
-  const int lpr = lanes_per_row(Gm.K);
-  if (x_f32) {
-    if (lpr == 64) return glu_launch_nt<64, true>(dev, nt, map, epi, xp, ldx_bytes, C, s);
-    if (lpr == 32) return glu_launch_nt<32, true>(dev, nt, map, epi, xp, ldx_bytes, C, s);
-    return glu_launch_nt<16, true>(dev, nt, map, epi, xp, ldx_bytes, C, s);
-  }
-  if (lpr == 64) return glu_launch_nt<64, false>(dev, nt, map, epi, xp, ldx_bytes, C, s);
-  if (lpr == 32) return glu_launch_nt<32, false>(dev, nt, map, epi, xp, ldx_bytes, C, s);
-  return glu_launch_nt<16, false>(dev, nt, map, epi, xp, ldx_bytes, C, s);
+  return dispatch_chunks(Gm.fmt, lanes_for(Gm.fmt, Gm.K), x_f32, [&](auto f, auto l, auto xf) {
+    return glu_launch_nt<decltype(f)::value, decltype(l)::value, decltype(xf)::value>(
+        dev, nt, map, epi, xp, ldx_bytes, C, s);
+  });
 }
 
-template <int NT, int LPR, bool XF32, int MODE>
+template <int F, int NT, int LPR, bool XF32, int MODE>
 static hipError_t launch_t(const DevInfo& dev, DenseMap map, DenseEpi epi, const char* x,
                            int64_t ldx_bytes, int C, hipStream_t s) {
   constexpr int G = (kWave / LPR) * TuneM<NT, MODE>::R;
-  const size_t lds = (size_t)NT * C * 16 * XPlanes<XF32>::P;
+  const size_t lds = (size_t)NT * C * 16 * ChunkPlanes<F, XF32>::P;
   const int64_t n_groups = (map.Mtot + G - 1) / G;
   const int64_t need = (n_groups + kWavesPerBlock - 1) / kWavesPerBlock;
-  auto fn = gemv_kernel<NT, LPR, XF32, MODE>;
+  auto fn = gemv_kernel<F, NT, LPR, XF32, MODE>;
   if (lds > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize,
                                        (int)lds);
@@ -238,11 +233,11 @@ static hipError_t launch_t(const DevInfo& dev, DenseMap map, DenseEpi epi, const
   return hipLaunchKernel((const void*)fn, dim3((unsigned)blocks), dim3(kBlock), args, lds, s);
 }
 
-template <int NT, int LPR, bool XF32>
+template <int F, int NT, int LPR, bool XF32>
 static hipError_t launch_sz(const DevInfo& dev, DenseMap map, DenseEpi epi, const char* x,
                             int64_t ldx_bytes, int C, hipStream_t s) {
   if (NT == 1 && map.Mtot >= kBigRows)
-    return launch_t<NT, LPR, XF32, 1>(dev, map, epi, x, ldx_bytes, C, s);
+    return launch_t<F, NT, LPR, XF32, 1>(dev, map, epi, x, ldx_bytes, C, s);
   // Small-matrix mode when the usual row groups cannot occupy the chip:
   // at most two groups per CU, or (for N >= 2, where teams carry 2-4 rows)
   // fewer groups than the chip's wave slots. Measured on MI355X: 5120 x
@@ -252,22 +247,22 @@ static hipError_t launch_sz(const DevInfo& dev, DenseMap map, DenseEpi epi, cons
   constexpr int G0 = (kWave / LPR) * TuneM<NT, 0>::R;
   const int64_t groups = (map.Mtot + G0 - 1) / G0;
   if (groups <= 2 * (int64_t)dev.cus || (NT > 1 && groups < (int64_t)dev.cus * 32))
-    return launch_t<NT, LPR, XF32, 2>(dev, map, epi, x, ldx_bytes, C, s);
-  return launch_t<NT, LPR, XF32, 0>(dev, map, epi, x, ldx_bytes, C, s);
+    return launch_t<F, NT, LPR, XF32, 2>(dev, map, epi, x, ldx_bytes, C, s);
+  return launch_t<F, NT, LPR, XF32, 0>(dev, map, epi, x, ldx_bytes, C, s);
 }
 
-template <int LPR, bool XF32>
+template <int F, int LPR, bool XF32>
 static hipError_t launch_nt(const DevInfo& dev, int nt, DenseMap map, DenseEpi epi, const char* x,
                             int64_t ldx_bytes, int C, hipStream_t s) {
   switch (nt) {
-    case 1: return launch_sz<1, LPR, XF32>(dev, map, epi, x, ldx_bytes, C, s);
-    case 2: return launch_sz<2, LPR, XF32>(dev, map, epi, x, ldx_bytes, C, s);
-    case 3: return launch_sz<3, LPR, XF32>(dev, map, epi, x, ldx_bytes, C, s);
-    case 4: return launch_sz<4, LPR, XF32>(dev, map, epi, x, ldx_bytes, C, s);
-    case 5: return launch_sz<5, LPR, XF32>(dev, map, epi, x, ldx_bytes, C, s);
-    case 6: return launch_sz<6, LPR, XF32>(dev, map, epi, x, ldx_bytes, C, s);
-    case 7: return launch_sz<7, LPR, XF32>(dev, map, epi, x, ldx_bytes, C, s);
-    case 8: return launch_sz<8, LPR, XF32>(dev, map, epi, x, ldx_bytes, C, s);
+    case 1: return launch_sz<F, 1, LPR, XF32>(dev, map, epi, x, ldx_bytes, C, s);
+    case 2: return launch_sz<F, 2, LPR, XF32>(dev, map, epi, x, ldx_bytes, C, s);
+    case 3: return launch_sz<F, 3, LPR, XF32>(dev, map, epi, x, ldx_bytes, C, s);
+    case 4: return launch_sz<F, 4, LPR, XF32>(dev, map, epi, x, ldx_bytes, C, s);
+    case 5: return launch_sz<F, 5, LPR, XF32>(dev, map, epi, x, ldx_bytes, C, s);
+    case 6: return launch_sz<F, 6, LPR, XF32>(dev, map, epi, x, ldx_bytes, C, s);
+    case 7: return launch_sz<F, 7, LPR, XF32>(dev, map, epi, x, ldx_bytes, C, s);
+    case 8: return launch_sz<F, 8, LPR, XF32>(dev, map, epi, x, ldx_bytes, C, s);
   }
   return hipErrorInvalidValue;
 }
@@ -323,18 +318,13 @@ hipError_t launch_gemv(const DevInfo& dev, const HMat& A, const HMat* B, const v
   epi.Ma = map.Ma;
   epi.Mtot = map.Mtot;
   epi.f16 = y_f16;
-  const int C = (int)(A.K / 16);
+  const int C = (int)chunks_per_row(A.fmt, A.K);
   const int64_t ldx_bytes = ldx * (x_f32 ? 4 : 2);
   const char* xp = (const char*)x;
-  const int lpr = lanes_per_row(A.K);
-  if (x_f32) {
-    if (lpr == 64) return launch_nt<64, true>(dev, nt, map, epi, xp, ldx_bytes, C, s);
-    if (lpr == 32) return launch_nt<32, true>(dev, nt, map, epi, xp, ldx_bytes, C, s);
-    return launch_nt<16, true>(dev, nt, map, epi, xp, ldx_bytes, C, s);
-  }
-  if (lpr == 64) return launch_nt<64, false>(dev, nt, map, epi, xp, ldx_bytes, C, s);
-  if (lpr == 32) return launch_nt<32, false>(dev, nt, map, epi, xp, ldx_bytes, C, s);
-  return launch_nt<16, false>(dev, nt, map, epi, xp, ldx_bytes, C, s);
+  return dispatch_chunks(A.fmt, lanes_for(A.fmt, A.K), x_f32, [&](auto f, auto l, auto xf) {
+    return launch_nt<decltype(f)::value, decltype(l)::value, decltype(xf)::value>(
+        dev, nt, map, epi, xp, ldx_bytes, C, s);
+  });
 }
 
 }  // namespace q8

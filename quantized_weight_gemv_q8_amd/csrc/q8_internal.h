@@ -6,6 +6,10 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <type_traits>
+
+#include "q8_format.h"
+
 namespace q8 {
 
 struct DevInfo {
@@ -19,6 +23,7 @@ struct HMat {  // host view of one packed matrix
   const int8_t* qs;
   const uint16_t* d;
   int64_t M, K, ld_qs, ld_d;
+  int fmt;  // kFmtQ8 or kFmtQ4
 };
 
 struct HBank {
@@ -28,8 +33,27 @@ struct HBank {
 };
 
 // Lanes per row team for a given K (K only: keeps per-token results
-// independent of N and of the kernel that runs the row).
+// independent of N and of the kernel that runs the row). Chosen from the
+// number of 16-byte chunks, K/16 for Q8_0.
 int lanes_per_row(int64_t K);
+inline int lanes_for(int fmt, int64_t K) { return lanes_per_row(fmt == kFmtQ4 ? K / 2 : K); }
+
+// Calls fn(F, LPR, XF32) with the runtime format, lane count and x type as
+// compile-time constants (std::integral_constant values).
+template <class Fn>
+inline hipError_t dispatch_chunks(int fmt, int lpr, bool x_f32, Fn&& fn) {
+  auto by_x = [&](auto f, auto l) -> hipError_t {
+    if (x_f32) return fn(f, l, std::true_type{});
+    return fn(f, l, std::false_type{});
+  };
+  auto by_l = [&](auto f) -> hipError_t {
+    if (lpr == 64) return by_x(f, std::integral_constant<int, 64>{});
+    if (lpr == 32) return by_x(f, std::integral_constant<int, 32>{});
+    return by_x(f, std::integral_constant<int, 16>{});
+  };
+  if (fmt == kFmtQ4) return by_l(std::integral_constant<int, kFmtQ4>{});
+  return by_l(std::integral_constant<int, kFmtQ8>{});
+}
 
 // Resident workgroups of kernel `fn` per compute unit at `lds` bytes of
 // dynamic LDS (kBlock threads), from the runtime's occupancy calculator;
@@ -92,10 +116,6 @@ hipError_t launch_moe_gate_up(const DevInfo& dev, const HBank& G, const HBank& U
 // h[n][m] = silu(G x_n)[m] * (U x_n)[m]; G, U of one shape; h fp32 or fp16.
 hipError_t launch_glu(const DevInfo& dev, const HMat& G, const HMat& U, const void* x,
                       bool x_f32, void* h, bool h_f16, int nt, hipStream_t s);
-// Q4_0 GEMV: W.qs is the nibble plane (16-byte blocks, row stride ld_qs
-// bytes >= K/2), W.d the fp16 scales; y [nt][M] fp32 or fp16.
-hipError_t launch_gemv_q4(const DevInfo& dev, const HMat& W, const void* x, bool x_f32, void* y,
-                          bool y_f16, int nt, hipStream_t s);
 // Router: ids [T][topk] and softmax weights [T][topk] from logits [T][E].
 constexpr int kRouterMaxE = 4096;  // 64 experts per lane of the token's wave
 constexpr int kRouterMaxK = 64;    // one picked logit per lane

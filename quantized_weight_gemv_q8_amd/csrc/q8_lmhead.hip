@@ -114,7 +114,7 @@ struct LmEpi {
   }
 };
 
-template <int NT, int LPR, bool XF32, bool BIG>
+template <int F, int NT, int LPR, bool XF32, bool BIG>
 __global__ __launch_bounds__(kBlock) void lmhead_kernel(LmMap map, float* logits, int64_t ld,
                                                         const char* x, int64_t ldx_bytes, int C,
                                                         char* ws, int32_t* ids) {
@@ -138,12 +138,12 @@ __global__ __launch_bounds__(kBlock) void lmhead_kernel(LmMap map, float* logits
     const char* rows[NT];
 #pragma unroll
     for (int n = 0; n < NT; ++n) rows[n] = x + n * ldx_bytes;
-    stage_x<NT, XF32>(rows, C, lds_x);
+    stage_fmt<F, NT, XF32>(rows, C, lds_x);
     __syncthreads();
   };
-  run_rows<NT, LPR, R, T::D, 1, XF32>(map, epi, lds_x, C, n_groups,
-                                      (int64_t)blockIdx.x * kWavesPerBlock + wave,
-                                      (int64_t)gridDim.x * kWavesPerBlock, 0, stage);
+  run_rows<NT, LPR, R, T::D, 1, XF32, F>(map, epi, lds_x, C, n_groups,
+                                         (int64_t)blockIdx.x * kWavesPerBlock + wave,
+                                         (int64_t)gridDim.x * kWavesPerBlock, 0, stage);
 
 #pragma unroll
   for (int n = 0; n < NT; ++n) {
@@ -209,13 +209,13 @@ __global__ __launch_bounds__(kBlock) void lmhead_kernel(LmMap map, float* logits
   }
 }
 
-template <int NT, int LPR, bool XF32, bool BIG>
+template <int F, int NT, int LPR, bool XF32, bool BIG>
 static hipError_t lm_launch_t(const DevInfo& dev, LmMap map, float* logits, int64_t ld,
                               const char* x, int64_t ldx_bytes, int C, char* ws,
                               int32_t* ids, hipStream_t s) {
   constexpr int G = (kWave / LPR) * Tune<NT, BIG>::R;
-  const size_t lds = (size_t)NT * C * 16 * XPlanes<XF32>::P;
-  auto fn = lmhead_kernel<NT, LPR, XF32, BIG>;
+  const size_t lds = (size_t)NT * C * 16 * ChunkPlanes<F, XF32>::P;
+  auto fn = lmhead_kernel<F, NT, LPR, XF32, BIG>;
   if (lds > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize,
                                        (int)lds);
@@ -231,23 +231,25 @@ static hipError_t lm_launch_t(const DevInfo& dev, LmMap map, float* logits, int6
   return hipLaunchKernel((const void*)fn, dim3((unsigned)blocks), dim3(kBlock), args, lds, s);
 }
 
-template <int LPR, bool XF32>
+template <int F, int LPR, bool XF32>
 static hipError_t lm_launch_nt(const DevInfo& dev, int nt, LmMap map, float* logits, int64_t ld,
-                               const char* x, int64_t ldx_bytes, int C, char* ws,
-                               int32_t* ids, hipStream_t s) {
+                               const char* x, int64_t ldx_bytes, int C, char* ws, int32_t* ids,
+                               hipStream_t s) {
+#define Q8_LM(NTV, BIGV) \
+  return lm_launch_t<F, NTV, LPR, XF32, BIGV>(dev, map, logits, ld, x, ldx_bytes, C, ws, ids, s)
   switch (nt) {
     case 1:
-      if (map.V >= kBigRows)
-        return lm_launch_t<1, LPR, XF32, true>(dev, map, logits, ld, x, ldx_bytes, C, ws, ids, s);
-      return lm_launch_t<1, LPR, XF32, false>(dev, map, logits, ld, x, ldx_bytes, C, ws, ids, s);
-    case 2: return lm_launch_t<2, LPR, XF32, false>(dev, map, logits, ld, x, ldx_bytes, C, ws, ids, s);
-    case 3: return lm_launch_t<3, LPR, XF32, false>(dev, map, logits, ld, x, ldx_bytes, C, ws, ids, s);
-    case 4: return lm_launch_t<4, LPR, XF32, false>(dev, map, logits, ld, x, ldx_bytes, C, ws, ids, s);
-    case 5: return lm_launch_t<5, LPR, XF32, false>(dev, map, logits, ld, x, ldx_bytes, C, ws, ids, s);
-    case 6: return lm_launch_t<6, LPR, XF32, false>(dev, map, logits, ld, x, ldx_bytes, C, ws, ids, s);
-    case 7: return lm_launch_t<7, LPR, XF32, false>(dev, map, logits, ld, x, ldx_bytes, C, ws, ids, s);
-    case 8: return lm_launch_t<8, LPR, XF32, false>(dev, map, logits, ld, x, ldx_bytes, C, ws, ids, s);
+      if (map.V >= kBigRows) Q8_LM(1, true);
+      Q8_LM(1, false);
+    case 2: Q8_LM(2, false);
+    case 3: Q8_LM(3, false);
+    case 4: Q8_LM(4, false);
+    case 5: Q8_LM(5, false);
+    case 6: Q8_LM(6, false);
+    case 7: Q8_LM(7, false);
+    case 8: Q8_LM(8, false);
   }
+#undef Q8_LM
   return hipErrorInvalidValue;
 }
 
@@ -260,18 +262,13 @@ hipError_t launch_lmhead(const DevInfo& dev, const HMat& W, const int32_t* row_i
   map.w = MatDesc{W.qs, W.d, W.ld_qs, W.ld_d};
   map.V = W.M;
   map.row_ids = row_ids;
-  const int C = (int)(W.K / 16);
+  const int C = (int)chunks_per_row(W.fmt, W.K);
   const int64_t ldx_bytes = W.K * (x_f32 ? 4 : 2);
   const char* xp = (const char*)x;
-  const int lpr = lanes_per_row(W.K);
-  if (x_f32) {
-    if (lpr == 64) return lm_launch_nt<64, true>(dev, nt, map, logits, ld_logits, xp, ldx_bytes, C, ws, ids, s);
-    if (lpr == 32) return lm_launch_nt<32, true>(dev, nt, map, logits, ld_logits, xp, ldx_bytes, C, ws, ids, s);
-    return lm_launch_nt<16, true>(dev, nt, map, logits, ld_logits, xp, ldx_bytes, C, ws, ids, s);
-  }
-  if (lpr == 64) return lm_launch_nt<64, false>(dev, nt, map, logits, ld_logits, xp, ldx_bytes, C, ws, ids, s);
-  if (lpr == 32) return lm_launch_nt<32, false>(dev, nt, map, logits, ld_logits, xp, ldx_bytes, C, ws, ids, s);
-  return lm_launch_nt<16, false>(dev, nt, map, logits, ld_logits, xp, ldx_bytes, C, ws, ids, s);
+  return dispatch_chunks(W.fmt, lanes_for(W.fmt, W.K), x_f32, [&](auto f, auto l, auto xf) {
+    return lm_launch_nt<decltype(f)::value, decltype(l)::value, decltype(xf)::value>(
+        dev, nt, map, logits, ld_logits, xp, ldx_bytes, C, ws, ids, s);
+  });
 }
 
 }  // namespace q8

@@ -242,7 +242,8 @@ struct SiluMulEpi {  // values come in (gate, up) pairs for one token
 // seg_pid[j * NT ..], and its tokens' activations at LDS block j * NT.
 // Same per-lane chunk order, accumulation and team reduction as the dense
 // engine, so each (row, token) result is the dense result.
-template <int NT, int LPR, int R, int D, int MINC, bool XF32, class RowOf, class Epi, class Stage>
+template <int F, int NT, int LPR, int R, int D, int MINC, bool XF32, class RowOf, class Epi,
+          class Stage>
 __device__ __forceinline__ void run_routed(const RowOf& rowof, Epi& epi, const uint4* lds, int C,
                                            int g_begin, int g_end, int gpv, int rpv, int v0,
                                            const int32_t* seg_e, const int32_t* seg_nt,
@@ -252,7 +253,7 @@ __device__ __forceinline__ void run_routed(const RowOf& rowof, Epi& epi, const u
   constexpr int V = NT * R;
   constexpr int VP = Pow2<V>::value;
   using Shape = ReduceShape<LPR, VP, MINC>;
-  constexpr int P = XPlanes<XF32>::P;
+  constexpr int P = ChunkPlanes<F, XF32>::P;
   constexpr int S = kWavesPerBlock;  // waves of the workgroup take groups in turn
 
   const int wave = threadIdx.x / kWave;
@@ -286,7 +287,7 @@ __device__ __forceinline__ void run_routed(const RowOf& rowof, Epi& epi, const u
     for (int r = 0; r < R; ++r) {
       if (iok[r] && c < C) {
         sl.q[r] = load_stream16(iq[r] + (int64_t)c * 16);
-        sl.d[r] = id[r][c >> 1];
+        sl.d[r] = id[r][c >> Fmt<F>::kScaleShift];
       } else {
         sl.q[r] = make_uint4(0, 0, 0, 0);
         sl.d[r] = 0;
@@ -330,44 +331,7 @@ __device__ __forceinline__ void run_routed(const RowOf& rowof, Epi& epi, const u
 #pragma unroll
     for (int s = 0; s < D; ++s) {
       const int c = p + LPR * cj;
-      if (c < C) {
-        float df[R];
-#pragma unroll
-        for (int r = 0; r < R; ++r) df[r] = half_bits_to_float((uint16_t)slot[s].d[r]);
-        if constexpr (!XF32) {
-          h2_t qh[R][8];
-#pragma unroll
-          for (int r = 0; r < R; ++r) quants_to_h2(slot[s].q[r], qh[r]);
-#pragma unroll
-          for (int n = 0; n < NT; ++n) {
-            if (n >= nt) break;
-            const uint4 xlo = xb[(n * P + 0) * C + c];
-            const uint4 xhi = xb[(n * P + 1) * C + c];
-#pragma unroll
-            for (int r = 0; r < R; ++r) {
-              const float sum = dot16_f16(qh[r], xlo, xhi);
-              acc[n * R + r] = __builtin_fmaf(df[r], sum, acc[n * R + r]);
-            }
-          }
-        } else {
-          float qf[R][16];
-#pragma unroll
-          for (int r = 0; r < R; ++r) quants_to_f32(slot[s].q[r], qf[r]);
-#pragma unroll
-          for (int n = 0; n < NT; ++n) {
-            if (n >= nt) break;
-            const float4 x0 = __builtin_bit_cast(float4, xb[(n * P + 0) * C + c]);
-            const float4 x1 = __builtin_bit_cast(float4, xb[(n * P + 1) * C + c]);
-            const float4 x2 = __builtin_bit_cast(float4, xb[(n * P + 2) * C + c]);
-            const float4 x3 = __builtin_bit_cast(float4, xb[(n * P + 3) * C + c]);
-#pragma unroll
-            for (int r = 0; r < R; ++r) {
-              const float sum = dot16_f32(qf[r], x0, x1, x2, x3);
-              acc[n * R + r] = __builtin_fmaf(df[r], sum, acc[n * R + r]);
-            }
-          }
-        }
-      }
+      if (c < C) chunk_fma<F, NT, R, XF32>(slot[s].q, slot[s].d, xb, C, c, nt, acc);
       issue(slot[s]);
       if (++cj == CPL) {
         if (cg < g_end) {
@@ -398,14 +362,13 @@ __device__ __forceinline__ void run_routed(const RowOf& rowof, Epi& epi, const u
 // segments' slot records, issue the first weight loads, stage the
 // activations of their tokens (x row p / topk, or p when x holds one row
 // per pair), then stream.
-template <int NT, int LPR, int R, int MINC, bool XF32, class RowOf, class Epi>
+template <int F, int NT, int LPR, int R, int MINC, bool XF32, class RowOf, class Epi>
 __device__ __forceinline__ void routed_slices(const MoeWs& ws, const RowOf& rowof, Epi& epi,
                                               const char* x, int64_t ldx_bytes, bool x_per_pair,
                                               int topk, int C, int rpv, uint4* lds) {
   __shared__ int32_t seg_e[kSegV], seg_nt[kSegV], seg_pid[kSegV * NT];
   static_assert(NT == kMoeNT, "slot records hold kMoeNT pairs");
   constexpr int G = (kWave / LPR) * R;
-  constexpr int P = XPlanes<XF32>::P;
   const int gpv = (rpv + G - 1) / G;
   const int nv = __builtin_amdgcn_readfirstlane(*ws.n_vslots);
   const int n_groups = nv * gpv;
@@ -440,17 +403,27 @@ __device__ __forceinline__ void routed_slices(const MoeWs& ws, const RowOf& rowo
         const int src = x_per_pair ? pid : pid / topk;
         rows[i] = pid < 0 ? nullptr : x + (int64_t)src * ldx_bytes;
       }
-      stage_x<kSegV * NT, XF32, 1>(rows, C, lds);
+      stage_fmt<F, kSegV * NT, XF32, 1>(rows, C, lds);
       __syncthreads();
     };
-    run_routed<NT, LPR, R, 1, MINC, XF32>(rowof, epi, lds, C, g, seg_end, gpv, rpv, v0, seg_e,
+    run_routed<F, NT, LPR, R, 1, MINC, XF32>(rowof, epi, lds, C, g, seg_end, gpv, rpv, v0, seg_e,
                                           seg_nt, seg_pid, stage);
     g = seg_end;
   }
 }
 
-template <int LPR, bool XF32>
-__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(XF32 ? 4 : 6))) void moe_rows_kernel(HBank W, MoeWs ws, int topk,
+// Occupancy request: 6 waves per SIMD (80 VGPRs) for Q8_0 with fp16
+// activations, which the kernels meet without spilling (measured faster
+// than the 5 waves the allocator picks unasked); 4 for the heavier fp32
+// or Q4_0 variants; none for Q4_0 with fp32 activations, which needs more
+// than 128 VGPRs.
+template <int F, bool XF32>
+constexpr int moe_waves() {
+  return (XF32 && F == kFmtQ4) ? 1 : (XF32 || F == kFmtQ4) ? 4 : 6;
+}
+
+template <int F, int LPR, bool XF32>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(moe_waves<F, XF32>()))) void moe_rows_kernel(HBank W, MoeWs ws, int topk,
                                                          const char* x, int64_t ldx_bytes,
                                                          int x_per_pair, float* y) {
   extern __shared__ uint4 lds_x[];
@@ -466,13 +439,14 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(XF32 ? 4
     d = W.e0.d + (int64_t)e * W.stride_d + (int64_t)i * W.e0.ld_d;
     return true;
   };
-  routed_slices<kMoeNT, LPR, Tune<kMoeNT, false>::R, 1, XF32>(
-      ws, rowof, epi, x, ldx_bytes, x_per_pair != 0, topk, (int)(W.e0.K / 16), M, lds_x);
+  routed_slices<F, kMoeNT, LPR, Tune<kMoeNT, false>::R, 1, XF32>(
+      ws, rowof, epi, x, ldx_bytes, x_per_pair != 0, topk, (int)chunks_per_row(F, W.e0.K), M,
+      lds_x);
 }
 
 // virtual row i = 2*rho + s: s = 0 gate row rho, s = 1 up row rho
-template <int LPR, bool XF32>
-__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(XF32 ? 4 : 6))) void moe_gate_up_kernel(HBank Gb, HBank Ub, MoeWs ws,
+template <int FM, int LPR, bool XF32>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(moe_waves<FM, XF32>()))) void moe_gate_up_kernel(HBank Gb, HBank Ub, MoeWs ws,
                                                             int topk, const char* x,
                                                             int64_t ldx_bytes, float* h) {
   extern __shared__ uint4 lds_x[];
@@ -496,8 +470,8 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(XF32 ? 4
     d = d0 + (int64_t)e * sd + rho * ld;
     return true;
   };
-  routed_slices<kMoeNT, LPR, 2, 2, XF32>(ws, rowof, epi, x, ldx_bytes, false, topk,
-                                         (int)(Gb.e0.K / 16), 2 * F, lds_x);
+  routed_slices<FM, kMoeNT, LPR, 2, 2, XF32>(ws, rowof, epi, x, ldx_bytes, false, topk,
+                                             (int)chunks_per_row(FM, Gb.e0.K), 2 * F, lds_x);
 }
 
 __global__ __launch_bounds__(256) void moe_combine_kernel(const int32_t* ids, int E,
@@ -583,7 +557,7 @@ static hipError_t moe_launch(Fn fn, size_t lds, void** args, hipStream_t s, cons
                          args, lds, s);
 }
 
-template <int LPR, bool XF32>
+template <int F, int LPR, bool XF32>
 static hipError_t moe_rows_t(const DevInfo& dev, const HBank& W, const MoeWs& ws, int topk,
                              const char* x, int64_t ldx_bytes, int x_per_pair, float* y,
                              hipStream_t s) {
@@ -591,7 +565,7 @@ static hipError_t moe_rows_t(const DevInfo& dev, const HBank& W, const MoeWs& ws
   HBank w = W;
   MoeWs wsv = ws;
   void* args[] = {&w, &wsv, &topk, (void*)&x, &ldx_bytes, &x_per_pair, &y};
-  return moe_launch(moe_rows_kernel<LPR, XF32>, lds, args, s, dev);
+  return moe_launch(moe_rows_kernel<F, LPR, XF32>, lds, args, s, dev);
 }
 
 hipError_t launch_moe_gemv(const DevInfo& dev, const HBank& W, const MoeWs& ws, int topk,
@@ -599,26 +573,22 @@ hipError_t launch_moe_gemv(const DevInfo& dev, const HBank& W, const MoeWs& ws, 
                            hipStream_t s) {
   const int64_t ldx_bytes = W.e0.K * (x_f32 ? 4 : 2);
   const char* xp = (const char*)x;
-  const int lpr = lanes_per_row(W.e0.K);
   const int xpp = x_per_pair ? 1 : 0;
-  if (x_f32) {
-    if (lpr == 64) return moe_rows_t<64, true>(dev, W, ws, topk, xp, ldx_bytes, xpp, y_pair, s);
-    if (lpr == 32) return moe_rows_t<32, true>(dev, W, ws, topk, xp, ldx_bytes, xpp, y_pair, s);
-    return moe_rows_t<16, true>(dev, W, ws, topk, xp, ldx_bytes, xpp, y_pair, s);
-  }
-  if (lpr == 64) return moe_rows_t<64, false>(dev, W, ws, topk, xp, ldx_bytes, xpp, y_pair, s);
-  if (lpr == 32) return moe_rows_t<32, false>(dev, W, ws, topk, xp, ldx_bytes, xpp, y_pair, s);
-  return moe_rows_t<16, false>(dev, W, ws, topk, xp, ldx_bytes, xpp, y_pair, s);
+  return dispatch_chunks(W.e0.fmt, lanes_for(W.e0.fmt, W.e0.K), x_f32,
+                         [&](auto f, auto l, auto xf) {
+    return moe_rows_t<decltype(f)::value, decltype(l)::value, decltype(xf)::value>(
+        dev, W, ws, topk, xp, ldx_bytes, xpp, y_pair, s);
+  });
 }
 
-template <int LPR, bool XF32>
+template <int F, int LPR, bool XF32>
 static hipError_t moe_gu_t(const DevInfo& dev, const HBank& G, const HBank& U, const MoeWs& ws,
                            int topk, const char* x, int64_t ldx_bytes, float* h, hipStream_t s) {
   const size_t lds = moe_lds_bytes(G.e0.K, XF32);
   HBank g = G, u = U;
   MoeWs wsv = ws;
   void* args[] = {&g, &u, &wsv, &topk, (void*)&x, &ldx_bytes, &h};
-  return moe_launch(moe_gate_up_kernel<LPR, XF32>, lds, args, s, dev);
+  return moe_launch(moe_gate_up_kernel<F, LPR, XF32>, lds, args, s, dev);
 }
 
 hipError_t launch_moe_gate_up(const DevInfo& dev, const HBank& G, const HBank& U,
@@ -628,13 +598,16 @@ hipError_t launch_moe_gate_up(const DevInfo& dev, const HBank& G, const HBank& U
   const char* xp = (const char*)x;
   // Teams of at most 32 lanes: a wave then works on two gate/up row pairs
   // (2.5% faster than 64-lane teams at K = 2048 in same-process A/B).
-  const int lpr = lanes_per_row(G.e0.K) < 32 ? lanes_per_row(G.e0.K) : 32;
-  if (x_f32) {
-    if (lpr == 32) return moe_gu_t<32, true>(dev, G, U, ws, topk, xp, ldx_bytes, h, s);
-    return moe_gu_t<16, true>(dev, G, U, ws, topk, xp, ldx_bytes, h, s);
-  }
-  if (lpr == 32) return moe_gu_t<32, false>(dev, G, U, ws, topk, xp, ldx_bytes, h, s);
-  return moe_gu_t<16, false>(dev, G, U, ws, topk, xp, ldx_bytes, h, s);
+  const int lpr0 = lanes_for(G.e0.fmt, G.e0.K);
+  const int lpr = lpr0 < 32 ? lpr0 : 32;
+  return dispatch_chunks(G.e0.fmt, lpr, x_f32, [&](auto f, auto l, auto xf) -> hipError_t {
+    if constexpr (decltype(l)::value == 64) {
+      return hipErrorInvalidValue;  // never chosen: teams are capped at 32 lanes
+    } else {
+      return moe_gu_t<decltype(f)::value, decltype(l)::value, decltype(xf)::value>(
+          dev, G, U, ws, topk, xp, ldx_bytes, h, s);
+    }
+  });
 }
 
 hipError_t launch_moe_combine(const int32_t* ids, int E, const float* gate_w,

@@ -104,15 +104,22 @@ def test_q4_0_pack_roundtrip_and_layout(L, M, K):
     assert np.array_equal(q8.unpack_q4_0_host(qs, dd, M, K), blocks)
 
 
-def test_q4_0_validation(L):
-    W = _mat(K=256, ld_qs=128)
-    assert L.q8_gemv_q4_0(ctypes.byref(W), X, 1, Y, 2, 1, None) in (0, -6)  # valid shape
-    assert L.q8_gemv_q4_0(ctypes.byref(_mat(K=256, ld_qs=112)), X, 1, Y, 2, 1, None) == -2
-    assert L.q8_gemv_q4_0(ctypes.byref(_mat(K=256, ld_qs=136)), X, 1, Y, 2, 1, None) == -3
-    assert L.q8_gemv_q4_0(ctypes.byref(W), 0, 1, Y, 2, 1, None) == -1
-    assert L.q8_gemv_q4_0(ctypes.byref(W), X, 1, Y, 2, 0, None) == -2
-    assert L.q8_gemv_q4_0(ctypes.byref(W), X, 9, Y, 2, 1, None) == -4
-    assert L.q8_gemv_q4_0(ctypes.byref(W), X, 1, X + 64, 2, 1, None) == -8
+def test_format_validation(L):
+    """The format field selects the row layout check; unknown formats and
+    mixed formats in one call are rejected before any device work."""
+    def m(fmt, **kw):
+        w = _mat(**kw)
+        w.format = fmt
+        return w
+    q4 = m(1, K=256, ld_qs=128)
+    assert L.q8_gemv(ctypes.byref(q4), X, 1, Y, 2, 1, None) in (0, -6)  # a valid Q4_0 shape
+    assert L.q8_gemv(ctypes.byref(m(1, K=256, ld_qs=112)), X, 1, Y, 2, 1, None) == -2
+    assert L.q8_gemv(ctypes.byref(m(0, K=256, ld_qs=128)), X, 1, Y, 2, 1, None) == -2  # Q8 needs K
+    assert L.q8_gemv(ctypes.byref(m(1, K=256, ld_qs=136)), X, 1, Y, 2, 1, None) == -3
+    assert L.q8_gemv(ctypes.byref(m(2)), X, 1, Y, 2, 1, None) == -4
+    assert L.q8_gemv_pair(ctypes.byref(_mat()), ctypes.byref(m(1)), X, 1, Y, Y + 4096, 2, 1,
+                          None) == -4
+    assert L.q8_gemv_pair_silu(ctypes.byref(_mat()), ctypes.byref(m(1)), X, 1, Y, 2, 1, None) == -4
     assert L.q8_pack_q4_0_layout(4, 48, None, None, None, None) == -2
 
 

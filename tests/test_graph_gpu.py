@@ -65,7 +65,7 @@ def test_gemv_pair_silu_q4_in_one_graph():
         q8.gemv(Wa, x, out=y)
         q8.gemv_pair(Wa, Wb, x, out_a=ya, out_b=yb)
         q8.gemv_pair_silu(Wa, Wb, x, out=h)
-        q8.gemv_q4_0(W4, x, out=y4)
+        q8.gemv(W4, x, out=y4)
 
     step()
     torch.cuda.synchronize()
