@@ -94,9 +94,12 @@ struct LmEpi {
   template <int NT, int R, int CNT_>
   __device__ __forceinline__ void emit(int64_t rbase, int base, bool owner, const float* v) {
     static_assert(CNT_ == CNT, "slot count");
-    my_base = base;
-    my_owner = owner;
+    // Ownership and base depend only on the lane's position; a call with
+    // owner false (a lane that owns nothing, or a group past the end)
+    // leaves them and the running best as they are.
     if (!owner) return;
+    my_base = base;
+    my_owner = true;
 #pragma unroll
     for (int i = 0; i < CNT; ++i) {
       const int idx = base + i;
@@ -132,7 +135,7 @@ __global__ __launch_bounds__(kBlock) void lmhead_kernel(LmMap map, float* logits
   epi.V = map.V;
   epi.init();
   const int64_t n_groups = (map.V + G - 1) / G;
-  const int wave = threadIdx.x / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lane = threadIdx.x % kWave;
   auto stage = [=]() {
     const char* rows[NT];

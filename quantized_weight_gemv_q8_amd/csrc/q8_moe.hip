@@ -256,7 +256,7 @@ __device__ __forceinline__ void run_routed(const RowOf& rowof, Epi& epi, const u
   constexpr int P = ChunkPlanes<F, XF32>::P;
   constexpr int S = kWavesPerBlock;  // waves of the workgroup take groups in turn
 
-  const int wave = threadIdx.x / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lane = threadIdx.x & (kWave - 1);
   const int p = lane % LPR;
   const int team = lane / LPR;
