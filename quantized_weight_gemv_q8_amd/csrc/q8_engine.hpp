@@ -43,6 +43,7 @@ typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
 constexpr int kWave = 64;
 constexpr int kBlock = 512;  // threads per workgroup for every row kernel
 constexpr int kWavesPerBlock = kBlock / kWave;
+constexpr int kOnceMaxBlock = 1024;  // largest workgroup of the one-group-per-wave kernels
 constexpr int kMaxNT = 8;    // tokens per pass
 
 __device__ __forceinline__ float half_bits_to_float(uint16_t b) {

@@ -8,6 +8,7 @@
 // row and the token count picks the rows per team).
 #include <map>
 #include <mutex>
+#include <tuple>
 #include <utility>
 
 #include "q8_engine.hpp"
@@ -81,22 +82,23 @@ __global__ __launch_bounds__(kBlock) void gemv_kernel(DenseMap map, DenseEpi epi
                                             (int64_t)gridDim.x * kWavesPerBlock, 0, stage);
 }
 
-// One token, at most one row group per wave, C = CPL * LPR: run_once.
+// One token, at most one row group per wave, C = CPL * LPR: run_once. The
+// workgroup size is chosen per launch (once_waves), up to 16 waves.
 template <int F, int LPR, bool XF32, int CPL>
-__global__ __launch_bounds__(kBlock) void gemv_once_kernel(DenseMap map, DenseEpi epi,
-                                                           const char* x, int C) {
+__global__ __launch_bounds__(kOnceMaxBlock) void gemv_once_kernel(DenseMap map, DenseEpi epi,
+                                                                  const char* x, int C) {
   extern __shared__ uint4 lds_x[];
   constexpr int G = kWave / LPR;
   const int64_t n_groups = (map.Mtot + G - 1) / G;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int waves = __builtin_amdgcn_readfirstlane(blockDim.x / kWave);
   auto stage = [=]() {
     const char* rows[1] = {x};
     stage_fmt<F, 1, XF32>(rows, C, lds_x);
     __syncthreads();
   };
   run_once<1, LPR, 1, CPL, (CPL < kOnceDepth ? CPL : kOnceDepth), 1, XF32, F>(
-      map, epi, lds_x, C, n_groups, (int64_t)blockIdx.x * kWavesPerBlock + wave, 0,
-      map.Mtot - 1, stage);
+      map, epi, lds_x, C, n_groups, (int64_t)blockIdx.x * waves + wave, 0, map.Mtot - 1, stage);
 }
 
 // ---------------------------------------------------------------- gate/up + SiLU
@@ -180,7 +182,7 @@ static hipError_t glu_launch_t(const DevInfo& dev, GluMap map, GluEpi epi, const
                                        (int)lds);
     if (e != hipSuccess) return e;
   }
-  int64_t blocks = (int64_t)dev.cus * blocks_per_cu((const void*)fn, lds);
+  int64_t blocks = (int64_t)dev.cus * blocks_per_cu((const void*)fn, lds, kBlock);
   if (blocks > need) blocks = need;
   if (blocks < 1) blocks = 1;
   void* args[] = {&map, &epi, (void*)&x, &ldx_bytes, &C};
@@ -244,7 +246,7 @@ static hipError_t launch_t(const DevInfo& dev, DenseMap map, DenseEpi epi, const
                                        (int)lds);
     if (e != hipSuccess) return e;
   }
-  int64_t blocks = (int64_t)dev.cus * blocks_per_cu((const void*)fn, lds);
+  int64_t blocks = (int64_t)dev.cus * blocks_per_cu((const void*)fn, lds, kBlock);
   if (blocks > need) blocks = need;
   if (blocks < 1) blocks = 1;
   void* args[] = {&map, &epi, (void*)&x, &ldx_bytes, &C};
@@ -269,10 +271,38 @@ static hipError_t launch_sz(const DevInfo& dev, DenseMap map, DenseEpi epi, cons
   return launch_t<F, NT, LPR, XF32, 0>(dev, map, epi, x, ldx_bytes, C, s);
 }
 
+// Waves per workgroup for a one-group-per-wave launch of n_groups waves:
+// among the sizes whose workgroups are all resident at once, the one that
+// spreads the waves most evenly over the compute units, then one with a
+// thread per 16-byte piece of x (a single staging round), then the smallest.
+// Measured on MI355X, 5120 x 5120 at N = 1 (5120 waves, 640 pieces of x):
+// 8 waves 6.67 us (640 workgroups, 2 or 3 per CU), 10 waves 6.35 us (512
+// workgroups, 2 per CU, one piece per thread), 5 waves 6.56 us.
+static int once_waves(const DevInfo& dev, const void* fn, int64_t n_groups, int pieces,
+                      size_t lds) {
+  static const int kSizes[] = {4, 5, 8, 10, 16};
+  int best = 0;
+  double best_eff = 0.0;
+  bool best_fit = false;
+  for (int w : kSizes) {
+    const int64_t blocks = (n_groups + w - 1) / w;
+    const int64_t per_cu = (blocks + dev.cus - 1) / dev.cus;
+    if (per_cu > blocks_per_cu(fn, lds, w * kWave)) continue;
+    const double eff = (double)n_groups / ((double)dev.cus * (double)per_cu * w);
+    const bool fit = w * kWave >= pieces;
+    if (best == 0 || eff > best_eff + 1e-9 || (eff > best_eff - 1e-9 && fit && !best_fit)) {
+      best = w;
+      best_eff = eff;
+      best_fit = fit;
+    }
+  }
+  return best;
+}
+
 // The one-group-per-wave launch for N = 1 when the row groups fit in the
 // resident waves and C is a whole number of lane steps with an instantiated
 // count; hipErrorNotSupported when it does not apply (the caller then takes
-// the persistent launch). Measured on MI355X, 5120 x 5120: 7.6 -> 6.7 us.
+// the persistent launch). Measured on MI355X, 5120 x 5120: 7.6 -> 6.4 us.
 template <int F, int LPR, bool XF32, int CPL>
 static hipError_t once_launch_t(const DevInfo& dev, DenseMap map, DenseEpi epi, const char* x,
                                 int C, hipStream_t s) {
@@ -285,10 +315,11 @@ static hipError_t once_launch_t(const DevInfo& dev, DenseMap map, DenseEpi epi, 
     if (e != hipSuccess) return e;
   }
   const int64_t n_groups = (map.Mtot + G - 1) / G;
-  const int64_t blocks = (n_groups + kWavesPerBlock - 1) / kWavesPerBlock;
-  if (blocks > (int64_t)dev.cus * blocks_per_cu((const void*)fn, lds)) return hipErrorNotSupported;
+  const int w = once_waves(dev, (const void*)fn, n_groups, C * ChunkPlanes<F, XF32>::P, lds);
+  if (w == 0) return hipErrorNotSupported;
+  const int64_t blocks = (n_groups + w - 1) / w;
   void* args[] = {&map, &epi, (void*)&x, &C};
-  return hipLaunchKernel((const void*)fn, dim3((unsigned)blocks), dim3(kBlock), args, lds, s);
+  return hipLaunchKernel((const void*)fn, dim3((unsigned)blocks), dim3(w * kWave), args, lds, s);
 }
 
 template <int F, int LPR, bool XF32>
@@ -326,15 +357,15 @@ static hipError_t launch_nt(const DevInfo& dev, int nt, DenseMap map, DenseEpi e
   return hipErrorInvalidValue;
 }
 
-int blocks_per_cu(const void* fn, size_t lds) {
+int blocks_per_cu(const void* fn, size_t lds, int threads) {
   static std::mutex mu;
-  static std::map<std::pair<const void*, size_t>, int> cache;
+  static std::map<std::tuple<const void*, size_t, int>, int> cache;
   std::lock_guard<std::mutex> lock(mu);
-  auto key = std::make_pair(fn, lds);
+  auto key = std::make_tuple(fn, lds, threads);
   auto it = cache.find(key);
   if (it != cache.end()) return it->second;
   int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, kBlock, lds) != hipSuccess || n < 1) n = 1;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, threads, lds) != hipSuccess || n < 1) n = 1;
   cache[key] = n;
   return n;
 }

@@ -56,9 +56,10 @@ inline hipError_t dispatch_chunks(int fmt, int lpr, bool x_f32, Fn&& fn) {
 }
 
 // Resident workgroups of kernel `fn` per compute unit at `lds` bytes of
-// dynamic LDS (kBlock threads), from the runtime's occupancy calculator;
-// cached per (kernel, lds). Persistent grids launch cus * this many blocks.
-int blocks_per_cu(const void* fn, size_t lds);
+// dynamic LDS and `threads` threads per workgroup, from the runtime's
+// occupancy calculator; cached per (kernel, lds, threads). Persistent grids
+// launch cus * this many blocks.
+int blocks_per_cu(const void* fn, size_t lds, int threads);
 
 // LDS bytes for x of one pass of nt tokens of K activations.
 inline size_t x_lds_bytes(int nt, int64_t K, bool x_f32) {

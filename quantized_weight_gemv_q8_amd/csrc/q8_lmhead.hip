@@ -226,7 +226,7 @@ static hipError_t lm_launch_t(const DevInfo& dev, LmMap map, float* logits, int6
   }
   const int64_t n_groups = (map.V + G - 1) / G;
   const int64_t need = (n_groups + kWavesPerBlock - 1) / kWavesPerBlock;
-  int64_t blocks = (int64_t)dev.cus * blocks_per_cu((const void*)fn, lds);
+  int64_t blocks = (int64_t)dev.cus * blocks_per_cu((const void*)fn, lds, kBlock);
   if (blocks > need) blocks = need;
   if (blocks > kLmMaxBlocks) blocks = kLmMaxBlocks;
   if (blocks < 1) blocks = 1;

@@ -552,7 +552,7 @@ static hipError_t moe_launch(Fn fn, size_t lds, void** args, hipStream_t s, cons
                                        (int)lds);
     if (e != hipSuccess) return e;
   }
-  const int64_t blocks = (int64_t)dev.cus * blocks_per_cu((const void*)fn, lds);
+  const int64_t blocks = (int64_t)dev.cus * blocks_per_cu((const void*)fn, lds, kBlock);
   return hipLaunchKernel((const void*)fn, dim3((unsigned)(blocks > 0 ? blocks : 1)), dim3(kBlock),
                          args, lds, s);
 }
