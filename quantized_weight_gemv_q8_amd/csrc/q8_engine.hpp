@@ -652,8 +652,6 @@ __device__ __forceinline__ void run_rows(const Map& map, Epi& epi, const uint4* 
 // every wave) and emits nothing. Per (row, token) the arithmetic is that of
 // run_rows: the same chunk order per lane, the same fma and the same
 // reduction tree, so results are bitwise those of run_rows.
-constexpr int kOnceDepth = 3;  // chunks in flight per lane (1, 2, 3 within 2% on MI355X)
-
 template <int NT, int LPR, int R, int CPL, int D, int MINC, bool XF32, int F, class Map, class Epi,
           class Stage>
 __device__ __forceinline__ void run_once(const Map& map, Epi& epi, const uint4* lds, int C,

@@ -82,6 +82,15 @@ __global__ __launch_bounds__(kBlock) void gemv_kernel(DenseMap map, DenseEpi epi
                                             (int64_t)gridDim.x * kWavesPerBlock, 0, stage);
 }
 
+// Chunks in flight per lane for run_once: all of them up to three, two up
+// to seven, four from eight. Measured on MI355X at N = 1 (us, windows of
+// 1 / 2 / up to 4 chunks): 5120 x 5120 (5 chunks per lane) 6.91 / 6.60 /
+// 7.38; 8192 x 4096 (4) 7.77 / 7.77 / 8.08; 2048 x 768 (3) 3.33 / 3.36 /
+// 3.01; 1024 x 16384 (16) 8.24 / 8.07 / 6.71. A runtime choice between
+// windows (three copies of the loop in one kernel) cost up to 9% on small
+// shapes, so the window follows the chunk count alone.
+constexpr int once_depth(int cpl) { return cpl <= 3 ? cpl : cpl < 8 ? 2 : 4; }
+
 // One token, at most one row group per wave, C = CPL * LPR: run_once. The
 // workgroup size is chosen per launch (once_waves), up to 16 waves.
 template <int F, int LPR, bool XF32, int CPL>
@@ -97,9 +106,11 @@ __global__ __launch_bounds__(kOnceMaxBlock) void gemv_once_kernel(DenseMap map, 
     stage_fmt<F, 1, XF32>(rows, C, lds_x);
     __syncthreads();
   };
-  run_once<1, LPR, 1, CPL, (CPL < kOnceDepth ? CPL : kOnceDepth), 1, XF32, F>(
-      map, epi, lds_x, C, n_groups, (int64_t)blockIdx.x * waves + wave, 0, map.Mtot - 1, stage);
+  const int64_t g = (int64_t)blockIdx.x * waves + wave;
+  run_once<1, LPR, 1, CPL, once_depth(CPL), 1, XF32, F>(map, epi, lds_x, C, n_groups, g, 0,
+                                                         map.Mtot - 1, stage);
 }
+
 
 // ---------------------------------------------------------------- gate/up + SiLU
 // The gate and up rows of output rho are virtual rows 2*rho and 2*rho + 1,
@@ -271,29 +282,27 @@ static hipError_t launch_sz(const DevInfo& dev, DenseMap map, DenseEpi epi, cons
   return launch_t<F, NT, LPR, XF32, 0>(dev, map, epi, x, ldx_bytes, C, s);
 }
 
-// Waves per workgroup for a one-group-per-wave launch of n_groups waves:
-// among the sizes whose workgroups are all resident at once, the one that
-// spreads the waves most evenly over the compute units, then one with a
-// thread per 16-byte piece of x (a single staging round), then the smallest.
-// Measured on MI355X, 5120 x 5120 at N = 1 (5120 waves, 640 pieces of x):
-// 8 waves 6.67 us (640 workgroups, 2 or 3 per CU), 10 waves 6.35 us (512
-// workgroups, 2 per CU, one piece per thread), 5 waves 6.56 us.
-static int once_waves(const DevInfo& dev, const void* fn, int64_t n_groups, int pieces,
-                      size_t lds) {
-  static const int kSizes[] = {4, 5, 8, 10, 16};
+// Waves per workgroup for a one-group-per-wave launch of n_groups waves: 8,
+// unless the launch gives the compute units at least 8 waves each and
+// another resident size spreads them more evenly (the first in the order
+// 10, 16, 5, 4 among the most even). Measured on MI355X at N = 1 (us,
+// sweeps of 4, 5, 8, 10 and 16 waves): 5120 x 5120 10 waves 6.60 against 8
+// waves 6.86 (640 workgroups, 2 or 3 per CU); with fewer waves per CU
+// larger workgroups win, e.g. 1024 x 16384 8 waves 6.71 against 4 waves
+// 7.43 (each workgroup stages all of x).
+static int once_waves(const DevInfo& dev, const void* fn, int64_t n_groups, size_t lds) {
+  static const int kSizes[] = {8, 10, 16, 5, 4};
+  const bool spread = n_groups >= 8 * (int64_t)dev.cus;
   int best = 0;
   double best_eff = 0.0;
-  bool best_fit = false;
   for (int w : kSizes) {
     const int64_t blocks = (n_groups + w - 1) / w;
     const int64_t per_cu = (blocks + dev.cus - 1) / dev.cus;
     if (per_cu > blocks_per_cu(fn, lds, w * kWave)) continue;
     const double eff = (double)n_groups / ((double)dev.cus * (double)per_cu * w);
-    const bool fit = w * kWave >= pieces;
-    if (best == 0 || eff > best_eff + 1e-9 || (eff > best_eff - 1e-9 && fit && !best_fit)) {
+    if (best == 0 || (spread && eff > best_eff + 1e-9)) {
       best = w;
       best_eff = eff;
-      best_fit = fit;
     }
   }
   return best;
@@ -315,7 +324,7 @@ static hipError_t once_launch_t(const DevInfo& dev, DenseMap map, DenseEpi epi, 
     if (e != hipSuccess) return e;
   }
   const int64_t n_groups = (map.Mtot + G - 1) / G;
-  const int w = once_waves(dev, (const void*)fn, n_groups, C * ChunkPlanes<F, XF32>::P, lds);
+  const int w = once_waves(dev, (const void*)fn, n_groups, lds);
   if (w == 0) return hipErrorNotSupported;
   const int64_t blocks = (n_groups + w - 1) / w;
   void* args[] = {&map, &epi, (void*)&x, &C};
@@ -341,7 +350,7 @@ static hipError_t launch_nt(const DevInfo& dev, int nt, DenseMap map, DenseEpi e
                             int64_t ldx_bytes, int C, hipStream_t s) {
   switch (nt) {
     case 1:
-      if constexpr (LPR >= 32) {
+      {
         const hipError_t e = once_launch<F, LPR, XF32>(dev, map, epi, x, C, s);
         if (e != hipErrorNotSupported) return e;
       }
