@@ -1,0 +1,104 @@
+"""The one-token GEMV launch in which every wave owns one row group.
+
+At N = 1, when the row groups fit in the resident waves and a row is a
+whole number of lane steps, q8_gemv runs a kernel whose chunk loop is
+fixed at compile time. Its arithmetic per (row, token) is the persistent
+engine's, so its output must be bitwise equal to token 0 of an N = 2 call
+(which takes the persistent engine) and within 1e-3 * sum|d*q*x| of the
+fp64 oracle. Shapes cover 16-, 32- and 64-lane rows, 1 to 16 chunks per
+lane, row counts that leave the last row group partly empty, Q4_0, fp32
+activations, fp16 outputs, the two-matrix pair, and canary bands.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import quantized_weight_gemv_q8_amd as q8
+from quantized_weight_gemv_q8_amd import synth
+from tests.gpu_util import assert_parity, dev, host, note, require_gpu, threads, torch, upload
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+# (M, K): lanes per row and chunks per lane in the comments (Q8_0: C = K/16)
+SHAPES = [
+    (1001, 768),   # 16 lanes, 3 chunks, 4 rows per wave, last group 1 row
+    (333, 1536),   # 32 lanes, 3 chunks, 2 rows per wave, last group 1 row
+    (5119, 5120),  # 64 lanes, 5 chunks
+    (77, 1024),    # 64 lanes, 1 chunk
+    (250, 2048),   # 2 chunks
+    (130, 7168),   # 7 chunks
+    (64, 8192),    # 8 chunks
+    (40, 16384),   # 16 chunks
+    (513, 3584),   # 32 lanes, 7 chunks
+    (96, 2560),    # 32 lanes, 5 chunks
+]
+
+
+def check(W, q, d, x, what):
+    y1 = host(q8.gemv(W, dev(x[:1])))
+    y2 = host(q8.gemv(W, dev(x[:2])))
+    assert np.array_equal(y1[0].view(np.uint32), y2[0].view(np.uint32)), f"{what}: N=1 vs N=2"
+    ref, A = oracle.gemv(q, d, x[:1], threads())
+    assert_parity(y1, ref, A, what=what)
+
+
+@pytest.mark.parametrize("M,K", SHAPES)
+def test_q8_shapes_match_engine_and_oracle(M, K):
+    note(f"single-group q8 M={M} K={K}")
+    c = synth.gemv_case(M, K, 2, seed=M * 7 + K)
+    check(upload(c.q, c.d), c.q, c.d, c.x, f"{M}x{K}")
+
+
+@pytest.mark.parametrize("M,K", [(1001, 5120), (300, 2048), (45, 4096)])
+def test_q4_shapes_match_engine_and_oracle(M, K):
+    note(f"single-group q4 M={M} K={K}")
+    c = synth.q4_0_case(M, K, 2, seed=M + K)
+    W = q8.pack_q4_0(synth.to_gguf_q4_0_blocks(c.q, c.d))
+    check(W, c.q, c.d, c.x, f"q4 {M}x{K}")
+
+
+def test_fp32_activations_and_fp16_output():
+    note("single-group fp32 x / fp16 y")
+    c = synth.gemv_case(333, 1536, 2, seed=5)
+    W = upload(c.q, c.d)
+    x32 = c.x.astype(np.float32)
+    check(W, c.q, c.d, x32, "fp32 x")
+    y16 = host(q8.gemv(W, dev(c.x[:1]), out_dtype=torch.float16))
+    ref, A = oracle.gemv(c.q, c.d, c.x[:1], threads())
+    assert_parity(y16.astype(np.float64), ref, A, out_dtype="f16", what="fp16 y")
+
+
+def test_pair_rows_of_both_matrices():
+    note("single-group pair")
+    rng = np.random.default_rng(9)
+    qa, da = synth.draw_weights(rng, 301, 2048)
+    qb, db = synth.draw_weights(rng, 77, 2048)
+    x = synth.draw_x(rng, 2, 2048)
+    Wa, Wb = upload(qa, da), upload(qb, db)
+    ya, yb = (host(t) for t in q8.gemv_pair(Wa, Wb, dev(x[:1])))
+    ya2, yb2 = (host(t) for t in q8.gemv_pair(Wa, Wb, dev(x)))
+    assert np.array_equal(ya[0].view(np.uint32), ya2[0].view(np.uint32))
+    assert np.array_equal(yb[0].view(np.uint32), yb2[0].view(np.uint32))
+    for q, d, y in ((qa, da, ya), (qb, db, yb)):
+        ref, A = oracle.gemv(q, d, x[:1], threads())
+        assert_parity(y, ref, A, what="pair")
+
+
+@pytest.mark.parametrize("M,K", [(1001, 768), (5119, 5120), (333, 1536)])
+def test_canary_bands(M, K):
+    """Rows past the end are read from the last row and never written."""
+    note(f"single-group canary M={M} K={K}")
+    c = synth.gemv_case(M, K, 1, seed=3)
+    W = upload(c.q, c.d)
+    buf = torch.full((M + 4096,), float("nan"), device="cuda")
+    y = buf[2048:2048 + M].view(1, M)
+    q8.gemv(W, dev(c.x), out=y)
+    b = host(buf)
+    assert np.all(np.isnan(b[:2048])) and np.all(np.isnan(b[2048 + M:]))
+    assert not np.any(np.isnan(b[2048:2048 + M]))
