@@ -145,6 +145,13 @@ struct Fmt<kFmtQ4> {
   static constexpr int kScaleShift = 0;
 };
 
+// 16-byte pieces of one row's scales (8 fp16 per piece; a scale row is
+// read in whole pieces, which the 8-element row alignment of the scale
+// plane keeps in bounds).
+__host__ __device__ constexpr int row_scale_pieces(int fmt, int C) {
+  return ((fmt == kFmtQ4 ? C : C / 2) + 7) / 8;
+}
+
 // 16-byte pieces of x per chunk in the LDS image.
 template <int F, bool XF32>
 struct ChunkPlanes {
@@ -652,15 +659,27 @@ __device__ __forceinline__ void run_rows(const Map& map, Epi& epi, const uint4* 
 // every wave) and emits nothing. Per (row, token) the arithmetic is that of
 // run_rows: the same chunk order per lane, the same fma and the same
 // reduction tree, so results are bitwise those of run_rows.
+//
+// Scales: the team fetches each of its rows' whole scale row with 16-byte
+// loads (once_scale_pieces pieces, lane p takes pieces p, p + LPR, ...),
+// issued before the first weight load, and writes it after stage() to the
+// wave's own LDS area lds_s + wave * G * pieces (no barrier: only this wave
+// reads it); every chunk then reads its scale from LDS. One or two loads
+// per row instead of one 2-byte load per chunk. lds_s holds
+// waves-per-workgroup * G * once_scale_pieces(F, CPL * LPR) pieces.
 template <int NT, int LPR, int R, int CPL, int D, int MINC, bool XF32, int F, class Map, class Epi,
           class Stage>
-__device__ __forceinline__ void run_once(const Map& map, Epi& epi, const uint4* lds, int C,
-                                         int64_t n_groups, int64_t g, int64_t row_origin,
-                                         int64_t last_row, Stage&& stage, int nt = NT) {
+__device__ __forceinline__ void run_once(const Map& map, Epi& epi, const uint4* lds,
+                                         uint4* lds_s, int64_t n_groups, int64_t g,
+                                         int64_t row_origin, int64_t last_row, Stage&& stage,
+                                         int nt = NT) {
   constexpr int RPW = kWave / LPR;
   constexpr int G = RPW * R;
   constexpr int V = NT * R;
   constexpr int VP = Pow2<V>::value;
+  constexpr int C = CPL * LPR;
+  constexpr int SP = row_scale_pieces(F, C);  // 16-byte pieces of a scale row
+  constexpr int NSP = (SP + LPR - 1) / LPR;   // of them per lane
   using Shape = ReduceShape<LPR, VP, MINC>;
   static_assert(D >= 1 && D <= CPL, "window within the row");
 
@@ -675,25 +694,44 @@ __device__ __forceinline__ void run_once(const Map& map, Epi& epi, const uint4* 
     const int64_t i = rbase + r;
     map.row(i < last_row ? i : last_row, q[r], d[r]);
   }
+  // Scale rows: unconditional loads, lanes past the last piece re-read it
+  // (same line, no extra traffic).
+  uint4 srow[R][NSP];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int k = 0; k < NSP; ++k) {
+      const int piece = p + LPR * k;
+      srow[r][k] = load_stream16(reinterpret_cast<const int8_t*>(d[r]) +
+                                 16 * (piece < SP ? piece : SP - 1));
+    }
   Slot<R> slot[D];
   auto issue = [&](Slot<R>& sl, int j) {
     const int c = p + LPR * j;
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      sl.q[r] = load_stream16(q[r] + (int64_t)c * 16);
-      sl.d[r] = d[r][c >> Fmt<F>::kScaleShift];
-    }
+    for (int r = 0; r < R; ++r) sl.q[r] = load_stream16(q[r] + (int64_t)c * 16);
   };
 #pragma unroll
   for (int s = 0; s < D; ++s) issue(slot[s], s);
   stage();
+  uint4* const srow_lds = lds_s + ((int)(threadIdx.x / kWave) * G + team * R) * SP;
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int k = 0; k < NSP; ++k)
+      if (p + LPR * k < SP) srow_lds[r * SP + p + LPR * k] = srow[r][k];
 
   float acc[VP];
 #pragma unroll
   for (int i = 0; i < VP; ++i) acc[i] = 0.0f;
 #pragma unroll
   for (int j = 0; j < CPL; ++j) {
-    chunk_fma<F, NT, R, XF32>(slot[j % D].q, slot[j % D].d, lds, C, p + LPR * j, nt, acc);
+    const int c = p + LPR * j;
+    uint32_t dd[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      dd[r] = reinterpret_cast<const uint16_t*>(srow_lds + r * SP)[c >> Fmt<F>::kScaleShift];
+    chunk_fma<F, NT, R, XF32>(slot[j % D].q, dd, lds, C, c, nt, acc);
     if (j + D < CPL) issue(slot[j % D], j + D);
   }
   // Reduced and emitted without a branch on g: a wave-uniform early exit

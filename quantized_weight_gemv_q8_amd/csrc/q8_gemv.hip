@@ -6,6 +6,7 @@
 // reused from LDS for all rows (memra wiki, feature list: Q8_0 decode
 // matvecs with per-shape auto-dispatch; here the shape picks the lanes per
 // row and the token count picks the rows per team).
+#include <algorithm>
 #include <map>
 #include <mutex>
 #include <tuple>
@@ -107,8 +108,9 @@ __global__ __launch_bounds__(kOnceMaxBlock) void gemv_once_kernel(DenseMap map, 
     __syncthreads();
   };
   const int64_t g = (int64_t)blockIdx.x * waves + wave;
-  run_once<1, LPR, 1, CPL, once_depth(CPL), 1, XF32, F>(map, epi, lds_x, C, n_groups, g, 0,
-                                                         map.Mtot - 1, stage);
+  run_once<1, LPR, 1, CPL, once_depth(CPL), 1, XF32, F>(
+      map, epi, lds_x, lds_x + CPL * LPR * ChunkPlanes<F, XF32>::P, n_groups, g, 0, map.Mtot - 1,
+      stage);
 }
 
 
@@ -290,7 +292,9 @@ static hipError_t launch_sz(const DevInfo& dev, DenseMap map, DenseEpi epi, cons
 // waves 6.86 (640 workgroups, 2 or 3 per CU); with fewer waves per CU
 // larger workgroups win, e.g. 1024 x 16384 8 waves 6.71 against 4 waves
 // 7.43 (each workgroup stages all of x).
-static int once_waves(const DevInfo& dev, const void* fn, int64_t n_groups, size_t lds) {
+// LDS per workgroup: lds_fixed plus lds_per_wave for each wave.
+static int once_waves(const DevInfo& dev, const void* fn, int64_t n_groups, size_t lds_fixed,
+                      size_t lds_per_wave) {
   static const int kSizes[] = {8, 10, 16, 5, 4};
   const bool spread = n_groups >= 8 * (int64_t)dev.cus;
   int best = 0;
@@ -298,7 +302,8 @@ static int once_waves(const DevInfo& dev, const void* fn, int64_t n_groups, size
   for (int w : kSizes) {
     const int64_t blocks = (n_groups + w - 1) / w;
     const int64_t per_cu = (blocks + dev.cus - 1) / dev.cus;
-    if (per_cu > blocks_per_cu(fn, lds, w * kWave)) continue;
+    const size_t lds = lds_fixed + (size_t)w * lds_per_wave;
+    if (lds > dev.lds_per_block || per_cu > blocks_per_cu(fn, lds, w * kWave)) continue;
     const double eff = (double)n_groups / ((double)dev.cus * (double)per_cu * w);
     if (best == 0 || (spread && eff > best_eff + 1e-9)) {
       best = w;
@@ -316,16 +321,19 @@ template <int F, int LPR, bool XF32, int CPL>
 static hipError_t once_launch_t(const DevInfo& dev, DenseMap map, DenseEpi epi, const char* x,
                                 int C, hipStream_t s) {
   constexpr int G = kWave / LPR;
-  const size_t lds = (size_t)C * 16 * ChunkPlanes<F, XF32>::P;
+  const size_t lds_x = (size_t)C * 16 * ChunkPlanes<F, XF32>::P;
+  const size_t lds_wave = (size_t)G * row_scale_pieces(F, C) * 16;  // a wave's scale rows
   auto fn = gemv_once_kernel<F, LPR, XF32, CPL>;
-  if (lds > 64 * 1024) {
+  if (lds_x + kOnceMaxBlock / kWave * lds_wave > 64 * 1024) {
+    const size_t most = std::min(lds_x + kOnceMaxBlock / kWave * lds_wave, dev.lds_per_block);
     hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)lds);
+                                       (int)most);
     if (e != hipSuccess) return e;
   }
   const int64_t n_groups = (map.Mtot + G - 1) / G;
-  const int w = once_waves(dev, (const void*)fn, n_groups, lds);
+  const int w = once_waves(dev, (const void*)fn, n_groups, lds_x, lds_wave);
   if (w == 0) return hipErrorNotSupported;
+  const size_t lds = lds_x + (size_t)w * lds_wave;
   const int64_t blocks = (n_groups + w - 1) / w;
   void* args[] = {&map, &epi, (void*)&x, &C};
   return hipLaunchKernel((const void*)fn, dim3((unsigned)blocks), dim3(w * kWave), args, lds, s);
