@@ -193,21 +193,20 @@ __device__ __forceinline__ float dot32_f16(const h2_t q[16], const uint4 xs[4]) 
   return s;
 }
 
-// fp32 activations: nibble - 8 as fp32 (exact), then an FMA chain in K order.
-__device__ __forceinline__ float dot32_f32(const uint4 q, const uint4 x[8]) {
+// fp32 activations: nibble - 8 as fp32 (exact), then an FMA chain in K
+// order. One half of a Q4_0 block: elements 16*half .. 16*half + 15 (the
+// low nibbles for half 0, the high ones for half 1) against x[0..3], the
+// chain continuing from s.
+__device__ __forceinline__ float dot16_f32_q4(const uint4 q, const uint4 x[4], int half, float s) {
   const unsigned w[4] = {q.x, q.y, q.z, q.w};
-  float s = 0.0f;
 #pragma unroll
-  for (int half = 0; half < 2; ++half) {
+  for (int i = 0; i < 4; ++i) {
+    const float4 xv = __builtin_bit_cast(float4, x[i]);
+    const float xe[4] = {xv.x, xv.y, xv.z, xv.w};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float4 xv = __builtin_bit_cast(float4, x[half * 4 + i]);
-      const float xe[4] = {xv.x, xv.y, xv.z, xv.w};
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const int nib = (int)((w[i] >> (8 * b + 4 * half)) & 0xFu) - 8;
-        s = __builtin_fmaf((float)nib, xe[b], s);
-      }
+    for (int b = 0; b < 4; ++b) {
+      const int nib = (int)((w[i] >> (8 * b + 4 * half)) & 0xFu) - 8;
+      s = __builtin_fmaf((float)nib, xe[b], s);
     }
   }
   return s;
@@ -271,17 +270,31 @@ __device__ __forceinline__ void chunk_fma(const uint4* q, const uint32_t* d, con
       }
     }
   } else {
+    // Half a block (16 activations) of a token at a time, each (row, token)
+    // chain carried across the halves: the same FMA order as one pass over
+    // the block, with a quarter of the activation registers live.
+    float sum[NT][R];
+#pragma unroll
+    for (int n = 0; n < NT; ++n)
+#pragma unroll
+      for (int r = 0; r < R; ++r) sum[n][r] = 0.0f;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+#pragma unroll
+      for (int n = 0; n < NT; ++n) {
+        if (n >= nt) break;
+        uint4 xv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) xv[i] = xb[(n * P + 4 * half + i) * C + c];
+#pragma unroll
+        for (int r = 0; r < R; ++r) sum[n][r] = dot16_f32_q4(q[r], xv, half, sum[n][r]);
+      }
+    }
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
       if (n >= nt) break;
-      uint4 xv[8];
 #pragma unroll
-      for (int h = 0; h < 8; ++h) xv[h] = xb[(n * P + h) * C + c];
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const float sum = dot32_f32(q[r], xv);
-        acc[n * R + r] = __builtin_fmaf(df[r], sum, acc[n * R + r]);
-      }
+      for (int r = 0; r < R; ++r) acc[n * R + r] = __builtin_fmaf(df[r], sum[n][r], acc[n * R + r]);
     }
   }
 }

@@ -414,12 +414,11 @@ __device__ __forceinline__ void routed_slices(const MoeWs& ws, const RowOf& rowo
 
 // Occupancy request: 6 waves per SIMD (80 VGPRs) for Q8_0 with fp16
 // activations, which the kernels meet without spilling (measured faster
-// than the 5 waves the allocator picks unasked); 4 for the heavier fp32
-// or Q4_0 variants; none for Q4_0 with fp32 activations, which needs more
-// than 128 VGPRs.
+// than the 5 waves the allocator picks unasked); 4 (128 VGPRs) for the
+// heavier fp32 or Q4_0 variants.
 template <int F, bool XF32>
 constexpr int moe_waves() {
-  return (XF32 && F == kFmtQ4) ? 1 : (XF32 || F == kFmtQ4) ? 4 : 6;
+  return (XF32 || F == kFmtQ4) ? 4 : 6;
 }
 
 template <int F, int LPR, bool XF32>
