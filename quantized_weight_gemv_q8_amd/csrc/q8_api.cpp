@@ -445,9 +445,8 @@ int q8_moe_gemv(const q8_bank* W, const int32_t* expert_ids, const float* gate_w
   q8::MoeWs w = moe_ws_ptrs(ws, W->E, T, topk, 0, M);
   float* yp = gate_w ? w.y_pair : y;
   hipStream_t s = (hipStream_t)stream;
-  if (q8::launch_moe_route(expert_ids, W->E, P, w, gate_w ? nullptr : y, M, s) != hipSuccess)
-    return Q8_ERR_LAUNCH;
-  if (q8::launch_moe_gemv(*dev, to_hb(W), w, topk, x, xf, x_per_pair != 0, yp, s) !=
+  const q8::RouteReq route{expert_ids, W->E, P, gate_w ? nullptr : y, M};
+  if (q8::launch_moe_gemv(*dev, to_hb(W), w, topk, x, xf, x_per_pair != 0, yp, route, s) !=
       hipSuccess)
     return Q8_ERR_LAUNCH;
   if (gate_w)
@@ -488,11 +487,12 @@ int q8_moe_ffn(const q8_bank* gate, const q8_bank* up, const q8_bank* down,
   const int P = T * topk;
   q8::MoeWs w = moe_ws_ptrs(ws, E, T, topk, F, H);
   hipStream_t s = (hipStream_t)stream;
-  if (q8::launch_moe_route(expert_ids, E, P, w, nullptr, 0, s) != hipSuccess) return Q8_ERR_LAUNCH;
-  if (q8::launch_moe_gate_up(*dev, to_hb(gate), to_hb(up), w, topk, x, xf, w.h, s) !=
+  const q8::RouteReq route{expert_ids, E, P, nullptr, 0};
+  const q8::RouteReq routed{nullptr, E, P, nullptr, 0};  // the workspace holds it by then
+  if (q8::launch_moe_gate_up(*dev, to_hb(gate), to_hb(up), w, topk, x, xf, w.h, route, s) !=
       hipSuccess)
     return Q8_ERR_LAUNCH;
-  if (q8::launch_moe_gemv(*dev, to_hb(down), w, topk, w.h, true, true, w.y_pair, s) !=
+  if (q8::launch_moe_gemv(*dev, to_hb(down), w, topk, w.h, true, true, w.y_pair, routed, s) !=
       hipSuccess)
     return Q8_ERR_LAUNCH;
   return launch_rc(q8::launch_moe_combine(expert_ids, E, gate_w, w.y_pair, out, T, topk, H, s));

@@ -105,15 +105,26 @@ bool moe_fits(const DevInfo& dev, int64_t K, bool x_f32);
 
 hipError_t launch_moe_route(const int32_t* ids, int E, int P, const MoeWs& ws, float* zero_rows,
                             int64_t zero_ld, hipStream_t s);
+// The routing a routed launch needs first: ids null when the workspace
+// already holds it (a later kernel of the same layer); otherwise the
+// launch routes (inside the kernel when its LDS has room, else with a
+// separate route launch before it) and zeroes the zero_rows rows of pairs
+// with out-of-range expert ids.
+struct RouteReq {
+  const int32_t* ids;
+  int E, P;
+  float* zero_rows;
+  int64_t zero_ld;
+};
 // Routed GEMV over a bank: y_pair[p] = W[e_p] x[src(p)]; src(p) = p / topk
 // (x_per_pair false) or p. x fp16 or fp32.
 hipError_t launch_moe_gemv(const DevInfo& dev, const HBank& W, const MoeWs& ws, int topk,
                            const void* x, bool x_f32, bool x_per_pair, float* y_pair,
-                           hipStream_t s);
+                           const RouteReq& rq, hipStream_t s);
 // h[p] = silu(Wg[e_p] x_t) * (Wu[e_p] x_t), x fp16 [T][H].
 hipError_t launch_moe_gate_up(const DevInfo& dev, const HBank& G, const HBank& U,
                               const MoeWs& ws, int topk, const void* x, bool x_f32, float* h,
-                              hipStream_t s);
+                              const RouteReq& rq, hipStream_t s);
 // h[n][m] = silu(G x_n)[m] * (U x_n)[m]; G, U of one shape; h fp32 or fp16.
 hipError_t launch_glu(const DevInfo& dev, const HMat& G, const HMat& U, const void* x,
                       bool x_f32, void* h, bool h_f16, int nt, hipStream_t s);
