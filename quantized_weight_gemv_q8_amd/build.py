@@ -20,7 +20,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libq8gemv.so")
 
-SOURCES = ["q8_api.cpp", "q8_gemv.hip", "q8_lmhead.hip", "q8_moe.hip", "q8_router.hip"]
+SOURCES = ["q8_api.cpp", "q8_gemv.hip", "q8_lmhead.hip", "q8_moe.hip", "q8_router.hip",
+           "q8_once1.hip", "q8_once2.hip", "q8_once3.hip", "q8_once4.hip"]
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 COMMON = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-function",
           "-I", INCLUDE, "-I", CSRC]
@@ -47,7 +48,7 @@ def _compile(src: str) -> str:
 
 def build(verbose: bool = False) -> str:
     """Compile every source and link the shared library; returns its path."""
-    with cf.ThreadPoolExecutor(max_workers=min(6, len(SOURCES))) as ex:
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB + ".tmp"
     cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]

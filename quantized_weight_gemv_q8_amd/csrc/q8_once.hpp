@@ -1,0 +1,136 @@
+// q8_once.hpp -- the dense GEMV with one row group per wave (run_once) for
+// passes of 1 to 4 tokens: kernels, their launch shape and the launcher.
+// Each q8_once<N>.hip instantiates it for N tokens (separate translation
+// units so the build compiles them in parallel).
+#pragma once
+#include <algorithm>
+
+#include "q8_dense.h"
+#include "q8_engine.hpp"
+#include "q8_internal.h"
+
+namespace q8 {
+
+// Chunks in flight per lane for run_once: all of them up to three, two up
+// to seven, four from eight. Measured on MI355X at N = 1 (us, windows of
+// 1 / 2 / up to 4 chunks): 5120 x 5120 (5 chunks per lane) 6.91 / 6.60 /
+// 7.38; 8192 x 4096 (4) 7.77 / 7.77 / 8.08; 2048 x 768 (3) 3.33 / 3.36 /
+// 3.01; 1024 x 16384 (16) 8.24 / 8.07 / 6.71. A runtime choice between
+// windows (three copies of the loop in one kernel) cost up to 9% on small
+// shapes, so the window follows the chunk count alone.
+constexpr int once_depth(int cpl) { return cpl <= 3 ? cpl : cpl < 8 ? 2 : 4; }
+
+// NT tokens, at most one row group per wave, C = CPL * LPR: run_once. The
+// workgroup size is chosen per launch (once_waves), up to 16 waves.
+template <int F, int NT, int LPR, bool XF32, int CPL>
+__global__ __launch_bounds__(kOnceMaxBlock) void gemv_once_kernel(DenseMap map, DenseEpi epi,
+                                                                  const char* x,
+                                                                  int64_t ldx_bytes, int C) {
+  extern __shared__ uint4 lds_x[];
+  constexpr int G = kWave / LPR;
+  const int64_t n_groups = (map.Mtot + G - 1) / G;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int waves = __builtin_amdgcn_readfirstlane(blockDim.x / kWave);
+  auto stage = [=]() {
+    const char* rows[NT];
+#pragma unroll
+    for (int n = 0; n < NT; ++n) rows[n] = x + n * ldx_bytes;
+    stage_fmt<F, NT, XF32>(rows, C, lds_x);
+    __syncthreads();
+  };
+  const int64_t g = (int64_t)blockIdx.x * waves + wave;
+  run_once<NT, LPR, 1, CPL, once_depth(CPL), 1, XF32, F>(
+      map, epi, lds_x, lds_x + NT * CPL * LPR * ChunkPlanes<F, XF32>::P, n_groups, g, 0,
+      map.Mtot - 1, stage);
+}
+
+
+// Waves per workgroup for a one-group-per-wave launch of n_groups waves: 8,
+// unless the launch gives the compute units at least 8 waves each and
+// another resident size spreads them more evenly (the first in the order
+// 10, 16, 5, 4 among the most even). Measured on MI355X at N = 1 (us,
+// sweeps of 4, 5, 8, 10 and 16 waves): 5120 x 5120 10 waves 6.60 against 8
+// waves 6.86 (640 workgroups, 2 or 3 per CU); with fewer waves per CU
+// larger workgroups win, e.g. 1024 x 16384 8 waves 6.71 against 4 waves
+// 7.43 (each workgroup stages all of x).
+// LDS per workgroup: lds_fixed plus lds_per_wave for each wave.
+static int once_waves(const DevInfo& dev, const void* fn, int64_t n_groups, size_t lds_fixed,
+                      size_t lds_per_wave) {
+  static const int kSizes[] = {8, 10, 16, 5, 4};
+  const bool spread = n_groups >= 8 * (int64_t)dev.cus;
+  int best = 0;
+  double best_eff = 0.0;
+  for (int w : kSizes) {
+    const int64_t blocks = (n_groups + w - 1) / w;
+    const int64_t per_cu = (blocks + dev.cus - 1) / dev.cus;
+    const size_t lds = lds_fixed + (size_t)w * lds_per_wave;
+    if (lds > dev.lds_per_block || per_cu > blocks_per_cu(fn, lds, w * kWave)) continue;
+    const double eff = (double)n_groups / ((double)dev.cus * (double)per_cu * w);
+    if (best == 0 || (spread && eff > best_eff + 1e-9)) {
+      best = w;
+      best_eff = eff;
+    }
+  }
+  return best;
+}
+
+// The one-group-per-wave launch for N = 1 when the row groups fit in the
+// resident waves and C is a whole number of lane steps with an instantiated
+// count; hipErrorNotSupported when it does not apply (the caller then takes
+// the persistent launch). Measured on MI355X, 5120 x 5120: 7.6 -> 6.4 us.
+template <int F, int NT, int LPR, bool XF32, int CPL>
+static hipError_t once_launch_t(const DevInfo& dev, DenseMap map, DenseEpi epi, const char* x,
+                                int64_t ldx_bytes, int C, hipStream_t s) {
+  constexpr int G = kWave / LPR;
+  const size_t lds_x = (size_t)NT * C * 16 * ChunkPlanes<F, XF32>::P;
+  const size_t lds_wave = (size_t)G * row_scale_pieces(F, C) * 16;  // a wave's scale rows
+  auto fn = gemv_once_kernel<F, NT, LPR, XF32, CPL>;
+  if (lds_x + kOnceMaxBlock / kWave * lds_wave > 64 * 1024) {
+    const size_t most = std::min(lds_x + kOnceMaxBlock / kWave * lds_wave, dev.lds_per_block);
+    hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)most);
+    if (e != hipSuccess) return e;
+  }
+  const int64_t n_groups = (map.Mtot + G - 1) / G;
+  const int w = once_waves(dev, (const void*)fn, n_groups, lds_x, lds_wave);
+  if (w == 0) return hipErrorNotSupported;
+  const size_t lds = lds_x + (size_t)w * lds_wave;
+  const int64_t blocks = (n_groups + w - 1) / w;
+  void* args[] = {&map, &epi, (void*)&x, &ldx_bytes, &C};
+  return hipLaunchKernel((const void*)fn, dim3((unsigned)blocks), dim3(w * kWave), args, lds, s);
+}
+
+template <int F, int NT, int LPR, bool XF32>
+static hipError_t once_launch(const DevInfo& dev, DenseMap map, DenseEpi epi, const char* x,
+                              int64_t ldx_bytes, int C, hipStream_t s) {
+  if (C % LPR != 0) return hipErrorNotSupported;
+  switch (C / LPR) {
+#define Q8_ONCE(N) \
+  case N: return once_launch_t<F, NT, LPR, XF32, N>(dev, map, epi, x, ldx_bytes, C, s);
+    Q8_ONCE(1) Q8_ONCE(2) Q8_ONCE(3) Q8_ONCE(4) Q8_ONCE(5) Q8_ONCE(6) Q8_ONCE(7) Q8_ONCE(8)
+    Q8_ONCE(10) Q8_ONCE(12) Q8_ONCE(14) Q8_ONCE(16)
+#undef Q8_ONCE
+  }
+  return hipErrorNotSupported;
+}
+
+template <int NT>
+hipError_t launch_once_nt(const DevInfo& dev, const DenseMap& map, const DenseEpi& epi, int fmt,
+                          int lpr, bool x_f32, const char* x, int64_t ldx_bytes, int C,
+                          hipStream_t s) {
+  return dispatch_chunks(fmt, lpr, x_f32, [&](auto f, auto l, auto xf) {
+    return once_launch<decltype(f)::value, NT, decltype(l)::value, decltype(xf)::value>(
+        dev, map, epi, x, ldx_bytes, C, s);
+  });
+}
+
+hipError_t launch_once_nt1(const DevInfo&, const DenseMap&, const DenseEpi&, int, int, bool,
+                          const char*, int64_t, int, hipStream_t);
+hipError_t launch_once_nt2(const DevInfo&, const DenseMap&, const DenseEpi&, int, int, bool,
+                          const char*, int64_t, int, hipStream_t);
+hipError_t launch_once_nt3(const DevInfo&, const DenseMap&, const DenseEpi&, int, int, bool,
+                          const char*, int64_t, int, hipStream_t);
+hipError_t launch_once_nt4(const DevInfo&, const DenseMap&, const DenseEpi&, int, int, bool,
+                          const char*, int64_t, int, hipStream_t);
+
+}  // namespace q8

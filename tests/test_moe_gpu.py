@@ -161,3 +161,20 @@ def test_invalid_ids_are_skipped():
     e = int(ids[1, 0])
     ref, A = oracle.gemv(c.q_gate[e], c.d_gate[e], c.x[1:2])
     assert_parity(yp[2:3], ref, A, what="valid slot next to invalid one")
+
+
+def test_many_experts_route_in_its_own_launch():
+    """With 4096 experts and 4096 pairs the route's LDS does not fit next to
+    the activations, so it runs as a separate launch before the routed
+    kernels; the results and the workspace must be the same as ever."""
+    note("moe E=4096 T=512 separate route launch")
+    c = synth.moe_case(E=4096, F=32, H=128, T=512, topk=8, seed=21)
+    stagewise(c, banks(c))
+    W = upload_bank(c.q_gate, c.d_gate)
+    ids = c.expert_ids.copy()
+    ids[7, 3] = -1
+    yp = host(q8.moe_gemv(W, dev(ids), dev(c.x)))
+    assert np.all(yp[7 * 8 + 3] == 0)
+    e = int(ids[7, 2])
+    ref, A = oracle.gemv(c.q_gate[e], c.d_gate[e], c.x[7:8])
+    assert_parity(yp[7 * 8 + 2:7 * 8 + 3], ref, A, what="valid slot next to invalid one")

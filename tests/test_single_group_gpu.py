@@ -1,11 +1,11 @@
-"""The one-token GEMV launch in which every wave owns one row group.
+"""The GEMV launch in which every wave owns one row group.
 
-At N = 1, when the row groups fit in the resident waves and a row is a
-whole number of lane steps, q8_gemv runs a kernel whose chunk loop is
-fixed at compile time. Its arithmetic per (row, token) is the persistent
-engine's, so its output must be bitwise equal to token 0 of an N = 2 call
-(which takes the persistent engine) and within 1e-3 * sum|d*q*x| of the
-fp64 oracle. Shapes cover 16-, 32- and 64-lane rows, 1 to 16 chunks per
+For passes of 1 to 4 tokens, when the row groups fit in the resident
+waves and a row is a whole number of lane steps, q8_gemv runs a kernel
+whose chunk loop is fixed at compile time. Its arithmetic per (row, token)
+is the persistent engine's, so its outputs for N = 1..4 must be bitwise
+equal to the first tokens of an N = 5 call (which takes the persistent
+engine) and within 1e-3 * sum|d*q*x| of the fp64 oracle. Shapes cover 16-, 32- and 64-lane rows, 1 to 16 chunks per
 lane, row counts that leave the last row group partly empty, Q4_0, fp32
 activations, fp16 outputs, the two-matrix pair, and canary bands.
 """
@@ -41,31 +41,32 @@ SHAPES = [
 
 
 def check(W, q, d, x, what):
-    y1 = host(q8.gemv(W, dev(x[:1])))
-    y2 = host(q8.gemv(W, dev(x[:2])))
-    assert np.array_equal(y1[0].view(np.uint32), y2[0].view(np.uint32)), f"{what}: N=1 vs N=2"
-    ref, A = oracle.gemv(q, d, x[:1], threads())
-    assert_parity(y1, ref, A, what=what)
+    y5 = host(q8.gemv(W, dev(x[:5])))
+    for n in (1, 2, 3, 4):
+        yn = host(q8.gemv(W, dev(x[:n])))
+        assert np.array_equal(yn.view(np.uint32), y5[:n].view(np.uint32)), f"{what}: N={n} vs N=5"
+    ref, A = oracle.gemv(q, d, x[:4], threads())
+    assert_parity(y5[:4], ref, A, what=what)
 
 
 @pytest.mark.parametrize("M,K", SHAPES)
 def test_q8_shapes_match_engine_and_oracle(M, K):
     note(f"single-group q8 M={M} K={K}")
-    c = synth.gemv_case(M, K, 2, seed=M * 7 + K)
+    c = synth.gemv_case(M, K, 5, seed=M * 7 + K)
     check(upload(c.q, c.d), c.q, c.d, c.x, f"{M}x{K}")
 
 
 @pytest.mark.parametrize("M,K", [(1001, 5120), (300, 2048), (45, 4096)])
 def test_q4_shapes_match_engine_and_oracle(M, K):
     note(f"single-group q4 M={M} K={K}")
-    c = synth.q4_0_case(M, K, 2, seed=M + K)
+    c = synth.q4_0_case(M, K, 5, seed=M + K)
     W = q8.pack_q4_0(synth.to_gguf_q4_0_blocks(c.q, c.d))
     check(W, c.q, c.d, c.x, f"q4 {M}x{K}")
 
 
 def test_fp32_activations_and_fp16_output():
     note("single-group fp32 x / fp16 y")
-    c = synth.gemv_case(333, 1536, 2, seed=5)
+    c = synth.gemv_case(333, 1536, 5, seed=5)
     W = upload(c.q, c.d)
     x32 = c.x.astype(np.float32)
     check(W, c.q, c.d, x32, "fp32 x")
@@ -79,14 +80,15 @@ def test_pair_rows_of_both_matrices():
     rng = np.random.default_rng(9)
     qa, da = synth.draw_weights(rng, 301, 2048)
     qb, db = synth.draw_weights(rng, 77, 2048)
-    x = synth.draw_x(rng, 2, 2048)
+    x = synth.draw_x(rng, 5, 2048)
     Wa, Wb = upload(qa, da), upload(qb, db)
-    ya, yb = (host(t) for t in q8.gemv_pair(Wa, Wb, dev(x[:1])))
-    ya2, yb2 = (host(t) for t in q8.gemv_pair(Wa, Wb, dev(x)))
-    assert np.array_equal(ya[0].view(np.uint32), ya2[0].view(np.uint32))
-    assert np.array_equal(yb[0].view(np.uint32), yb2[0].view(np.uint32))
-    for q, d, y in ((qa, da, ya), (qb, db, yb)):
-        ref, A = oracle.gemv(q, d, x[:1], threads())
+    ya5, yb5 = (host(t) for t in q8.gemv_pair(Wa, Wb, dev(x)))
+    for n in (1, 3):
+        ya, yb = (host(t) for t in q8.gemv_pair(Wa, Wb, dev(x[:n])))
+        assert np.array_equal(ya.view(np.uint32), ya5[:n].view(np.uint32))
+        assert np.array_equal(yb.view(np.uint32), yb5[:n].view(np.uint32))
+    for q, d, y in ((qa, da, ya5), (qb, db, yb5)):
+        ref, A = oracle.gemv(q, d, x, threads())
         assert_parity(y, ref, A, what="pair")
 
 
@@ -94,11 +96,11 @@ def test_pair_rows_of_both_matrices():
 def test_canary_bands(M, K):
     """Rows past the end are read from the last row and never written."""
     note(f"single-group canary M={M} K={K}")
-    c = synth.gemv_case(M, K, 1, seed=3)
+    c = synth.gemv_case(M, K, 3, seed=3)
     W = upload(c.q, c.d)
-    buf = torch.full((M + 4096,), float("nan"), device="cuda")
-    y = buf[2048:2048 + M].view(1, M)
+    buf = torch.full((3 * M + 4096,), float("nan"), device="cuda")
+    y = buf[2048:2048 + 3 * M].view(3, M)
     q8.gemv(W, dev(c.x), out=y)
     b = host(buf)
-    assert np.all(np.isnan(b[:2048])) and np.all(np.isnan(b[2048 + M:]))
-    assert not np.any(np.isnan(b[2048:2048 + M]))
+    assert np.all(np.isnan(b[:2048])) and np.all(np.isnan(b[2048 + 3 * M:]))
+    assert not np.any(np.isnan(b[2048:2048 + 3 * M]))
