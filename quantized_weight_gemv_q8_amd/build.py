@@ -21,7 +21,8 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libq8gemv.so")
 
 SOURCES = ["q8_api.cpp", "q8_gemv.hip", "q8_lmhead.hip", "q8_moe.hip", "q8_router.hip",
-           "q8_once1.hip", "q8_once2.hip", "q8_once3.hip", "q8_once4.hip"]
+           "q8_once1.hip", "q8_once2.hip", "q8_once3.hip", "q8_once4.hip", "q8_once5.hip",
+           "q8_once6.hip", "q8_once7.hip", "q8_once8.hip"]
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 COMMON = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-function",
           "-I", INCLUDE, "-I", CSRC]

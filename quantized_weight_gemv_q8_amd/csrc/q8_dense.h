@@ -55,7 +55,7 @@ struct DenseEpi {
   }
 };
 
-// One-group-per-wave launch of a dense pass of nt = 1..4 tokens (weight
+// One-group-per-wave launch of a dense pass of nt = 1..8 tokens (weight
 // format fmt, lpr lanes per row): hipErrorNotSupported when it does not
 // apply (the row groups do not fit in the resident waves, or the chunks per
 // lane are not an instantiated count); the caller then takes the

@@ -236,10 +236,30 @@ static hipError_t launch_nt(const DevInfo& dev, int nt, DenseMap map, DenseEpi e
         if (e != hipErrorNotSupported) return e;
       }
       return launch_sz<F, 4, LPR, XF32>(dev, map, epi, x, ldx_bytes, C, s);
-    case 5: return launch_sz<F, 5, LPR, XF32>(dev, map, epi, x, ldx_bytes, C, s);
-    case 6: return launch_sz<F, 6, LPR, XF32>(dev, map, epi, x, ldx_bytes, C, s);
-    case 7: return launch_sz<F, 7, LPR, XF32>(dev, map, epi, x, ldx_bytes, C, s);
-    case 8: return launch_sz<F, 8, LPR, XF32>(dev, map, epi, x, ldx_bytes, C, s);
+    case 5:
+      {
+        const hipError_t e = launch_gemv_once(5, dev, map, epi, F, LPR, XF32, x, ldx_bytes, C, s);
+        if (e != hipErrorNotSupported) return e;
+      }
+      return launch_sz<F, 5, LPR, XF32>(dev, map, epi, x, ldx_bytes, C, s);
+    case 6:
+      {
+        const hipError_t e = launch_gemv_once(6, dev, map, epi, F, LPR, XF32, x, ldx_bytes, C, s);
+        if (e != hipErrorNotSupported) return e;
+      }
+      return launch_sz<F, 6, LPR, XF32>(dev, map, epi, x, ldx_bytes, C, s);
+    case 7:
+      {
+        const hipError_t e = launch_gemv_once(7, dev, map, epi, F, LPR, XF32, x, ldx_bytes, C, s);
+        if (e != hipErrorNotSupported) return e;
+      }
+      return launch_sz<F, 7, LPR, XF32>(dev, map, epi, x, ldx_bytes, C, s);
+    case 8:
+      {
+        const hipError_t e = launch_gemv_once(8, dev, map, epi, F, LPR, XF32, x, ldx_bytes, C, s);
+        if (e != hipErrorNotSupported) return e;
+      }
+      return launch_sz<F, 8, LPR, XF32>(dev, map, epi, x, ldx_bytes, C, s);
   }
   return hipErrorInvalidValue;
 }

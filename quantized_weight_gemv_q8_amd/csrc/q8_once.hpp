@@ -1,5 +1,5 @@
 // q8_once.hpp -- the dense GEMV with one row group per wave (run_once) for
-// passes of 1 to 4 tokens: kernels, their launch shape and the launcher.
+// passes of 1 to 8 tokens: kernels, their launch shape and the launcher.
 // Each q8_once<N>.hip instantiates it for N tokens (separate translation
 // units so the build compiles them in parallel).
 #pragma once
@@ -20,6 +20,11 @@ namespace q8 {
 // shapes, so the window follows the chunk count alone.
 constexpr int once_depth(int cpl) { return cpl <= 3 ? cpl : cpl < 8 ? 2 : 4; }
 
+// Rows per team: one up to 4 tokens; two from 5, which halves the groups
+// (so that 5120 rows fit in the waves the larger x image leaves resident)
+// and shares each LDS read of x between two rows.
+constexpr int once_rows(int nt) { return nt <= 4 ? 1 : 2; }
+
 // NT tokens, at most one row group per wave, C = CPL * LPR: run_once. The
 // workgroup size is chosen per launch (once_waves), up to 16 waves.
 template <int F, int NT, int LPR, bool XF32, int CPL>
@@ -27,7 +32,7 @@ __global__ __launch_bounds__(kOnceMaxBlock) void gemv_once_kernel(DenseMap map, 
                                                                   const char* x,
                                                                   int64_t ldx_bytes, int C) {
   extern __shared__ uint4 lds_x[];
-  constexpr int G = kWave / LPR;
+  constexpr int G = kWave / LPR * once_rows(NT);
   const int64_t n_groups = (map.Mtot + G - 1) / G;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int waves = __builtin_amdgcn_readfirstlane(blockDim.x / kWave);
@@ -39,7 +44,7 @@ __global__ __launch_bounds__(kOnceMaxBlock) void gemv_once_kernel(DenseMap map, 
     __syncthreads();
   };
   const int64_t g = (int64_t)blockIdx.x * waves + wave;
-  run_once<NT, LPR, 1, CPL, once_depth(CPL), 1, XF32, F>(
+  run_once<NT, LPR, once_rows(NT), CPL, once_depth(CPL), 1, XF32, F>(
       map, epi, lds_x, lds_x + NT * CPL * LPR * ChunkPlanes<F, XF32>::P, n_groups, g, 0,
       map.Mtot - 1, stage);
 }
@@ -81,7 +86,7 @@ static int once_waves(const DevInfo& dev, const void* fn, int64_t n_groups, size
 template <int F, int NT, int LPR, bool XF32, int CPL>
 static hipError_t once_launch_t(const DevInfo& dev, DenseMap map, DenseEpi epi, const char* x,
                                 int64_t ldx_bytes, int C, hipStream_t s) {
-  constexpr int G = kWave / LPR;
+  constexpr int G = kWave / LPR * once_rows(NT);
   const size_t lds_x = (size_t)NT * C * 16 * ChunkPlanes<F, XF32>::P;
   const size_t lds_wave = (size_t)G * row_scale_pieces(F, C) * 16;  // a wave's scale rows
   auto fn = gemv_once_kernel<F, NT, LPR, XF32, CPL>;
@@ -131,6 +136,14 @@ hipError_t launch_once_nt2(const DevInfo&, const DenseMap&, const DenseEpi&, int
 hipError_t launch_once_nt3(const DevInfo&, const DenseMap&, const DenseEpi&, int, int, bool,
                           const char*, int64_t, int, hipStream_t);
 hipError_t launch_once_nt4(const DevInfo&, const DenseMap&, const DenseEpi&, int, int, bool,
+                          const char*, int64_t, int, hipStream_t);
+hipError_t launch_once_nt5(const DevInfo&, const DenseMap&, const DenseEpi&, int, int, bool,
+                          const char*, int64_t, int, hipStream_t);
+hipError_t launch_once_nt6(const DevInfo&, const DenseMap&, const DenseEpi&, int, int, bool,
+                          const char*, int64_t, int, hipStream_t);
+hipError_t launch_once_nt7(const DevInfo&, const DenseMap&, const DenseEpi&, int, int, bool,
+                          const char*, int64_t, int, hipStream_t);
+hipError_t launch_once_nt8(const DevInfo&, const DenseMap&, const DenseEpi&, int, int, bool,
                           const char*, int64_t, int, hipStream_t);
 
 }  // namespace q8
