@@ -57,9 +57,9 @@ struct DenseEpi {
 
 // One-group-per-wave launch of a dense pass of nt = 1..8 tokens (weight
 // format fmt, lpr lanes per row): hipErrorNotSupported when it does not
-// apply (the row groups do not fit in the resident waves, or the chunks per
-// lane are not an instantiated count); the caller then takes the
-// persistent launch.
+// apply (the chunks per lane are not an instantiated count, or, for more
+// than 2 tokens, the row groups do not fit in the resident waves); the
+// caller then takes the persistent launch.
 hipError_t launch_gemv_once(int nt, const DevInfo& dev, const DenseMap& map, const DenseEpi& epi,
                             int fmt, int lpr, bool x_f32, const char* x, int64_t ldx_bytes, int C,
                             hipStream_t s);

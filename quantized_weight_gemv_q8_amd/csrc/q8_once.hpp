@@ -58,9 +58,16 @@ __global__ __launch_bounds__(kOnceMaxBlock) void gemv_once_kernel(DenseMap map, 
 // waves 6.86 (640 workgroups, 2 or 3 per CU); with fewer waves per CU
 // larger workgroups win, e.g. 1024 x 16384 8 waves 6.71 against 4 waves
 // 7.43 (each workgroup stages all of x).
-// LDS per workgroup: lds_fixed plus lds_per_wave for each wave.
+// LDS per workgroup: lds_fixed plus lds_per_wave for each wave. With
+// stream set, a launch whose groups do not all fit in the resident waves
+// still takes this kernel with 8-wave workgroups, the hardware starting
+// workgroups as others finish (0 otherwise: the caller takes the
+// persistent launch). Measured on MI355X, one-group against persistent:
+// 34816 x 5120 N = 1 30.3 -> 28.7 us, N = 2 36.5 -> 32.1; 102400 x 5120
+// N = 1 87.5 -> 77.9; but N = 4 38.8 -> 43.0 and N = 8 57.2 -> 73.8 (each
+// workgroup stages x again), so only passes of 1 or 2 tokens stream.
 static int once_waves(const DevInfo& dev, const void* fn, int64_t n_groups, size_t lds_fixed,
-                      size_t lds_per_wave) {
+                      size_t lds_per_wave, bool stream) {
   static const int kSizes[] = {8, 10, 16, 5, 4};
   const bool spread = n_groups >= 8 * (int64_t)dev.cus;
   int best = 0;
@@ -76,6 +83,7 @@ static int once_waves(const DevInfo& dev, const void* fn, int64_t n_groups, size
       best_eff = eff;
     }
   }
+  if (best == 0 && stream && lds_fixed + 8 * lds_per_wave <= dev.lds_per_block) return 8;
   return best;
 }
 
@@ -97,7 +105,7 @@ static hipError_t once_launch_t(const DevInfo& dev, DenseMap map, DenseEpi epi, 
     if (e != hipSuccess) return e;
   }
   const int64_t n_groups = (map.Mtot + G - 1) / G;
-  const int w = once_waves(dev, (const void*)fn, n_groups, lds_x, lds_wave);
+  const int w = once_waves(dev, (const void*)fn, n_groups, lds_x, lds_wave, NT <= 2);
   if (w == 0) return hipErrorNotSupported;
   const size_t lds = lds_x + (size_t)w * lds_wave;
   const int64_t blocks = (n_groups + w - 1) / w;
