@@ -1,6 +1,6 @@
-// q8_dense.h -- the dense GEMV's row map and epilogue, shared by the
-// persistent kernels (q8_gemv.hip) and the one-group-per-wave kernels
-// (q8_once*.hip).
+// q8_dense.h -- the row maps and epilogues of the dense GEMV and of the
+// gate/up + SiLU pair, shared by the persistent kernels (q8_gemv.hip) and
+// the one-group-per-wave kernels (q8_once*.hip).
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -55,6 +55,48 @@ struct DenseEpi {
   }
 };
 
+// The gate and up rows of output rho are virtual rows 2*rho and 2*rho + 1,
+// so a team (an even number of rows) holds both sums of an output in one
+// lane after the reduction and the MLP activation h = silu(g) * u is
+// applied before anything is stored. Per-row arithmetic is the engine's, so
+// g and u are bitwise those of q8_gemv_pair.
+struct GluMap {
+  const int8_t* qg;
+  const uint16_t* dg;
+  const int8_t* qu;
+  const uint16_t* du;
+  int64_t ldqg, lddg, ldqu, lddu;
+  int64_t M2;  // 2 * M virtual rows
+  __device__ __forceinline__ bool row(int64_t i, const int8_t*& q, const uint16_t*& d) const {
+    const int64_t rho = i >> 1;
+    const bool up = (i & 1) != 0;
+    const int64_t ldq = up ? ldqu : ldqg;
+    const int64_t ldd = up ? lddu : lddg;
+    q = (up ? qu : qg) + rho * ldq;
+    d = (up ? du : dg) + rho * ldd;
+    return i < M2;
+  }
+};
+
+struct GluEpi {
+  char* h;
+  int64_t M;
+  bool f16;
+  template <int NT, int R, int CNT>
+  __device__ __forceinline__ void emit(int64_t rbase, int base, bool owner, const float* v) {
+    static_assert(R % 2 == 0 && CNT == 2, "gate/up pairs");
+    if (!owner || base >= NT * R) return;
+    const int n = base / R, r = base - (base / R) * R;
+    const int64_t row = rbase + r;  // the gate row of the pair (even)
+    if (row >= 2 * M) return;
+    const float g = v[0], u = v[1];
+    const float val = g / (1.0f + expf(-g)) * u;
+    const int64_t o = (int64_t)n * M + (row >> 1);
+    if (f16) reinterpret_cast<_Float16*>(h)[o] = (_Float16)val;
+    else reinterpret_cast<float*>(h)[o] = val;
+  }
+};
+
 // One-group-per-wave launch of a dense pass of nt = 1..8 tokens (weight
 // format fmt, lpr lanes per row): hipErrorNotSupported when it does not
 // apply (the chunks per lane are not an instantiated count, or, for more
@@ -63,5 +105,10 @@ struct DenseEpi {
 hipError_t launch_gemv_once(int nt, const DevInfo& dev, const DenseMap& map, const DenseEpi& epi,
                             int fmt, int lpr, bool x_f32, const char* x, int64_t ldx_bytes, int C,
                             hipStream_t s);
+
+// The same for the gate/up + SiLU pair (2M virtual rows), nt = 1 or 2.
+hipError_t launch_glu_once(int nt, const DevInfo& dev, const GluMap& map, const GluEpi& epi,
+                           int fmt, int lpr, bool x_f32, const char* x, int64_t ldx_bytes, int C,
+                           hipStream_t s);
 
 }  // namespace q8

@@ -39,48 +39,6 @@ __global__ __launch_bounds__(kBlock) void gemv_kernel(DenseMap map, DenseEpi epi
 }
 
 // ---------------------------------------------------------------- gate/up + SiLU
-// The gate and up rows of output rho are virtual rows 2*rho and 2*rho + 1,
-// so a team (an even number of rows) holds both sums of an output in one
-// lane after the reduction and the MLP activation h = silu(g) * u is
-// applied before anything is stored. Per-row arithmetic is the engine's, so
-// g and u are bitwise those of q8_gemv_pair.
-struct GluMap {
-  const int8_t* qg;
-  const uint16_t* dg;
-  const int8_t* qu;
-  const uint16_t* du;
-  int64_t ldqg, lddg, ldqu, lddu;
-  int64_t M2;  // 2 * M virtual rows
-  __device__ __forceinline__ bool row(int64_t i, const int8_t*& q, const uint16_t*& d) const {
-    const int64_t rho = i >> 1;
-    const bool up = (i & 1) != 0;
-    const int64_t ldq = up ? ldqu : ldqg;
-    const int64_t ldd = up ? lddu : lddg;
-    q = (up ? qu : qg) + rho * ldq;
-    d = (up ? du : dg) + rho * ldd;
-    return i < M2;
-  }
-};
-
-struct GluEpi {
-  char* h;
-  int64_t M;
-  bool f16;
-  template <int NT, int R, int CNT>
-  __device__ __forceinline__ void emit(int64_t rbase, int base, bool owner, const float* v) {
-    static_assert(R % 2 == 0 && CNT == 2, "gate/up pairs");
-    if (!owner || base >= NT * R) return;
-    const int n = base / R, r = base - (base / R) * R;
-    const int64_t row = rbase + r;  // the gate row of the pair (even)
-    if (row >= 2 * M) return;
-    const float g = v[0], u = v[1];
-    const float val = g / (1.0f + expf(-g)) * u;
-    const int64_t o = (int64_t)n * M + (row >> 1);
-    if (f16) reinterpret_cast<_Float16*>(h)[o] = (_Float16)val;
-    else reinterpret_cast<float*>(h)[o] = val;
-  }
-};
-
 template <int NT, bool BIG>
 struct GluTune {
   static constexpr int R = Tune<NT, BIG>::R < 2 ? 2 : Tune<NT, BIG>::R;
@@ -164,6 +122,11 @@ hipError_t launch_glu(const DevInfo& dev, const HMat& Gm, const HMat& Um, const 
   const int C = (int)chunks_per_row(Gm.fmt, Gm.K);
   const int64_t ldx_bytes = Gm.K * (x_f32 ? 4 : 2);
   const char* xp = (const char*)x;
+  if (nt <= 2) {
+    const hipError_t e = launch_glu_once(nt, dev, map, epi, Gm.fmt, lanes_for(Gm.fmt, Gm.K), x_f32,
+                                         xp, ldx_bytes, C, s);
+    if (e != hipErrorNotSupported) return e;
+  }
   return dispatch_chunks(Gm.fmt, lanes_for(Gm.fmt, Gm.K), x_f32, [&](auto f, auto l, auto xf) {
     return glu_launch_nt<decltype(f)::value, decltype(l)::value, decltype(xf)::value>(
         dev, nt, map, epi, xp, ldx_bytes, C, s);

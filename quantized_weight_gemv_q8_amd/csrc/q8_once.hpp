@@ -4,6 +4,7 @@
 // units so the build compiles them in parallel).
 #pragma once
 #include <algorithm>
+#include <type_traits>
 
 #include "q8_dense.h"
 #include "q8_engine.hpp"
@@ -25,30 +26,70 @@ constexpr int once_depth(int cpl) { return cpl <= 3 ? cpl : cpl < 8 ? 2 : 4; }
 // and shares each LDS read of x between two rows.
 constexpr int once_rows(int nt) { return nt <= 4 ? 1 : 2; }
 
+// The two kinds of one-group kernels: the dense GEMV (and pair) and the
+// gate/up + SiLU pair, whose teams hold a gate row and its up row (R = 2,
+// both sums reduced into one lane: MINC = 2).
+struct DenseKind {
+  using Map = DenseMap;
+  using Epi = DenseEpi;
+  static constexpr int rows_per_team(int nt) { return once_rows(nt); }
+  static constexpr int kMinc = 1;
+  __host__ __device__ static int64_t rows(const Map& m) { return m.Mtot; }
+};
+struct GluKind {
+  using Map = GluMap;
+  using Epi = GluEpi;
+  static constexpr int rows_per_team(int) { return 2; }
+  static constexpr int kMinc = 2;
+  __host__ __device__ static int64_t rows(const Map& m) { return m.M2; }
+};
+
 // NT tokens, at most one row group per wave, C = CPL * LPR: run_once. The
 // workgroup size is chosen per launch (once_waves), up to 16 waves.
+template <class K, int F, int NT, int LPR, bool XF32, int CPL>
+__device__ __forceinline__ void once_body(const typename K::Map& map, typename K::Epi& epi,
+                                          const char* x, int64_t ldx_bytes, int C) {
+  extern __shared__ uint4 lds_x[];
+  constexpr int R = K::rows_per_team(NT);
+  constexpr int G = kWave / LPR * R;
+  const int64_t rows = K::rows(map);
+  const int64_t n_groups = (rows + G - 1) / G;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int waves = __builtin_amdgcn_readfirstlane(blockDim.x / kWave);
+  auto stage = [=]() {
+    const char* xr[NT];
+#pragma unroll
+    for (int n = 0; n < NT; ++n) xr[n] = x + n * ldx_bytes;
+    stage_fmt<F, NT, XF32>(xr, C, lds_x);
+    __syncthreads();
+  };
+  const int64_t g = (int64_t)blockIdx.x * waves + wave;
+  run_once<NT, LPR, R, CPL, once_depth(CPL), K::kMinc, XF32, F>(
+      map, epi, lds_x, lds_x + NT * CPL * LPR * ChunkPlanes<F, XF32>::P, n_groups, g, 0,
+      rows - 1, stage);
+}
+
 template <int F, int NT, int LPR, bool XF32, int CPL>
 __global__ __launch_bounds__(kOnceMaxBlock) void gemv_once_kernel(DenseMap map, DenseEpi epi,
                                                                   const char* x,
                                                                   int64_t ldx_bytes, int C) {
-  extern __shared__ uint4 lds_x[];
-  constexpr int G = kWave / LPR * once_rows(NT);
-  const int64_t n_groups = (map.Mtot + G - 1) / G;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int waves = __builtin_amdgcn_readfirstlane(blockDim.x / kWave);
-  auto stage = [=]() {
-    const char* rows[NT];
-#pragma unroll
-    for (int n = 0; n < NT; ++n) rows[n] = x + n * ldx_bytes;
-    stage_fmt<F, NT, XF32>(rows, C, lds_x);
-    __syncthreads();
-  };
-  const int64_t g = (int64_t)blockIdx.x * waves + wave;
-  run_once<NT, LPR, once_rows(NT), CPL, once_depth(CPL), 1, XF32, F>(
-      map, epi, lds_x, lds_x + NT * CPL * LPR * ChunkPlanes<F, XF32>::P, n_groups, g, 0,
-      map.Mtot - 1, stage);
+  once_body<DenseKind, F, NT, LPR, XF32, CPL>(map, epi, x, ldx_bytes, C);
 }
 
+template <int F, int NT, int LPR, bool XF32, int CPL>
+__global__ __launch_bounds__(kOnceMaxBlock) void glu_once_kernel(GluMap map, GluEpi epi,
+                                                                 const char* x, int64_t ldx_bytes,
+                                                                 int C) {
+  once_body<GluKind, F, NT, LPR, XF32, CPL>(map, epi, x, ldx_bytes, C);
+}
+
+template <class K, int F, int NT, int LPR, bool XF32, int CPL>
+constexpr const void* once_fn() {
+  if constexpr (std::is_same_v<K, GluKind>)
+    return (const void*)glu_once_kernel<F, NT, LPR, XF32, CPL>;
+  else
+    return (const void*)gemv_once_kernel<F, NT, LPR, XF32, CPL>;
+}
 
 // Waves per workgroup for a one-group-per-wave launch of n_groups waves: 8,
 // unless the launch gives the compute units at least 8 waves each and
@@ -87,39 +128,39 @@ static int once_waves(const DevInfo& dev, const void* fn, int64_t n_groups, size
   return best;
 }
 
-// The one-group-per-wave launch for N = 1 when the row groups fit in the
-// resident waves and C is a whole number of lane steps with an instantiated
-// count; hipErrorNotSupported when it does not apply (the caller then takes
-// the persistent launch). Measured on MI355X, 5120 x 5120: 7.6 -> 6.4 us.
-template <int F, int NT, int LPR, bool XF32, int CPL>
-static hipError_t once_launch_t(const DevInfo& dev, DenseMap map, DenseEpi epi, const char* x,
-                                int64_t ldx_bytes, int C, hipStream_t s) {
-  constexpr int G = kWave / LPR * once_rows(NT);
+// The one-group-per-wave launch when the row groups fit in the resident
+// waves (or stream, for 1-2 tokens) and C is a whole number of lane steps
+// with an instantiated count; hipErrorNotSupported when it does not apply
+// (the caller then takes the persistent launch).
+template <class K, int F, int NT, int LPR, bool XF32, int CPL>
+static hipError_t once_launch_t(const DevInfo& dev, typename K::Map map, typename K::Epi epi,
+                                const char* x, int64_t ldx_bytes, int C, hipStream_t s) {
+  constexpr int G = kWave / LPR * K::rows_per_team(NT);
   const size_t lds_x = (size_t)NT * C * 16 * ChunkPlanes<F, XF32>::P;
   const size_t lds_wave = (size_t)G * row_scale_pieces(F, C) * 16;  // a wave's scale rows
-  auto fn = gemv_once_kernel<F, NT, LPR, XF32, CPL>;
+  const void* fn = once_fn<K, F, NT, LPR, XF32, CPL>();
   if (lds_x + kOnceMaxBlock / kWave * lds_wave > 64 * 1024) {
     const size_t most = std::min(lds_x + kOnceMaxBlock / kWave * lds_wave, dev.lds_per_block);
-    hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)most);
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)most);
     if (e != hipSuccess) return e;
   }
-  const int64_t n_groups = (map.Mtot + G - 1) / G;
-  const int w = once_waves(dev, (const void*)fn, n_groups, lds_x, lds_wave, NT <= 2);
+  const int64_t n_groups = (K::rows(map) + G - 1) / G;
+  const int w = once_waves(dev, fn, n_groups, lds_x, lds_wave, NT <= 2);
   if (w == 0) return hipErrorNotSupported;
   const size_t lds = lds_x + (size_t)w * lds_wave;
   const int64_t blocks = (n_groups + w - 1) / w;
   void* args[] = {&map, &epi, (void*)&x, &ldx_bytes, &C};
-  return hipLaunchKernel((const void*)fn, dim3((unsigned)blocks), dim3(w * kWave), args, lds, s);
+  return hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(w * kWave), args, lds, s);
 }
 
-template <int F, int NT, int LPR, bool XF32>
-static hipError_t once_launch(const DevInfo& dev, DenseMap map, DenseEpi epi, const char* x,
-                              int64_t ldx_bytes, int C, hipStream_t s) {
+template <class K, int F, int NT, int LPR, bool XF32>
+static hipError_t once_launch(const DevInfo& dev, const typename K::Map& map,
+                              const typename K::Epi& epi, const char* x, int64_t ldx_bytes, int C,
+                              hipStream_t s) {
   if (C % LPR != 0) return hipErrorNotSupported;
   switch (C / LPR) {
 #define Q8_ONCE(N) \
-  case N: return once_launch_t<F, NT, LPR, XF32, N>(dev, map, epi, x, ldx_bytes, C, s);
+  case N: return once_launch_t<K, F, NT, LPR, XF32, N>(dev, map, epi, x, ldx_bytes, C, s);
     Q8_ONCE(1) Q8_ONCE(2) Q8_ONCE(3) Q8_ONCE(4) Q8_ONCE(5) Q8_ONCE(6) Q8_ONCE(7) Q8_ONCE(8)
     Q8_ONCE(10) Q8_ONCE(12) Q8_ONCE(14) Q8_ONCE(16)
 #undef Q8_ONCE
@@ -127,12 +168,12 @@ static hipError_t once_launch(const DevInfo& dev, DenseMap map, DenseEpi epi, co
   return hipErrorNotSupported;
 }
 
-template <int NT>
-hipError_t launch_once_nt(const DevInfo& dev, const DenseMap& map, const DenseEpi& epi, int fmt,
-                          int lpr, bool x_f32, const char* x, int64_t ldx_bytes, int C,
-                          hipStream_t s) {
+template <class K, int NT>
+hipError_t launch_once_nt(const DevInfo& dev, const typename K::Map& map,
+                          const typename K::Epi& epi, int fmt, int lpr, bool x_f32, const char* x,
+                          int64_t ldx_bytes, int C, hipStream_t s) {
   return dispatch_chunks(fmt, lpr, x_f32, [&](auto f, auto l, auto xf) {
-    return once_launch<decltype(f)::value, NT, decltype(l)::value, decltype(xf)::value>(
+    return once_launch<K, decltype(f)::value, NT, decltype(l)::value, decltype(xf)::value>(
         dev, map, epi, x, ldx_bytes, C, s);
   });
 }
@@ -153,5 +194,9 @@ hipError_t launch_once_nt7(const DevInfo&, const DenseMap&, const DenseEpi&, int
                           const char*, int64_t, int, hipStream_t);
 hipError_t launch_once_nt8(const DevInfo&, const DenseMap&, const DenseEpi&, int, int, bool,
                           const char*, int64_t, int, hipStream_t);
+hipError_t launch_glu_once_nt1(const DevInfo&, const GluMap&, const GluEpi&, int, int, bool,
+                              const char*, int64_t, int, hipStream_t);
+hipError_t launch_glu_once_nt2(const DevInfo&, const GluMap&, const GluEpi&, int, int, bool,
+                              const char*, int64_t, int, hipStream_t);
 
 }  // namespace q8

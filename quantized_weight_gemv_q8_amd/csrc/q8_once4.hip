@@ -6,7 +6,7 @@ namespace q8 {
 hipError_t launch_once_nt4(const DevInfo& dev, const DenseMap& map, const DenseEpi& epi, int fmt,
                              int lpr, bool x_f32, const char* x, int64_t ldx_bytes, int C,
                              hipStream_t s) {
-  return launch_once_nt<4>(dev, map, epi, fmt, lpr, x_f32, x, ldx_bytes, C, s);
+  return launch_once_nt<DenseKind, 4>(dev, map, epi, fmt, lpr, x_f32, x, ldx_bytes, C, s);
 }
 
 }  // namespace q8
