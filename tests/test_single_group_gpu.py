@@ -104,3 +104,48 @@ def test_canary_bands(M, K):
     b = host(buf)
     assert np.all(np.isnan(b[:2048])) and np.all(np.isnan(b[2048 + 3 * M:]))
     assert not np.any(np.isnan(b[2048:2048 + 3 * M]))
+
+
+# ---------------------------------------------------------------- streaming launches
+# More row groups than resident waves: at 1-2 tokens the one-group kernel is
+# launched over every group anyway (the hardware starts workgroups as others
+# finish); results must equal the persistent launch's (token 0/1 of N = 5).
+def sampled_rows(M, seed):
+    rng = np.random.default_rng(seed)
+    return np.unique(np.concatenate([[0, M - 1], rng.choice(M, 600, replace=False)]))
+
+
+@pytest.mark.parametrize("fmt", ["q8", "q4"])
+def test_streaming_dense(fmt):
+    note(f"streaming dense {fmt}")
+    M, K = 40000, 2048
+    if fmt == "q8":
+        c = synth.gemv_case(M, K, 5, seed=31)
+        W = upload(c.q, c.d)
+    else:
+        c = synth.q4_0_case(M, K, 5, seed=31)
+        W = q8.pack_q4_0(synth.to_gguf_q4_0_blocks(c.q, c.d))
+    y5 = host(q8.gemv(W, dev(c.x)))
+    for n in (1, 2):
+        yn = host(q8.gemv(W, dev(c.x[:n])))
+        assert np.array_equal(yn.view(np.uint32), y5[:n].view(np.uint32)), f"N={n}"
+    rows = sampled_rows(M, 1)
+    ref, A = oracle.gemv_rows(c.q, c.d, c.x[:2], rows, threads())
+    assert_parity(y5[:2, rows], ref, A, what=f"streaming {fmt}")
+
+
+def test_streaming_silu_pair():
+    note("streaming SiLU pair")
+    M, K = 20000, 2048
+    rng = np.random.default_rng(32)
+    qg, dg = synth.draw_weights(rng, M, K)
+    qu, du = synth.draw_weights(rng, M, K)
+    x = synth.draw_x(rng, 5, K)
+    Wg, Wu = upload(qg, dg), upload(qu, du)
+    h5 = host(q8.gemv_pair_silu(Wg, Wu, dev(x)))
+    for n in (1, 2):
+        hn = host(q8.gemv_pair_silu(Wg, Wu, dev(x[:n])))
+        assert np.array_equal(hn.view(np.uint32), h5[:n].view(np.uint32)), f"N={n}"
+    rows = sampled_rows(M, 2)
+    r = oracle.gate_up_silu(qg[rows], dg[rows], qu[rows], du[rows], x[:2], threads())
+    assert np.all(np.abs(h5[:2, rows] - r["h"]) <= r["bh"])
