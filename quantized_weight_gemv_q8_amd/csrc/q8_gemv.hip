@@ -72,11 +72,7 @@ static hipError_t glu_launch_t(const DevInfo& dev, GluMap map, GluEpi epi, const
   const int64_t n_groups = (map.M2 + G - 1) / G;
   const int64_t need = (n_groups + kWavesPerBlock - 1) / kWavesPerBlock;
   auto fn = glu_kernel<F, NT, LPR, XF32, BIG>;
-  if (lds > 64 * 1024) {
-    hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)lds);
-    if (e != hipSuccess) return e;
-  }
+  if (hipError_t e = allow_dynamic_lds((const void*)fn, lds)) return e;
   int64_t blocks = (int64_t)dev.cus * blocks_per_cu((const void*)fn, lds, kBlock);
   if (blocks > need) blocks = need;
   if (blocks < 1) blocks = 1;
@@ -141,11 +137,7 @@ static hipError_t launch_t(const DevInfo& dev, DenseMap map, DenseEpi epi, const
   const int64_t n_groups = (map.Mtot + G - 1) / G;
   const int64_t need = (n_groups + kWavesPerBlock - 1) / kWavesPerBlock;
   auto fn = gemv_kernel<F, NT, LPR, XF32, MODE>;
-  if (lds > 64 * 1024) {
-    hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)lds);
-    if (e != hipSuccess) return e;
-  }
+  if (hipError_t e = allow_dynamic_lds((const void*)fn, lds)) return e;
   int64_t blocks = (int64_t)dev.cus * blocks_per_cu((const void*)fn, lds, kBlock);
   if (blocks > need) blocks = need;
   if (blocks < 1) blocks = 1;
@@ -225,6 +217,22 @@ static hipError_t launch_nt(const DevInfo& dev, int nt, DenseMap map, DenseEpi e
       return launch_sz<F, 8, LPR, XF32>(dev, map, epi, x, ldx_bytes, C, s);
   }
   return hipErrorInvalidValue;
+}
+
+hipError_t allow_dynamic_lds(const void* fn, size_t bytes) {
+  if (bytes <= 64 * 1024) return hipSuccess;
+  int device = 0;
+  if (hipError_t e = hipGetDevice(&device)) return e;
+  static std::mutex mu;
+  static std::map<std::pair<int, const void*>, size_t> raised;  // per device and kernel
+  std::lock_guard<std::mutex> lock(mu);
+  const auto key = std::make_pair(device, fn);
+  auto it = raised.find(key);
+  if (it != raised.end() && it->second >= bytes) return hipSuccess;
+  const hipError_t e =
+      hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  if (e == hipSuccess) raised[key] = bytes;
+  return e;
 }
 
 int blocks_per_cu(const void* fn, size_t lds, int threads) {

@@ -60,6 +60,9 @@ inline hipError_t dispatch_chunks(int fmt, int lpr, bool x_f32, Fn&& fn) {
 // occupancy calculator; cached per (kernel, lds, threads). Persistent grids
 // launch cus * this many blocks.
 int blocks_per_cu(const void* fn, size_t lds, int threads);
+// Lets kernel fn take `bytes` of dynamic LDS (above the default 64 KiB);
+// the attribute is set once per kernel and size, not on every launch.
+hipError_t allow_dynamic_lds(const void* fn, size_t bytes);
 
 // LDS bytes for x of one pass of nt tokens of K activations.
 inline size_t x_lds_bytes(int nt, int64_t K, bool x_f32) {

@@ -61,11 +61,7 @@ static hipError_t lm_launch_t(const DevInfo& dev, LmMap map, float* logits, int6
   constexpr int G = (kWave / LPR) * Tune<NT, BIG>::R;
   const size_t lds = (size_t)NT * C * 16 * ChunkPlanes<F, XF32>::P;
   auto fn = lmhead_kernel<F, NT, LPR, XF32, BIG>;
-  if (lds > 64 * 1024) {
-    hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)lds);
-    if (e != hipSuccess) return e;
-  }
+  if (hipError_t e = allow_dynamic_lds((const void*)fn, lds)) return e;
   const int64_t n_groups = (map.V + G - 1) / G;
   const int64_t need = (n_groups + kWavesPerBlock - 1) / kWavesPerBlock;
   int64_t blocks = (int64_t)dev.cus * blocks_per_cu((const void*)fn, lds, kBlock);

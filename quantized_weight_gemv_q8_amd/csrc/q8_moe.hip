@@ -612,21 +612,13 @@ hipError_t launch_moe_route(const int32_t* ids, int E, int P, const MoeWs& ws, f
   const size_t lds = 4 * (size_t)route_scratch_ints(E, P);
   MoeWs w = ws;
   void* args[] = {(void*)&ids, &E, &P, &w, &zero_rows, &zero_ld};
-  if (lds > 64 * 1024) {
-    hipError_t e = hipFuncSetAttribute((const void*)moe_route_kernel,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-  }
+  if (hipError_t e = allow_dynamic_lds((const void*)moe_route_kernel, lds)) return e;
   return hipLaunchKernel((const void*)moe_route_kernel, dim3(1), dim3(kRouteThreads), args, lds, s);
 }
 
 template <class Fn>
 static hipError_t moe_launch(Fn fn, size_t lds, void** args, hipStream_t s, const DevInfo& dev) {
-  if (lds > 64 * 1024) {
-    hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)lds);
-    if (e != hipSuccess) return e;
-  }
+  if (hipError_t e = allow_dynamic_lds((const void*)fn, lds)) return e;
   const int64_t blocks = (int64_t)dev.cus * blocks_per_cu((const void*)fn, lds, kBlock);
   return hipLaunchKernel((const void*)fn, dim3((unsigned)(blocks > 0 ? blocks : 1)), dim3(kBlock),
                          args, lds, s);

@@ -139,11 +139,9 @@ static hipError_t once_launch_t(const DevInfo& dev, typename K::Map map, typenam
   const size_t lds_x = (size_t)NT * C * 16 * ChunkPlanes<F, XF32>::P;
   const size_t lds_wave = (size_t)G * row_scale_pieces(F, C) * 16;  // a wave's scale rows
   const void* fn = once_fn<K, F, NT, LPR, XF32, CPL>();
-  if (lds_x + kOnceMaxBlock / kWave * lds_wave > 64 * 1024) {
-    const size_t most = std::min(lds_x + kOnceMaxBlock / kWave * lds_wave, dev.lds_per_block);
-    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)most);
-    if (e != hipSuccess) return e;
-  }
+  if (hipError_t e = allow_dynamic_lds(
+          fn, std::min(lds_x + kOnceMaxBlock / kWave * lds_wave, dev.lds_per_block)))
+    return e;
   const int64_t n_groups = (K::rows(map) + G - 1) / G;
   const int w = once_waves(dev, fn, n_groups, lds_x, lds_wave, NT <= 2);
   if (w == 0) return hipErrorNotSupported;
