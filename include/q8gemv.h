@@ -197,10 +197,14 @@ int q8_unpack_q4_0_host(const uint8_t *qs, int64_t ld_qs, const uint16_t *d, int
  *   ws [dev] workspace of at least q8_lmhead_ws_bytes(V, N) bytes,
  *   16-byte aligned, owned by the caller. It must be zero-filled once
  *   before its first use: it holds the argmax slots and the counters that
- *   let the last workgroup finish the argmax in the same launch, and every
- *   completed call leaves it all zero again, so the same workspace can be
- *   reused (and captured in a graph) without clearing it. Keep it for
- *   LM-head calls only; concurrent calls must use distinct workspaces. */
+ *   let the last workgroup finish the argmax, and every completed call
+ *   leaves it all zero again, so the same workspace can be reused (and
+ *   captured in a graph) without clearing it. Keep it for LM-head calls
+ *   only; concurrent calls must use distinct workspaces.
+ * Launches: with logits NULL, one launch per pass (GEMV and argmax fused);
+ * with logits requested for a pass of 1 or 2 tokens, the GEMV writes the
+ * logits and a second, short launch takes the argmax over them (faster
+ * for large vocabularies). Results are the same either way. */
 size_t q8_lmhead_ws_bytes(int64_t V, int N);
 int q8_lmhead_argmax(const q8_matrix *W, const void *x, int x_dt, float *logits,
                      int32_t *ids, int N, void *ws, size_t ws_bytes, void *stream);

@@ -100,28 +100,20 @@ struct LmEpi {
   }
 };
 
-// End of a workgroup: fold each token's best (logit, row) of this
-// workgroup's lanes into one key, merge it into the workspace slots, and
-// let the last workgroup decode the ids (see the top of q8_lmhead.hip).
-// Every thread of the workgroup calls it; waves <= kOnceMaxBlock / kWave.
-template <int NT, int R, int CNT>
-__device__ __forceinline__ void lm_merge(const LmEpi<CNT>& epi, const LmMap& map, char* ws,
-                                         int32_t* ids, int waves) {
+// End of a workgroup: merge each token's best key of the workgroup into
+// the workspace slots, and let the last workgroup decode the ids (see the
+// top of q8_lmhead.hip). key[n] is this lane's best key for token n (0 for
+// none). Every thread of the workgroup calls it; waves <=
+// kOnceMaxBlock / kWave.
+template <int NT>
+__device__ __forceinline__ void lm_merge_keys(const uint64_t* key, const int32_t* row_ids,
+                                              char* ws, int32_t* ids, int waves) {
   __shared__ uint64_t red[kOnceMaxBlock / kWave][kMaxNT];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lane = threadIdx.x % kWave;
 #pragma unroll
   for (int n = 0; n < NT; ++n) {
-    uint64_t k = 0;
-#pragma unroll
-    for (int i = 0; i < CNT; ++i) {
-      const int idx = epi.my_base + i;
-      if (epi.my_owner && idx < NT * R && idx / R == n && epi.bi[i] >= 0) {
-        const uint64_t c = argmax_key(epi.bv[i], epi.bi[i]);
-        k = c > k ? c : k;
-      }
-    }
-    k = wave_max_u64(k);
+    const uint64_t k = wave_max_u64(key[n]);
     if (lane == 0) red[wave][n] = k;
   }
   __syncthreads();
@@ -167,11 +159,32 @@ __device__ __forceinline__ void lm_merge(const LmEpi<CNT>& epi, const LmMap& map
           const uint64_t m = __hip_atomic_exchange(w.slot + n, (uint64_t)0, __ATOMIC_RELAXED,
                                                    __HIP_MEMORY_SCOPE_AGENT);
           const uint32_t row = ~(uint32_t)(m & 0xffffffffu);
-          ids[n] = map.row_ids ? map.row_ids[row] : (int32_t)row;
+          ids[n] = row_ids ? row_ids[row] : (int32_t)row;
         }
       }
     }
   }
+}
+
+// The same from a workgroup's LmEpi running bests.
+template <int NT, int R, int CNT>
+__device__ __forceinline__ void lm_merge(const LmEpi<CNT>& epi, const LmMap& map, char* ws,
+                                         int32_t* ids, int waves) {
+  uint64_t key[NT];
+#pragma unroll
+  for (int n = 0; n < NT; ++n) {
+    uint64_t k = 0;
+#pragma unroll
+    for (int i = 0; i < CNT; ++i) {
+      const int idx = epi.my_base + i;
+      if (epi.my_owner && idx < NT * R && idx / R == n && epi.bi[i] >= 0) {
+        const uint64_t c = argmax_key(epi.bv[i], epi.bi[i]);
+        k = c > k ? c : k;
+      }
+    }
+    key[n] = k;
+  }
+  lm_merge_keys<NT>(key, map.row_ids, ws, ids, waves);
 }
 
 }  // namespace q8

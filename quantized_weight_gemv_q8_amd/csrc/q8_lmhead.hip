@@ -18,6 +18,7 @@
 // row; the result does not depend on the order of the workgroups. A draft
 // head (a packed subset of the vocabulary rows) reports the winner through
 // its row-id table.
+#include "q8_dense.h"
 #include "q8_lmhead.h"
 
 namespace q8 {
@@ -94,6 +95,60 @@ static hipError_t lm_launch_nt(const DevInfo& dev, int nt, LmMap map, float* log
   return hipErrorInvalidValue;
 }
 
+// Argmax over logits already in memory (the second launch of the two-launch
+// head): each thread keeps the best key of a strided run of rows per token,
+// and the workgroups merge as the fused kernel's do.
+template <int NT>
+__global__ __launch_bounds__(kBlock) void lm_argmax_kernel(const float* logits, int64_t ld,
+                                                           int64_t V, const int32_t* row_ids,
+                                                           char* ws, int32_t* ids) {
+  uint64_t key[NT];
+#pragma unroll
+  for (int n = 0; n < NT; ++n) key[n] = 0;
+  const int64_t stride = (int64_t)gridDim.x * kBlock;
+  for (int64_t v = (int64_t)blockIdx.x * kBlock + threadIdx.x; v < V; v += stride) {
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      const uint64_t k = argmax_key(logits[n * ld + v], v);
+      key[n] = k > key[n] ? k : key[n];
+    }
+  }
+  lm_merge_keys<NT>(key, row_ids, ws, ids, kWavesPerBlock);
+}
+
+// With logits requested at 1 or 2 tokens the head runs as the dense GEMV
+// (the one-group kernel, which streams large vocabularies at ~90% of HBM
+// peak) writing the logits, then lm_argmax_kernel over them: measured on
+// MI355X, 151936 x 5120 N = 1, 114.3 us for the GEMV against 125.2 us for
+// the fused kernel. The logits are bitwise those of the fused kernel (same
+// per-row arithmetic), so are the ids. hipErrorNotSupported when the GEMV
+// kernel does not apply.
+static hipError_t lmhead_two_launch(const DevInfo& dev, const HMat& W, const int32_t* row_ids,
+                                    const char* x, bool x_f32, int64_t ldx_bytes, int C,
+                                    float* logits, int64_t ld, int32_t* ids, char* ws, int nt,
+                                    hipStream_t s) {
+  DenseMap map;
+  map.qa = map.qb = W.qs;
+  map.da = map.db = W.d;
+  map.ldqa = map.ldqb = W.ld_qs;
+  map.ldda = map.lddb = W.ld_d;
+  map.Ma = map.Mtot = W.M;
+  DenseEpi epi;
+  epi.ya = epi.yb = (char*)logits;
+  epi.Ma = epi.Mtot = W.M;
+  epi.f16 = false;
+  if (ld != W.M) return hipErrorNotSupported;
+  hipError_t e = launch_gemv_once(nt, dev, map, epi, W.fmt, lanes_for(W.fmt, W.K), x_f32, x,
+                                  ldx_bytes, C, s);
+  if (e != hipSuccess) return e;
+  int64_t blocks = (W.M + 4 * kBlock - 1) / (4 * kBlock);  // about four rows per thread
+  if (blocks > 2 * (int64_t)dev.cus) blocks = 2 * (int64_t)dev.cus;
+  int64_t V = W.M;
+  void* args[] = {(void*)&logits, &ld, &V, (void*)&row_ids, &ws, &ids};
+  const void* fn = nt == 1 ? (const void*)lm_argmax_kernel<1> : (const void*)lm_argmax_kernel<2>;
+  return hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(kBlock), args, 0, s);
+}
+
 size_t lmhead_ws_bytes() { return kLmWsBytes; }
 
 hipError_t launch_lmhead(const DevInfo& dev, const HMat& W, const int32_t* row_ids, const void* x,
@@ -106,6 +161,11 @@ hipError_t launch_lmhead(const DevInfo& dev, const HMat& W, const int32_t* row_i
   const int C = (int)chunks_per_row(W.fmt, W.K);
   const int64_t ldx_bytes = W.K * (x_f32 ? 4 : 2);
   const char* xp = (const char*)x;
+  if (logits && nt <= 2) {
+    const hipError_t e = lmhead_two_launch(dev, W, row_ids, xp, x_f32, ldx_bytes, C, logits,
+                                           ld_logits, ids, ws, nt, s);
+    if (e != hipErrorNotSupported) return e;
+  }
   return dispatch_chunks(W.fmt, lanes_for(W.fmt, W.K), x_f32, [&](auto f, auto l, auto xf) {
     return lm_launch_nt<decltype(f)::value, decltype(l)::value, decltype(xf)::value>(
         dev, nt, map, logits, ld_logits, xp, ldx_bytes, C, ws, ids, s);
