@@ -88,23 +88,36 @@ def test_lmhead_and_draft_head_graph_replays_reset_the_workspace():
     logits = torch.empty((3, 20000), device="cuda")
     ids = torch.empty((3,), dtype=torch.int32, device="cuda")
     ids2 = torch.empty((3,), dtype=torch.int32, device="cuda")
+    # one token with logits: the GEMV + argmax pair of launches
+    ws3 = torch.zeros((q8.lmhead_ws_bytes(20000, 1),), dtype=torch.uint8, device="cuda")
+    logits1 = torch.empty((1, 20000), device="cuda")
+    ids1 = torch.empty((1,), dtype=torch.int32, device="cuda")
 
     def step():
         q8.lmhead_argmax(W, x, logits=logits, ids=ids, ws=ws1)
         q8.lmhead_argmax(Wd, x, logits=False, ids=ids2, ws=ws2, row_ids=rid)
+        q8.lmhead_argmax(W, x[1:2], logits=logits1, ids=ids1, ws=ws3)
 
     step()
     torch.cuda.synchronize()
-    eager = [host(logits).copy(), host(ids).copy(), host(ids2).copy()]
+    eager = [host(logits).copy(), host(ids).copy(), host(ids2).copy(), host(logits1).copy(),
+             host(ids1).copy()]
     assert list(eager[1]) == list(c.planted_rows[:3]) and list(eager[2]) == list(c.planted_rows[:3])
+    assert eager[4][0] == c.planted_rows[1]
+    assert np.array_equal(eager[3][0].view(np.uint32), eager[0][1].view(np.uint32))
     g = capture(step)
     for r in range(4):
         logits.fill_(0)
+        logits1.fill_(0)
         ids.fill_(-1)
         ids2.fill_(-1)
+        ids1.fill_(-1)
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
         assert np.array_equal(host(logits).view(np.uint32), eager[0].view(np.uint32))
+        assert np.array_equal(host(logits1).view(np.uint32), eager[3].view(np.uint32))
         assert np.array_equal(host(ids), eager[1]) and np.array_equal(host(ids2), eager[2])
-        assert not host(ws1).any() and not host(ws2).any(), f"replay {r}: workspace not reset"
+        assert np.array_equal(host(ids1), eager[4])
+        assert not host(ws1).any() and not host(ws2).any() and not host(ws3).any(), \
+            f"replay {r}: workspace not reset"
