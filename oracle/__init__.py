@@ -236,7 +236,7 @@ def moe_route(expert_ids: np.ndarray, E: int):
     prefix sum (E+1 entries); pairs lists p grouped by expert in ascending e,
     and inside one expert in ascending p. active = experts with counts > 0,
     ascending. Follows the expert-major CSR batching of routed experts
-    (memra wiki, feature list, "MoE on 24 GB").
+    (memra wiki, feature list, the MoE item).
     """
     ids = np.asarray(expert_ids)
     T, topk = ids.shape

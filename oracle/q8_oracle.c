@@ -9,9 +9,9 @@
  * What it computes (the plain definition, nothing approximated):
  *   Q8_0 block = one fp16 scale d followed by 32 int8 quants q; the weight
  *   is d*q. This is the GGUF Q8_0 format that memra decodes and runs through
- *   its decode matvecs (memra wiki, feature list: "NVFP4 / Q4_0 / Q8_0
- *   decode" and "Loaders"; topairepos memra listing, crate table row
- *   memra-gguf).
+ *   its decode matvecs (memra wiki, feature list: the NVFP4/Q4_0/Q8_0
+ *   decode item and the loaders item; topairepos memra listing, crate
+ *   table row memra-gguf).
  *   y[n][m] = sum_{k=0}^{K-1} (d[m][k/32] * q[m][k]) * x[n][k]
  *   A[n][m] = sum_{k=0}^{K-1} |d[m][k/32] * q[m][k] * x[n][k]|
  *

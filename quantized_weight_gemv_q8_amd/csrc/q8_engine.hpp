@@ -3,8 +3,9 @@
 // The decode matvec is bound by HBM: each weight byte is used once per
 // token, so the kernel's job is to stream the quant and scale planes at the
 // memory system's rate and keep everything else off the critical path
-// (memra wiki: plain decode "sits at the DRAM wall"; memra performance,
-// "Dense IQ4_XS qmatvec arm 1": wide aligned loads relieve the load queue).
+// (memra wiki: plain decode is limited by DRAM bandwidth; memra
+// performance, the dense IQ4_XS qmatvec table, first arm: wide aligned
+// loads relieve the load queue).
 //
 // Work decomposition (wave64):
 //  * A row is cut into 16-byte chunks (16 quants = half a Q8_0 block).
@@ -26,9 +27,9 @@
 // the block's fp32(d) with one FMA into the lane's accumulator, and the
 // team's partials are combined by a fixed butterfly. Nothing in this
 // sequence depends on N, on R, or on the other tokens, so every token's
-// result is bitwise identical whatever the batch (memra wiki gate
-// paragraph: K=1..8 speculative verify must equal plain decode; "FP
-// summation order is part of the contract").
+// result is bitwise identical whatever the batch (memra wiki, gate
+// paragraph: K=1..8 speculative verify must equal plain decode, and the
+// order of floating-point sums is treated as part of the contract).
 #pragma once
 
 #include <hip/hip_runtime.h>

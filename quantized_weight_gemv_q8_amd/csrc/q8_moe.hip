@@ -2,10 +2,11 @@
 //
 // Decode-time MoE touches only the experts the router picked; the pages
 // batch the routed (token, slot) pairs by expert so each active expert's
-// weights stream once for all of its tokens (memra wiki, feature list:
-// "MoE ... expert-major CSR batching"), keep routing and lengths on the
-// device so the step stays graph-replayable ("graph-replayable
-// device-length counters"), and require a token's outputs not to depend on
+// weights stream once for all of its tokens (memra wiki, feature list, the
+// MoE item: routed tokens batched per expert in CSR form), keep routing and
+// lengths on the device so that the step stays replayable as a graph (same
+// item: lengths counted on the device), and require a token's outputs not
+// to depend on
 // its co-arrivals (memra performance, serving exactness arc).
 //
 // Kernels:

@@ -19,8 +19,8 @@ workload-specific extras (LM-head planting, MoE routing).
 
 The Q8_0 block itself (an fp16 scale ``d`` followed by 32 int8 quants,
 weight = d*q) is the GGUF format the memra pages load and decode (memra wiki,
-feature list: "NVFP4 / Q4_0 / Q8_0 decode" and "Loaders"; topairepos memra
-listing, crate table row memra-gguf).
+feature list: the NVFP4/Q4_0/Q8_0 decode item and the loaders item;
+topairepos memra listing, crate table row memra-gguf).
 """
 
 from __future__ import annotations
