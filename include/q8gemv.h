@@ -5,20 +5,22 @@
  * blocks of 32 consecutive elements along K; each block holds one fp16
  * scale d and 32 int8 quants q, and the weight is d*q. This is the GGUF
  * Q8_0 format that the memra engine loads and runs through its decode
- * matvecs (memra wiki, feature list: "NVFP4 / Q4_0 / Q8_0 decode" with
- * split-plane repacked matvecs and per-shape auto-dispatch; "Loaders").
+ * matvecs (memra wiki, feature list: the item on NVFP4, Q4_0 and Q8_0
+ * decode, which names repacked split-plane matvecs chosen per shape; and
+ * the loaders item).
  * For N tokens x [N][K]:
  *
  *     y[n][m] = sum_k d[m][k/32] * q[m][k] * x[n][k]
  *
  * N = 1 is plain decode; N = 2..8 is the batched K+1 verify of speculative
- * decoding (memra wiki, feature list: "MTP speculative decoding ... one
- * batched K+1 verify"). Accuracy contract: every output is within
+ * decoding (memra wiki, feature list: the item on MTP speculative decoding,
+ * whose K drafted tokens plus one are verified in one batched pass).
+ * Accuracy contract: every output is within
  * 1e-3 * sum_k |d*q*x| of the exact value (fp32 accumulation); the result
  * for token n is bitwise independent of N and of the other tokens' values
  * (the pages require verify logits to equal plain decode exactly: memra
- * wiki gate paragraph, "K=1..8 self-consistency gate"; bw24 README
- * "zero differing logits").
+ * wiki, gate paragraph, the self-consistency gate over K = 1..8; bw24
+ * README, where no logit may differ).
  *
  * Conventions for every entry point:
  *  - Pointers marked [dev] are device memory (hipMalloc or a torch
@@ -30,14 +32,14 @@
  *    only enqueue kernels on it: no allocation, no synchronisation, no
  *    host<->device copy, so they can be captured in a HIP graph (the pages
  *    run one graph replay per decoded token: memra wiki, feature list,
- *    "CUDA-graph decode").
+ *    the graph-decode item).
  *  - Errors: arguments are validated before anything is enqueued; a
  *    negative q8_status is returned and nothing is launched. A launch
  *    failure reported by the HIP runtime returns Q8_ERR_LAUNCH. Faults
  *    inside a kernel surface at the caller's next synchronisation, like any
  *    HIP call. Unsupported inputs are refused, never silently routed to a
- *    slow path (topairepos memra listing: "useful failures over silent
- *    fallbacks").
+ *    slow path (topairepos memra listing, which prefers a clear failure to a
+ *    quiet fallback).
  *  - The library runs only on gfx950; on any other device every hot-path
  *    call returns Q8_ERR_DEVICE (memra wiki: the engine verifies at start-up
  *    that the binary matches the device and fails early otherwise).
@@ -112,7 +114,7 @@ int q8_device_check(int device);
 
 /* ------------------------------------------------------------ packing (host)
  * Load-time repack of GGUF Q8_0 blocks into the split-plane layout (memra
- * wiki: "split-plane repacked matvecs"; the onboarding CLI packs models
+ * wiki, feature list: the split-plane repack; the onboarding CLI packs models
  * into the engine's own layout, topairepos memra listing, memra-cli row).
  *
  * q8_pack_layout: leading dimensions and plane sizes for an [M][K] matrix:
@@ -163,7 +165,7 @@ int q8_gemv_pair_silu(const q8_matrix *Wg, const q8_matrix *Wu, const void *x, i
 
 /* ------------------------------------------------------------ Q4_0
  * The same GEMV family over GGUF Q4_0 weights (memra wiki, feature list:
- * "NVFP4 / Q4_0 / Q8_0 decode ... split-plane repacked matvecs"). A Q4_0
+ * the item on NVFP4, Q4_0 and Q8_0 decode with split-plane matvecs). A Q4_0
  * block is 18 bytes: little-endian fp16 d, then 16 bytes whose low nibbles
  * are elements 0..15 and high nibbles elements 16..31, each stored as
  * q + 8 (q in [-8, 7]); the weight is d * q. The packed matrix is a
@@ -189,22 +191,26 @@ int q8_unpack_q4_0_host(const uint8_t *qs, int64_t ld_qs, const uint16_t *d, int
  * ids[n] = the smallest v with logits[n][v] == max_v logits[n][v]
  * (ties go to the lowest index; -0 and +0 compare equal). The argmax is
  * taken over the same fp32 values that are written to logits, so ids is
- * always consistent with logits. logits may be NULL (only ids are written:
- * "lean logits", the caller copies back 4 bytes per token, as in the pages'
- * graph decode; memra wiki feature list, "4 bytes/token host traffic").
+ * always consistent with logits. logits may be NULL (only ids are written,
+ * so the caller copies back 4 bytes per token, as the pages' graph decode
+ * does: memra wiki, feature list, the graph-decode item).
  *   x [dev] fp16 or fp32 [N][K]; logits [dev] fp32 [N][V] or NULL;
  *   ids [dev] int32 [N]; N >= 1 (passes of up to 8 tokens).
- *   ws [dev] workspace of at least q8_lmhead_ws_bytes(V, N) bytes,
- *   16-byte aligned, owned by the caller. It must be zero-filled once
- *   before its first use: it holds the argmax slots and the counters that
- *   let the last workgroup finish the argmax, and every completed call
- *   leaves it all zero again, so the same workspace can be reused (and
- *   captured in a graph) without clearing it. Keep it for LM-head calls
- *   only; concurrent calls must use distinct workspaces.
- * Launches: with logits NULL, one launch per pass (GEMV and argmax fused);
- * with logits requested for a pass of 1 or 2 tokens, the GEMV writes the
- * logits and a second, short launch takes the argmax over them (faster
- * for large vocabularies). Results are the same either way. */
+ *   ws [dev] workspace of at least q8_lmhead_ws_bytes(V, N) bytes
+ *   (4608 bytes plus 8 * V rounded up to 256; it grows with V, so size it
+ *   for the largest vocabulary it will serve), 16-byte aligned, owned by
+ *   the caller. It must be zero-filled once before its first use: it holds
+ *   the argmax slots, the counters that let the last workgroup finish the
+ *   argmax, and scratch logits for calls without logits; every completed
+ *   call leaves it all zero again, so the same workspace can be reused
+ *   (and captured in a graph) without clearing it. Keep it for LM-head
+ *   calls only; concurrent calls must use distinct workspaces.
+ * Launches: for a pass of 2 tokens, or of 1 token over a large enough
+ * matrix (from about 150 MB of weights with logits, 280 MB without), the
+ * GEMV writes the logits (the caller's, else the workspace's scratch) and
+ * a second, short launch takes the argmax over them (and zeroes the
+ * scratch); other passes run GEMV and argmax fused in one launch. Results
+ * are the same either way. */
 size_t q8_lmhead_ws_bytes(int64_t V, int N);
 int q8_lmhead_argmax(const q8_matrix *W, const void *x, int x_dt, float *logits,
                      int32_t *ids, int N, void *ws, size_t ws_bytes, void *stream);
@@ -226,7 +232,7 @@ int q8_lmhead_argmax_rows(const q8_matrix *W, const int32_t *row_ids, const void
 
 /* ------------------------------------------------------------ routed experts
  * Expert-major CSR batching of routed experts (memra wiki, feature list,
- * "MoE ... expert-major CSR batching"): the routed (token, slot) pairs are
+ * the MoE item, which batches routed tokens per expert in CSR form): the routed (token, slot) pairs are
  * grouped by expert on the device, and each active expert's weights are
  * streamed once for all tokens routed to it. Routing never leaves the
  * device (graph-replayable device-side lengths, memra wiki, feature list).

@@ -314,9 +314,8 @@ int q8_gemv_pair_silu(const q8_matrix* Wg, const q8_matrix* Wu, const void* x, i
 
 // ------------------------------------------------------------ LM head
 size_t q8_lmhead_ws_bytes(int64_t V, int N) {
-  (void)V;
   (void)N;
-  return q8::lmhead_ws_bytes();
+  return q8::lmhead_ws_bytes(V);
 }
 
 static int lmhead_impl(const q8_matrix* W, const int32_t* row_ids, const void* x, int x_dt,

@@ -80,7 +80,7 @@ hipError_t launch_gemv(const DevInfo& dev, const HMat& A, const HMat* B, const v
 // LM head pass: logits (may be null) and ids [nt]. The workspace holds the
 // argmax slots and counters; it must be zero before the first pass and is
 // zero again after each completed pass.
-size_t lmhead_ws_bytes();
+size_t lmhead_ws_bytes(int64_t V);
 hipError_t launch_lmhead(const DevInfo& dev, const HMat& W, const int32_t* row_ids, const void* x,
                          bool x_f32, float* logits, int64_t ld_logits, int32_t* ids, char* ws,
                          int nt, hipStream_t s);

@@ -1,12 +1,14 @@
 // q8_lmhead.hip -- LM-head Q8_0 GEMV fused with a greedy argmax (gfx950).
 //
 // The decode step ends with the vocabulary projection and a greedy pick;
-// the pages keep the logits lean and move 4 bytes per token to the host
-// (memra wiki, feature list: "CUDA-graph decode ... 4 bytes/token host
-// traffic"), and greedy argmax is their correctness instrument (memra wiki,
-// gate paragraph: run-gen prints its argmax gate before any number).
+// the pages keep the logits on the device and move only 4 bytes per token
+// to the host (memra wiki, feature list, the graph-decode item), and greedy
+// argmax is their correctness instrument (memra wiki, gate paragraph: the
+// generation runner reports its argmax gate before any timing).
 //
-// Pass structure: one persistent GEMV launch. Each workgroup folds the
+// Pass structure (passes of 3 to 8 tokens, one-token passes over small
+// vocabularies, or where the one-group GEMV does not apply; the rest take
+// the two-launch head below): one persistent GEMV launch. Each workgroup folds the
 // rows it produced into one 64-bit key per token, merges it into a
 // per-token slot with an atomic maximum, and then takes a ticket from a
 // wrapping counter; the workgroup that draws the last ticket reads the
@@ -97,11 +99,13 @@ static hipError_t lm_launch_nt(const DevInfo& dev, int nt, LmMap map, float* log
 
 // Argmax over logits already in memory (the second launch of the two-launch
 // head): each thread keeps the best key of a strided run of rows per token,
-// and the workgroups merge as the fused kernel's do.
+// and the workgroups merge as the fused kernel's do. With clear set the
+// logits are the workspace's scratch rows and each is set back to zero
+// once read.
 template <int NT>
-__global__ __launch_bounds__(kBlock) void lm_argmax_kernel(const float* logits, int64_t ld,
-                                                           int64_t V, const int32_t* row_ids,
-                                                           char* ws, int32_t* ids) {
+__global__ __launch_bounds__(kBlock) void lm_argmax_kernel(float* logits, int64_t ld, int64_t V,
+                                                           const int32_t* row_ids, char* ws,
+                                                           int32_t* ids, bool clear) {
   uint64_t key[NT];
 #pragma unroll
   for (int n = 0; n < NT; ++n) key[n] = 0;
@@ -111,22 +115,26 @@ __global__ __launch_bounds__(kBlock) void lm_argmax_kernel(const float* logits, 
     for (int n = 0; n < NT; ++n) {
       const uint64_t k = argmax_key(logits[n * ld + v], v);
       key[n] = k > key[n] ? k : key[n];
+      if (clear) logits[n * ld + v] = 0.0f;
     }
   }
   lm_merge_keys<NT>(key, row_ids, ws, ids, kWavesPerBlock);
 }
 
-// With logits requested at 1 or 2 tokens the head runs as the dense GEMV
-// (the one-group kernel, which streams large vocabularies at ~90% of HBM
-// peak) writing the logits, then lm_argmax_kernel over them: measured on
-// MI355X, 151936 x 5120 N = 1, 114.3 us for the GEMV against 125.2 us for
-// the fused kernel. The logits are bitwise those of the fused kernel (same
-// per-row arithmetic), so are the ids. hipErrorNotSupported when the GEMV
-// kernel does not apply.
+// The two-launch head (two_launch_pays): the dense GEMV (the one-group
+// kernel, which streams large vocabularies at ~90% of HBM peak) writes the
+// logits -- the caller's, or with none requested the workspace's scratch
+// rows -- then lm_argmax_kernel takes the argmax over them. Measured on MI355X, 151936 x 5120 N = 1:
+// GEMV 115.4 us + argmax 5.1 us against 125 us for the fused kernel.
+// Merging per-workgroup keys with atomics at the end of the one-group
+// kernel instead was slower (127 us for the GEMV alone): each workgroup
+// stays resident until its agent-scope atomic completes. The logits are
+// bitwise those of the fused kernel (same per-row arithmetic), so are the
+// ids. hipErrorNotSupported when the GEMV kernel does not apply.
 static hipError_t lmhead_two_launch(const DevInfo& dev, const HMat& W, const int32_t* row_ids,
                                     const char* x, bool x_f32, int64_t ldx_bytes, int C,
-                                    float* logits, int64_t ld, int32_t* ids, char* ws, int nt,
-                                    hipStream_t s) {
+                                    float* logits, int64_t ld, bool clear, int32_t* ids, char* ws,
+                                    int nt, hipStream_t s) {
   DenseMap map;
   map.qa = map.qb = W.qs;
   map.da = map.db = W.d;
@@ -144,12 +152,31 @@ static hipError_t lmhead_two_launch(const DevInfo& dev, const HMat& W, const int
   int64_t blocks = (W.M + 4 * kBlock - 1) / (4 * kBlock);  // about four rows per thread
   if (blocks > 2 * (int64_t)dev.cus) blocks = 2 * (int64_t)dev.cus;
   int64_t V = W.M;
-  void* args[] = {(void*)&logits, &ld, &V, (void*)&row_ids, &ws, &ids};
+  void* args[] = {(void*)&logits, &ld, &V, (void*)&row_ids, &ws, &ids, &clear};
   const void* fn = nt == 1 ? (const void*)lm_argmax_kernel<1> : (const void*)lm_argmax_kernel<2>;
   return hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(kBlock), args, 0, s);
 }
 
-size_t lmhead_ws_bytes() { return kLmWsBytes; }
+// Whether the two-launch head is the faster at this shape. Its one-group
+// GEMV streams at ~90% of HBM peak against the fused kernel's ~85%, and
+// the second launch costs a few microseconds, so one token needs enough
+// weight bytes; two tokens always gain. Measured on MI355X (us, fused ->
+// two launches), ids only: 16000 x 4096 15.8 -> 17.5, 48000 x 4096 36.9 ->
+// 37.7, 65536 x 4096 50.2 -> 47.1, 151936 x 5120 125.1 -> 120.0; with
+// logits: 32000 x 4096 26.3 -> 26.8, 48000 x 4096 37.9 -> 36.9; two
+// tokens: 16000 x 4096 23.9 -> 20.7, 151936 x 4096 121.4 -> 110.4.
+static bool two_launch_pays(const HMat& W, int nt, bool logits) {
+  if (nt > 2) return false;
+  if (nt == 2) return true;
+  const double bytes = (double)W.M * (double)W.K * (W.fmt == kFmtQ4 ? 18.0 : 34.0) / 32.0;
+  return bytes >= (logits ? 150e6 : 280e6);
+}
+
+// Slots and counters, then scratch logits for two tokens (256-byte aligned).
+size_t lmhead_ws_bytes(int64_t V) {
+  const size_t scratch = ((size_t)(V > 0 ? V : 0) * 2 * sizeof(float) + 255) / 256 * 256;
+  return kLmWsBytes + scratch;
+}
 
 hipError_t launch_lmhead(const DevInfo& dev, const HMat& W, const int32_t* row_ids, const void* x,
                          bool x_f32, float* logits, int64_t ld_logits, int32_t* ids, char* ws,
@@ -161,9 +188,11 @@ hipError_t launch_lmhead(const DevInfo& dev, const HMat& W, const int32_t* row_i
   const int C = (int)chunks_per_row(W.fmt, W.K);
   const int64_t ldx_bytes = W.K * (x_f32 ? 4 : 2);
   const char* xp = (const char*)x;
-  if (logits && nt <= 2) {
-    const hipError_t e = lmhead_two_launch(dev, W, row_ids, xp, x_f32, ldx_bytes, C, logits,
-                                           ld_logits, ids, ws, nt, s);
+  if (two_launch_pays(W, nt, logits != nullptr)) {
+    float* scratch = (float*)(ws + kLmWsBytes);
+    const hipError_t e = lmhead_two_launch(dev, W, row_ids, xp, x_f32, ldx_bytes, C,
+                                           logits ? logits : scratch, logits ? ld_logits : W.M,
+                                           !logits, ids, ws, nt, s);
     if (e != hipErrorNotSupported) return e;
   }
   return dispatch_chunks(W.fmt, lanes_for(W.fmt, W.K), x_f32, [&](auto f, auto l, auto xf) {

@@ -163,6 +163,12 @@ def test_lmhead_validation(L):
     W = _mat()
     n = L.q8_lmhead_ws_bytes(64, 1)
     assert n > 0
+    # slots and counters (4608 bytes), then scratch logits for two tokens,
+    # rounded up to 256 bytes; independent of N
+    assert n == 4608 + 512
+    assert L.q8_lmhead_ws_bytes(151936, 1) == 4608 + 151936 * 8
+    assert L.q8_lmhead_ws_bytes(151936, 8) == L.q8_lmhead_ws_bytes(151936, 1)
+    assert L.q8_lmhead_ws_bytes(1, 1) == 4608 + 256
     ok = dict(x=X, xdt=1, logits=Y, ids=Y + 0x10000, N=1, ws=WS, nws=n)
 
     def rc(**kw):

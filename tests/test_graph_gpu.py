@@ -92,18 +92,22 @@ def test_lmhead_and_draft_head_graph_replays_reset_the_workspace():
     ws3 = torch.zeros((q8.lmhead_ws_bytes(20000, 1),), dtype=torch.uint8, device="cuda")
     logits1 = torch.empty((1, 20000), device="cuda")
     ids1 = torch.empty((1,), dtype=torch.int32, device="cuda")
+    # two tokens, ids only, draft head: GEMV into the workspace's scratch + argmax
+    ws4 = torch.zeros((q8.lmhead_ws_bytes(4096, 2),), dtype=torch.uint8, device="cuda")
+    ids4 = torch.empty((2,), dtype=torch.int32, device="cuda")
 
     def step():
         q8.lmhead_argmax(W, x, logits=logits, ids=ids, ws=ws1)
         q8.lmhead_argmax(Wd, x, logits=False, ids=ids2, ws=ws2, row_ids=rid)
         q8.lmhead_argmax(W, x[1:2], logits=logits1, ids=ids1, ws=ws3)
+        q8.lmhead_argmax(Wd, x[1:3], logits=False, ids=ids4, ws=ws4, row_ids=rid)
 
     step()
     torch.cuda.synchronize()
     eager = [host(logits).copy(), host(ids).copy(), host(ids2).copy(), host(logits1).copy(),
-             host(ids1).copy()]
+             host(ids1).copy(), host(ids4).copy()]
     assert list(eager[1]) == list(c.planted_rows[:3]) and list(eager[2]) == list(c.planted_rows[:3])
-    assert eager[4][0] == c.planted_rows[1]
+    assert eager[4][0] == c.planted_rows[1] and list(eager[5]) == list(c.planted_rows[1:3])
     assert np.array_equal(eager[3][0].view(np.uint32), eager[0][1].view(np.uint32))
     g = capture(step)
     for r in range(4):
@@ -112,12 +116,13 @@ def test_lmhead_and_draft_head_graph_replays_reset_the_workspace():
         ids.fill_(-1)
         ids2.fill_(-1)
         ids1.fill_(-1)
+        ids4.fill_(-1)
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
         assert np.array_equal(host(logits).view(np.uint32), eager[0].view(np.uint32))
         assert np.array_equal(host(logits1).view(np.uint32), eager[3].view(np.uint32))
         assert np.array_equal(host(ids), eager[1]) and np.array_equal(host(ids2), eager[2])
-        assert np.array_equal(host(ids1), eager[4])
-        assert not host(ws1).any() and not host(ws2).any() and not host(ws3).any(), \
+        assert np.array_equal(host(ids1), eager[4]) and np.array_equal(host(ids4), eager[5])
+        assert not any(host(w).any() for w in (ws1, ws2, ws3, ws4)), \
             f"replay {r}: workspace not reset"

@@ -45,7 +45,7 @@ def vocab():
     return c, upload(c.q, c.d)
 
 
-@pytest.mark.parametrize("N", [1, 4])
+@pytest.mark.parametrize("N", [1, 2, 4])
 def test_full_vocab(vocab, N):
     note(f"lmhead 151936x5120 N={N}")
     c4, W = vocab
@@ -111,20 +111,39 @@ def test_all_zero_logits_pick_row_zero():
 
 
 def test_workspace_reused_across_shapes_returns_to_zero():
-    """One zero-filled workspace serves calls whose grids differ (vocab
-    size, token count, multi-pass N): every call's ids match the oracle and
-    the whole workspace (argmax slots and counters) reads zero after each
-    call, ready for the next one."""
-    ws = torch.zeros((q8.lmhead_ws_bytes(1, 1),), dtype=torch.uint8, device="cuda")
-    for i, (V, K, N) in enumerate([(4096, 1024, 1), (333, 96, 11), (20000, 512, 4), (1, 32, 1),
-                                   (9, 64, 2), (4096, 1024, 8)]):
+    """One zero-filled workspace, sized for the largest vocabulary, serves
+    calls whose grids differ (vocab size, token count, multi-pass N, with
+    and without logits): every call's ids match the oracle, the ids-only
+    call (which goes through the workspace's scratch logits at 1-2 tokens)
+    returns the same ids, and the whole workspace (argmax slots, counters
+    and scratch) reads zero after each call, ready for the next one."""
+    shapes = [(4096, 1024, 1), (333, 96, 11), (20000, 512, 4), (1, 32, 1), (9, 64, 2),
+              (20000, 512, 2), (4096, 1024, 8), (20000, 512, 1)]
+    nws = q8.lmhead_ws_bytes(max(V for V, _, _ in shapes), 1)
+    assert nws >= 4608 + 8 * 20000
+    ws = torch.zeros((nws,), dtype=torch.uint8, device="cuda")
+    for i, (V, K, N) in enumerate(shapes):
         note(f"lmhead ws reuse V={V} K={K} N={N}")
         c = synth.lmhead_case(V, K, min(N, V), seed=100 + i)
         if N > V:
             c.x = synth.draw_x(np.random.default_rng(i), N, K)
-        logits, ids = q8.lmhead_argmax(upload(c.q, c.d), dev(c.x), ws=ws)
+        W = upload(c.q, c.d)
+        logits, ids = q8.lmhead_argmax(W, dev(c.x), ws=ws)
         check_lmhead(c, host(logits), host(ids))
         assert not host(ws).any(), "workspace not returned to zero"
+        _, ids2 = q8.lmhead_argmax(W, dev(c.x), logits=False, ws=ws)
+        assert np.array_equal(host(ids2), host(ids)), "ids-only call differs"
+        assert not host(ws).any(), "workspace not returned to zero after an ids-only call"
+
+
+def test_workspace_smaller_than_the_vocabulary_needs_is_refused():
+    """The workspace grows with V (scratch logits for two tokens): one sized
+    for a smaller vocabulary is refused with Q8_ERR_WORKSPACE, nothing
+    launched."""
+    c = synth.lmhead_case(4096, 256, 1, seed=7)
+    ws = torch.zeros((q8.lmhead_ws_bytes(1024, 1),), dtype=torch.uint8, device="cuda")
+    with pytest.raises(RuntimeError, match="-5|WORKSPACE|workspace"):
+        q8.lmhead_argmax(upload(c.q, c.d), dev(c.x), logits=False, ws=ws)
 
 
 # ---------------------------------------------------------------- draft head (vocabulary subset)
