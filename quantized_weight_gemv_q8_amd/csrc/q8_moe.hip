@@ -550,29 +550,48 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(moe_wave
                                              (int)chunks_per_row(FM, Gb.e0.K), 2 * F, lds_x);
 }
 
+// The pairs of token t are taken eight at a time: their ids, gate weights
+// and rows are all loaded before the first FMA (one memory round trip per
+// eight pairs instead of one per pair), then folded in ascending j, a pair
+// with an out-of-range expert leaving the sum as it is.
 __global__ __launch_bounds__(256) void moe_combine_kernel(const int32_t* ids, int E,
                                                          const float* gate_w, const float* yp,
                                                          float* out, int topk, int64_t M) {
+  constexpr int U = 8;
   const int t = blockIdx.y;
   const int64_t m0 = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
   if (m0 >= M) return;
+  const bool vec = (M & 3) == 0;
+  const int nv = vec ? 4 : (int)(M - m0 < 4 ? M - m0 : 4);
   float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  for (int j = 0; j < topk; ++j) {
-    const int e = ids[t * topk + j];
-    if (e < 0 || e >= E) continue;
-    const float w = gate_w[t * topk + j];
-    const float* row = yp + ((int64_t)t * topk + j) * M;
-    if ((M & 3) == 0) {
-      const float4 v = *reinterpret_cast<const float4*>(row + m0);
-      acc[0] = __builtin_fmaf(w, v.x, acc[0]);
-      acc[1] = __builtin_fmaf(w, v.y, acc[1]);
-      acc[2] = __builtin_fmaf(w, v.z, acc[2]);
-      acc[3] = __builtin_fmaf(w, v.w, acc[3]);
-    } else {
-      for (int i = 0; i < 4 && m0 + i < M; ++i) acc[i] = __builtin_fmaf(w, row[m0 + i], acc[i]);
+  for (int j0 = 0; j0 < topk; j0 += U) {
+    bool ok[U];
+    float w[U];
+    float v[U][4];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int j = j0 + u < topk ? j0 + u : topk - 1;  // in range; unused past topk
+      const int e = ids[t * topk + j];
+      ok[u] = j0 + u < topk && e >= 0 && e < E;
+      w[u] = gate_w[t * topk + j];
+      const float* row = yp + ((int64_t)t * topk + j) * M + m0;
+      if (vec) {
+        const float4 r = *reinterpret_cast<const float4*>(row);
+        v[u][0] = r.x;
+        v[u][1] = r.y;
+        v[u][2] = r.z;
+        v[u][3] = r.w;
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[u][i] = i < nv ? row[i] : 0.0f;
+      }
     }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] = ok[u] ? __builtin_fmaf(w[u], v[u][i], acc[i]) : acc[i];
   }
-  for (int i = 0; i < 4 && m0 + i < M; ++i) out[(int64_t)t * M + m0 + i] = acc[i];
+  for (int i = 0; i < nv; ++i) out[(int64_t)t * M + m0 + i] = acc[i];
 }
 
 // ---------------------------------------------------------------- host side
