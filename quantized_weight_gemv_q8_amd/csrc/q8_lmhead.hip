@@ -102,20 +102,38 @@ static hipError_t lm_launch_nt(const DevInfo& dev, int nt, LmMap map, float* log
 // and the workgroups merge as the fused kernel's do. With clear set the
 // logits are the workspace's scratch rows and each is set back to zero
 // once read.
+constexpr int kLmArgU = 4;
+
 template <int NT>
 __global__ __launch_bounds__(kBlock) void lm_argmax_kernel(float* logits, int64_t ld, int64_t V,
                                                            const int32_t* row_ids, char* ws,
                                                            int32_t* ids, bool clear) {
+  // kLmArgU rows per thread per step, all loaded before the first compare
+  // (one memory round trip per step); the maximum does not depend on the
+  // order, so neither do the ids.
   uint64_t key[NT];
 #pragma unroll
   for (int n = 0; n < NT; ++n) key[n] = 0;
   const int64_t stride = (int64_t)gridDim.x * kBlock;
-  for (int64_t v = (int64_t)blockIdx.x * kBlock + threadIdx.x; v < V; v += stride) {
+  for (int64_t v0 = (int64_t)blockIdx.x * kBlock + threadIdx.x; v0 < V; v0 += kLmArgU * stride) {
+    float val[kLmArgU][NT];
 #pragma unroll
-    for (int n = 0; n < NT; ++n) {
-      const uint64_t k = argmax_key(logits[n * ld + v], v);
-      key[n] = k > key[n] ? k : key[n];
-      if (clear) logits[n * ld + v] = 0.0f;
+    for (int u = 0; u < kLmArgU; ++u) {
+      const int64_t v = v0 + u * stride;
+      const int64_t vc = v < V ? v : v0;
+#pragma unroll
+      for (int n = 0; n < NT; ++n) val[u][n] = logits[n * ld + vc];
+    }
+#pragma unroll
+    for (int u = 0; u < kLmArgU; ++u) {
+      const int64_t v = v0 + u * stride;
+      if (v >= V) continue;
+#pragma unroll
+      for (int n = 0; n < NT; ++n) {
+        const uint64_t k = argmax_key(val[u][n], v);
+        key[n] = k > key[n] ? k : key[n];
+        if (clear) logits[n * ld + v] = 0.0f;
+      }
     }
   }
   lm_merge_keys<NT>(key, row_ids, ws, ids, kWavesPerBlock);
@@ -149,7 +167,7 @@ static hipError_t lmhead_two_launch(const DevInfo& dev, const HMat& W, const int
   hipError_t e = launch_gemv_once(nt, dev, map, epi, W.fmt, lanes_for(W.fmt, W.K), x_f32, x,
                                   ldx_bytes, C, s);
   if (e != hipSuccess) return e;
-  int64_t blocks = (W.M + 4 * kBlock - 1) / (4 * kBlock);  // about four rows per thread
+  int64_t blocks = (W.M + kLmArgU * kBlock - 1) / (kLmArgU * kBlock);  // one step per thread
   if (blocks > 2 * (int64_t)dev.cus) blocks = 2 * (int64_t)dev.cus;
   int64_t V = W.M;
   void* args[] = {(void*)&logits, &ld, &V, (void*)&row_ids, &ws, &ids, &clear};
