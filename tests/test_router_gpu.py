@@ -144,3 +144,44 @@ def test_routed_layer_graph_replays_match_eager(routed_layer):
         assert np.array_equal(host(ids), eager[0]), f"replay {r}: ids"
         assert np.array_equal(host(gw).view(np.uint32), eager[1].view(np.uint32)), f"replay {r}: gate_w"
         assert np.array_equal(host(out).view(np.uint32), eager[2].view(np.uint32)), f"replay {r}: out"
+
+
+@pytest.mark.parametrize("T,E,K,q4,xf32,topk", [
+    (16, 128, 2048, False, False, 8),   # the routed layer's router: one launch, 8 rows per team
+    (1, 100, 1024, False, False, 6),    # one token: GEMV then top-k (keys in registers)
+    (9, 100, 1024, False, False, 6),    # ragged expert count, the fewest tokens of one launch
+    (64, 128, 2048, False, False, 8),   # the largest one-launch batch
+    (12, 64, 2048, False, False, 4),    # 4 rows per team, keys in one register per lane
+    (13, 200, 512, False, False, 16),   # 32 lanes per row, ragged last wave
+    (17, 256, 256, False, False, 64),   # 16 lanes per row, topk at its maximum
+    (7, 256, 256, False, False, 64),    # fewer than 9 tokens: two launches
+    (65, 128, 2048, False, False, 8),   # one token more: GEMV then top-k launch
+    (64, 128, 2048, False, True, 8),    # fp32 x: two launches
+    (16, 256, 4096, False, False, 8),   # too many loads per lane: two launches
+    (7, 4096, 512, False, False, 64),   # E and topk at their maximum: two launches
+    (16, 128, 2048, True, False, 8),    # Q4_0 router matrix: two launches
+    (5, 96, 96, True, True, 4),         # Q4_0, fp32 x, three blocks per row
+])
+def test_router_equals_gemv_then_topk(T, E, K, q4, xf32, topk):
+    """q8_moe_router (one launch for 9 to 64 tokens over a small enough
+    Q8_0 router matrix with fp16 x, else the GEMV and top-k launches) returns bitwise q8_gemv's logits and bitwise
+    q8_moe_topk_softmax's ids and weights over them, with duplicated router
+    rows so that equal logits occur; the picks also match the oracle's."""
+    note(f"router T={T} E={E} K={K} q4={q4} xf32={xf32} topk={topk}")
+    rng = np.random.default_rng(T * 7919 + E)
+    if q4:
+        q, d = synth.draw_weights_q4_0(rng, E, K)
+    else:
+        q, d = synth.draw_weights(rng, E, K)
+    q[E // 2] = q[E // 3]  # equal rows: equal logits, the lower expert first
+    d[E // 2] = d[E // 3]
+    W = q8.pack_q4_0(synth.to_gguf_q4_0_blocks(q, d)) if q4 else upload(q, d)
+    x = synth.draw_x(rng, T, K)
+    xd = dev(x.astype(np.float32) if xf32 else x)
+    logits, ids, gw = q8.moe_router(W, xd, topk)
+    ref_logits = q8.gemv(W, xd)
+    assert np.array_equal(host(logits).view(np.uint32), host(ref_logits).view(np.uint32))
+    rid, rgw = q8.moe_topk_softmax(ref_logits, topk)
+    assert np.array_equal(host(ids), host(rid))
+    assert np.array_equal(host(gw).view(np.uint32), host(rgw).view(np.uint32))
+    check_router(host(logits), host(ids), host(gw), topk)
