@@ -428,6 +428,53 @@ def gate_up_silu(qg, dg, qu, du, x, threads: int = 1, out_dtype: str = "f32"):
     return dict(h=h, bh=bh, g=g, u=u)
 
 
+# ---------------------------------------------------------------- shared expert
+def sigmoid(z: np.ndarray) -> np.ndarray:
+    """sigma(z) = 1 / (1 + e^-z) in fp64, as e^z / (1 + e^z) for z < 0 (the
+    same function, without overflow of e^-z)."""
+    z = np.asarray(z, np.float64)
+    ez = np.exp(np.minimum(z, 0.0))
+    return np.where(z >= 0, 1.0 / (1.0 + np.exp(-np.maximum(z, 0.0))), ez / (1.0 + ez))
+
+
+def shared_expert(qg, dg, qu, du, qd, dd, qsg, dsg, x, base, threads: int = 1):
+    """Shared expert of a routed MoE layer, added to the routed output:
+    out[t] = base[t] + sigmoid(w_sg . x_t) * W_down (silu(W_gate x_t) * W_up x_t).
+
+    The pages' MoE models run a dense expert on every token beside the
+    routed ones, scaled per token by its own sigmoid gate, and count that
+    gate's dot product among the decode kernels they fused (memra wiki,
+    board notes on the 35B MoE decode; memra performance, flip history).
+    The plain reading: the shared expert is an MLP of the routed experts'
+    shape (gate/up [F][H], down [H][F]); the gate is one row [1][H] whose
+    dot with x_t goes through a logistic sigmoid; the result is added to
+    the routed output.
+
+    fp64 throughout; the down GEMV takes h rounded to fp32 (the GPU's
+    activation dtype; the rounding is inside the 1e-6 * |h| term of h's
+    bound). Bound on an fp32 GPU result: with sg = sigmoid(gl) and b_sg =
+    0.25 * 1e-3 * A_gl + 1e-6 * sg (|sigma'| <= 1/4, plus fp32 exp, add and
+    division), and b_s = 1e-3 * A_down + |W_down| b_h (b_h from
+    gate_up_silu): |dout| <= sg * b_s + b_sg * |s| + b_sg * b_s
+    + 1e-6 * (|base| + sg * |s|).
+    Returns dict(out, bound, s, gate, h) with out [T][H], gate [T].
+    """
+    st = gate_up_silu(qg, dg, qu, du, x, threads)
+    s, As = gemv(qd, dd, st["h"].astype(np.float32), threads)
+    H = qd.shape[0]
+    wabs = (np.abs(qd.astype(np.int32)).astype(np.float64).reshape(H, -1, QK)
+            * dd.astype(np.float64)[:, :, None]).reshape(H, -1)
+    bs = REL_TOL * As + st["bh"] @ wabs.T
+    gl, Agl = gemv(qsg, dsg, x, threads)
+    sg = sigmoid(gl[:, 0])
+    bsg = 0.25 * REL_TOL * Agl[:, 0] + 1e-6 * sg
+    base = np.asarray(base, np.float64)
+    out = base + sg[:, None] * s
+    bound = (sg[:, None] * bs + bsg[:, None] * np.abs(s) + bsg[:, None] * bs
+             + 1e-6 * (np.abs(base) + sg[:, None] * np.abs(s)))
+    return dict(out=out, bound=bound, s=s, gate=sg, h=st["h"])
+
+
 # ---------------------------------------------------------------- masked LM head
 def argmax_masked(L_sub: np.ndarray, A_sub: np.ndarray, row_ids: np.ndarray):
     """Argmax over a ranked subset of the vocabulary (the pages' draft LM

@@ -552,3 +552,80 @@ def test_q4_0_synth_roundtrip():
     assert q.min() >= -8 and q.max() <= 7
     q2, d2 = oracle.decode_q4_0_blocks(synth.to_gguf_q4_0_blocks(q, d))
     assert np.array_equal(q2, q) and np.array_equal(d2.view(np.uint16), d.view(np.uint16))
+
+
+# ---------------------------------------------------------------- shared expert
+def test_sigmoid_closed_forms():
+    """sigma(0) = 1/2, sigma(ln 3) = 3/4, sigma(-ln 3) = 1/4,
+    sigma(z) + sigma(-z) = 1, and no overflow far out on either side."""
+    assert oracle.sigmoid(np.array([0.0]))[0] == 0.5
+    assert math.isclose(oracle.sigmoid(np.array([math.log(3.0)]))[0], 0.75, rel_tol=1e-15)
+    assert math.isclose(oracle.sigmoid(np.array([-math.log(3.0)]))[0], 0.25, rel_tol=1e-15)
+    z = np.array([-30.0, -2.5, -0.1, 0.7, 4.0, 30.0])
+    assert np.allclose(oracle.sigmoid(z) + oracle.sigmoid(-z), 1.0, rtol=0, atol=1e-15)
+    far = oracle.sigmoid(np.array([-1000.0, 1000.0]))
+    assert far[0] == 0.0 and far[1] == 1.0
+    # sigma' = sigma (1 - sigma): a central difference at z = 0.3
+    h = 1e-5
+    num = (oracle.sigmoid(np.array([0.3 + h]))[0] - oracle.sigmoid(np.array([0.3 - h]))[0]) / (2 * h)
+    s3 = oracle.sigmoid(np.array([0.3]))[0]
+    assert abs(num - s3 * (1 - s3)) < 1e-9
+
+
+def _shexp_case(seed, T=3, F=64, H=96, gate_row=None):
+    rng = np.random.default_rng(seed)
+    qg, dg = synth.draw_weights(rng, F, H)
+    qu, du = synth.draw_weights(rng, F, H)
+    qd, dd = synth.draw_weights(rng, H, F)
+    qsg, dsg = synth.draw_weights(rng, 1, H)
+    if gate_row is not None:
+        qsg, dsg = gate_row
+    x = synth.draw_x(rng, T, H)
+    base = rng.normal(0.0, 1.0, size=(T, H)).astype(np.float32)
+    return qg, dg, qu, du, qd, dd, qsg, dsg, x, base
+
+
+def test_shared_expert_equals_dense_composition():
+    """Against the same layer written with dequantised fp64 matrices and
+    numpy products: x -> silu(Wg x) * (Wu x) -> Wd (.) -> base + sigma(w.x) * (.)."""
+    qg, dg, qu, du, qd, dd, qsg, dsg, x, base = _shexp_case(4)
+    r = oracle.shared_expert(qg, dg, qu, du, qd, dd, qsg, dsg, x, base)
+    xf = x.astype(np.float64)
+    g = xf @ _dense(qg, dg).T
+    u = xf @ _dense(qu, du).T
+    h = (g / (1.0 + np.exp(-g))) * u
+    s = h.astype(np.float32).astype(np.float64) @ _dense(qd, dd).T
+    gl = xf @ _dense(qsg, dsg).T
+    ref = base.astype(np.float64) + s / (1.0 + np.exp(-gl))
+    assert np.allclose(r["out"], ref, rtol=1e-12, atol=1e-12)
+    assert np.all(r["bound"] > 0)
+
+
+def test_shared_expert_gate_extremes_select_base_or_sum():
+    """A gate row whose dot is +-40 (one quant of 1 with d = 40 against
+    x[0] = 1): sigma = 1 - 4e-18 or 4e-18, so out is base + s or base, up to
+    that margin; a flipped sign or a dropped gate fails one of them."""
+    H = 96
+    x0 = None
+    for sign, expect_s in ((1, True), (-1, False)):
+        qsg = np.zeros((1, H), np.int8)
+        qsg[0, 0] = sign
+        dsg = np.zeros((1, H // 32), np.float16)
+        dsg[0, 0] = 40.0
+        c = list(_shexp_case(9, gate_row=(qsg, dsg)))
+        c[8] = c[8].copy()
+        c[8][:, 0] = 1.0
+        r = oracle.shared_expert(*c)
+        base = c[9].astype(np.float64)
+        assert np.allclose(r["gate"], 1.0 if expect_s else 0.0, rtol=0, atol=1e-15)
+        want = base + r["s"] if expect_s else base
+        assert np.allclose(r["out"], want, rtol=0, atol=1e-12 * (1 + np.abs(r["s"]).max()))
+        if x0 is None:
+            x0 = r["s"]
+    assert np.abs(x0).max() > 1e-3  # the expert's output is not trivially zero
+
+
+def test_shared_expert_zero_down_returns_base_exactly():
+    qg, dg, qu, du, qd, dd, qsg, dsg, x, base = _shexp_case(5)
+    r = oracle.shared_expert(qg, dg, qu, du, np.zeros_like(qd), dd, qsg, dsg, x, base)
+    assert np.array_equal(r["out"], base.astype(np.float64))
