@@ -301,9 +301,34 @@ int q8_moe_topk_softmax(const float *logits, int T, int E, int topk, int32_t *ex
 /* Router from a Q8_0 router matrix Wr [E][K]: logits = Wr x (as q8_gemv
  * with fp32 output, so bitwise independent of T), then
  * q8_moe_topk_softmax. x [dev] [T][K] of x_dt; logits [dev] fp32 [T][E]
- * (written, caller-owned). Two launches on the stream. */
+ * (written, caller-owned). For 9..64 tokens over a Q8_0 matrix of at most
+ * 256 rows with fp16 x, one launch (one workgroup per token); otherwise
+ * the GEMV launches and the top-k launch. The outputs are the same either
+ * way (bitwise). */
 int q8_moe_router(const q8_matrix *Wr, const void *x, int x_dt, int T, int topk, float *logits,
                   int32_t *expert_ids, float *gate_w, void *stream);
+
+/* ------------------------------------------------------------ shared expert
+ * The dense expert that a routed layer runs on every token beside the
+ * routed ones, scaled per token by its own sigmoid gate and added to the
+ * routed output (the pages' MoE decode computes that per-layer gate as one
+ * fused dot: memra wiki, board notes on the 35B MoE decode; memra
+ * performance, flip history). For every token t:
+ *   out[t] += sigmoid(Wsg x_t) * Wd (silu(Wg x_t) * (Wu x_t))
+ * Wg, Wu [F][H] (one format), Wd [H][F], Wsg [1][H] (the gate row), any
+ * of Q8_0 / Q4_0. x [dev] [T][H] of x_dt; out [dev] fp32 [T][H], read and
+ * written (pass the routed output of q8_moe_ffn, or zeros); T >= 1.
+ * h = silu(g) * u is kept in fp32 and fed to Wd as fp32 activations; the
+ * gate is 1 / (1 + expf(-g)) in fp32. Each output is within the bound the
+ * oracle propagates from the GEMV bounds (sigma' <= 1/4).
+ *   ws [dev] at least q8_moe_shared_ws_bytes(F, H, T) bytes, 16-byte
+ *   aligned, caller-owned scratch (h, the gate logits and the expert's
+ *   output; no zero-fill needed). Launches: the SiLU pair and the gate
+ *   GEMV per pass of up to 8 tokens, the down GEMV per pass, one add. */
+size_t q8_moe_shared_ws_bytes(int64_t F, int64_t H, int T);
+int q8_moe_shared_expert(const q8_matrix *Wg, const q8_matrix *Wu, const q8_matrix *Wd,
+                         const q8_matrix *Wsg, const void *x, int x_dt, int T, float *out,
+                         void *ws, size_t ws_bytes, void *stream);
 
 #ifdef __cplusplus
 }

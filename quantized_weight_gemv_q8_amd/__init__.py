@@ -33,7 +33,7 @@ EXPORTS = (
     "q8_gemv", "q8_gemv_pair", "q8_gemv_pair_silu", "q8_lmhead_ws_bytes", "q8_lmhead_argmax",
     "q8_lmhead_argmax_rows",
     "q8_moe_ws_bytes", "q8_moe_ws_layout", "q8_moe_gemv", "q8_moe_ffn", "q8_moe_topk_softmax",
-    "q8_moe_router",
+    "q8_moe_router", "q8_moe_shared_ws_bytes", "q8_moe_shared_expert",
 )
 
 
@@ -92,6 +92,8 @@ def lib() -> ctypes.CDLL:
             "q8_moe_ffn": ([pb, pb, pb, vp, vp, vp, i32, vp, i32, i32, vp, sz, vp], i32),
             "q8_moe_topk_softmax": ([vp, i32, i32, i32, vp, vp, vp], i32),
             "q8_moe_router": ([pm, vp, i32, i32, i32, vp, vp, vp, vp], i32),
+            "q8_moe_shared_ws_bytes": ([i64, i64, i32], sz),
+            "q8_moe_shared_expert": ([pm, pm, pm, pm, vp, i32, i32, vp, vp, sz, vp], i32),
         }
         for name, (args, res) in sig.items():
             fn = getattr(L, name)
@@ -463,3 +465,28 @@ def moe_router(Wr: PackedQ8, x, topk: int, logits=None, ids=None, gate_w=None, s
                                logits.data_ptr(), ids.data_ptr(), gate_w.data_ptr(),
                                _stream(stream)), "q8_moe_router")
     return logits, ids, gate_w
+
+
+def moe_shared_ws_bytes(F: int, H: int, T: int) -> int:
+    return lib().q8_moe_shared_ws_bytes(F, H, T)
+
+
+def moe_shared_expert(Wg: PackedQ8, Wu: PackedQ8, Wd: PackedQ8, Wsg: PackedQ8, x, out,
+                      ws=None, stream=None):
+    """Shared expert added in place to ``out`` (fp32 [T][H], e.g. the routed
+    output): out[t] += sigmoid(Wsg x_t) * Wd (silu(Wg x_t) * Wu x_t).
+    Returns ``out``."""
+    import torch
+    x = _as_2d(x, Wg.K)
+    T = x.shape[0]
+    if out.dtype != torch.float32 or tuple(out.shape) != (T, Wg.K):
+        raise ValueError("out must be fp32 [T][H]")
+    nws = moe_shared_ws_bytes(Wg.M, Wg.K, T)
+    if ws is None:
+        ws = torch.empty((nws,), dtype=torch.uint8, device=x.device)
+    _check(lib().q8_moe_shared_expert(ctypes.byref(Wg.cmat()), ctypes.byref(Wu.cmat()),
+                                      ctypes.byref(Wd.cmat()), ctypes.byref(Wsg.cmat()),
+                                      x.data_ptr(), _dt(x), T, out.data_ptr(), ws.data_ptr(),
+                                      ws.numel() * ws.element_size(), _stream(stream)),
+           "q8_moe_shared_expert")
+    return out

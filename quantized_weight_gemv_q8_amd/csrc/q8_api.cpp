@@ -497,6 +497,76 @@ int q8_moe_ffn(const q8_bank* gate, const q8_bank* up, const q8_bank* down,
   return launch_rc(q8::launch_moe_combine(expert_ids, E, gate_w, w.y_pair, out, T, topk, H, s));
 }
 
+// ------------------------------------------------------------ shared expert
+// Workspace: h [T][F], the gate logits [T] and the expert's output [T][H],
+// fp32, each area 256-byte aligned.
+static void shared_ws_layout(int64_t F, int64_t H, int T, size_t off[3], size_t* total) {
+  auto up = [](size_t b) { return (b + 255) / 256 * 256; };
+  off[0] = 0;
+  off[1] = up((size_t)T * F * 4);
+  off[2] = off[1] + up((size_t)T * 4);
+  *total = off[2] + up((size_t)T * H * 4);
+}
+
+size_t q8_moe_shared_ws_bytes(int64_t F, int64_t H, int T) {
+  if (F < 1 || H < 1 || T < 1) return 0;
+  size_t off[3], total;
+  shared_ws_layout(F, H, T, off, &total);
+  return total;
+}
+
+int q8_moe_shared_expert(const q8_matrix* Wg, const q8_matrix* Wu, const q8_matrix* Wd,
+                         const q8_matrix* Wsg, const void* x, int x_dt, int T, float* out,
+                         void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_matrix(Wg);
+  if (rc) return rc;
+  if ((rc = check_matrix(Wu)) || (rc = check_matrix(Wd)) || (rc = check_matrix(Wsg))) return rc;
+  const int64_t F = Wg->M, H = Wg->K;
+  if (Wu->M != F || Wu->K != H || Wd->M != H || Wd->K != F || Wsg->M != 1 || Wsg->K != H)
+    return Q8_ERR_SHAPE;
+  if (Wu->format != Wg->format) return Q8_ERR_DTYPE;
+  if (!x || !out) return Q8_ERR_NULL;
+  if (T < 1) return Q8_ERR_SHAPE;
+  const size_t xs = dt_size(x_dt);
+  if (!xs) return Q8_ERR_DTYPE;
+  if (!aligned(x, 16) || !aligned(out, 4)) return Q8_ERR_ALIGN;
+  if (!ws || !aligned(ws, 16) || ws_bytes < q8_moe_shared_ws_bytes(F, H, T))
+    return Q8_ERR_WORKSPACE;
+  const size_t xbytes = (size_t)T * H * xs, obytes = (size_t)T * H * 4;
+  if (overlap(x, xbytes, out, obytes) || overlap(ws, ws_bytes, x, xbytes) ||
+      overlap(ws, ws_bytes, out, obytes))
+    return Q8_ERR_ALIAS;
+  const DevInfo* dev = nullptr;
+  rc = current_device(&dev);
+  if (rc) return rc;
+  const bool xf = x_dt == Q8_DT_F32;
+  const int pass_h = q8::max_tokens_per_pass(*dev, H, xf);
+  const int pass_f = q8::max_tokens_per_pass(*dev, F, true);
+  if (pass_h < 1 || pass_f < 1) return Q8_ERR_SHAPE;
+  size_t off[3], total;
+  shared_ws_layout(F, H, T, off, &total);
+  float* h = (float*)((char*)ws + off[0]);
+  float* gl = (float*)((char*)ws + off[1]);
+  float* sx = (float*)((char*)ws + off[2]);
+  const HMat G = to_h(Wg), U = to_h(Wu), D = to_h(Wd), SG = to_h(Wsg);
+  hipStream_t s = (hipStream_t)stream;
+  for (int n0 = 0; n0 < T; n0 += pass_h) {
+    const int nt = T - n0 < pass_h ? T - n0 : pass_h;
+    const char* xp = (const char*)x + (size_t)n0 * H * xs;
+    if (q8::launch_glu(*dev, G, U, xp, xf, h + (size_t)n0 * F, false, nt, s) != hipSuccess ||
+        q8::launch_gemv(*dev, SG, nullptr, xp, xf, H, gl + n0, nullptr, false, nt, s) !=
+            hipSuccess)
+      return Q8_ERR_LAUNCH;
+  }
+  for (int n0 = 0; n0 < T; n0 += pass_f) {
+    const int nt = T - n0 < pass_f ? T - n0 : pass_f;
+    if (q8::launch_gemv(*dev, D, nullptr, h + (size_t)n0 * F, true, F, sx + (size_t)n0 * H,
+                        nullptr, false, nt, s) != hipSuccess)
+      return Q8_ERR_LAUNCH;
+  }
+  return launch_rc(q8::launch_shared_gate_add(gl, sx, out, T, H, s));
+}
+
 // ------------------------------------------------------------ router
 static int check_topk(const float* logits, int T, int E, int topk, const int32_t* ids,
                       const float* gate_w) {

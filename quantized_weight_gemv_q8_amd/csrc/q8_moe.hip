@@ -594,6 +594,28 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(const int32_t* ids, in
   for (int i = 0; i < nv; ++i) out[(int64_t)t * M + m0 + i] = acc[i];
 }
 
+// Shared expert: out[t][m] += sigmoid(gl[t]) * s[t][m], four outputs per
+// thread (the gate is computed once per thread; fp32 expf, add, divide).
+__global__ __launch_bounds__(256) void shared_gate_add_kernel(const float* gl, const float* sx,
+                                                             float* out, int64_t H) {
+  const int64_t t = blockIdx.y;
+  const int64_t m0 = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+  if (m0 >= H) return;
+  const float g = 1.0f / (1.0f + expf(-gl[t]));
+  const float* src = sx + t * H + m0;
+  float* dst = out + t * H + m0;
+  const int n = H - m0 < 4 ? (int)(H - m0) : 4;
+  float v[4], o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[i] = i < n ? src[i] : 0.0f;
+    o[i] = i < n ? dst[i] : 0.0f;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if (i < n) dst[i] = __builtin_fmaf(g, v[i], o[i]);
+}
+
 // ---------------------------------------------------------------- host side
 static int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
 
@@ -728,6 +750,14 @@ hipError_t launch_moe_gate_up(const DevInfo& dev, const HBank& G, const HBank& U
           dev, G, U, ws, topk, xp, ldx_bytes, h, rq, s);
     }
   });
+}
+
+hipError_t launch_shared_gate_add(const float* gl, const float* sx, float* out, int T, int64_t H,
+                                  hipStream_t s) {
+  void* args[] = {(void*)&gl, (void*)&sx, &out, &H};
+  const unsigned gx = (unsigned)(((H + 3) / 4 + 255) / 256);
+  return hipLaunchKernel((const void*)shared_gate_add_kernel, dim3(gx, (unsigned)T), dim3(256),
+                         args, 0, s);
 }
 
 hipError_t launch_moe_combine(const int32_t* ids, int E, const float* gate_w,

@@ -258,3 +258,39 @@ def test_valid_call_without_gfx950_is_refused(L):
         pytest.skip("a gfx950 device is present; this check is for hosts without one")
     assert gemv_rc(L) == -6
     assert L.q8_device_check(0) == -6
+
+
+def test_shared_expert_validation(L):
+    """q8_moe_shared_expert refuses bad arguments before touching the
+    device: shapes that do not chain (Wg/Wu [F][H], Wd [H][F], Wsg [1][H]),
+    mixed gate/up formats, null pointers, a short or misaligned workspace
+    and overlapping buffers."""
+    F, H, T = 64, 256, 3
+    g, u = _mat(M=F, K=H), _mat(M=F, K=H)
+    dn, sg = _mat(M=H, K=F), _mat(M=1, K=H)
+    n = L.q8_moe_shared_ws_bytes(F, H, T)
+    assert n >= 4 * (T * F + T + T * H)
+    assert L.q8_moe_shared_ws_bytes(0, H, T) == 0
+    ok = dict(g=g, u=u, d=dn, s=sg, x=X, xdt=1, T=T, out=Y, ws=WS, nws=n)
+
+    def rc(**kw):
+        a = dict(ok, **kw)
+        return L.q8_moe_shared_expert(ctypes.byref(a["g"]), ctypes.byref(a["u"]),
+                                      ctypes.byref(a["d"]), ctypes.byref(a["s"]), a["x"],
+                                      a["xdt"], a["T"], a["out"], a["ws"], a["nws"], None)
+    assert rc(x=0) == -1
+    assert rc(out=0) == -1
+    assert rc(d=_mat(M=H, K=2 * F)) == -2  # down does not take h
+    assert rc(s=_mat(M=2, K=H)) == -2      # the gate is one row
+    assert rc(u=_mat(M=F, K=2 * H)) == -2
+    assert rc(T=0) == -2
+    assert rc(xdt=9) == -4
+    q4u = _mat(M=F, K=H)
+    q4u.format = q8.Q8_FMT_Q4_0
+    assert rc(u=q4u) == -4                 # gate and up in one format
+    assert rc(ws=0) == -5
+    assert rc(nws=n - 1) == -5
+    assert rc(ws=WS + 8) == -5
+    assert rc(x=X + 8) == -3
+    assert rc(out=X) == -8                 # out over x
+    assert rc(ws=Y) == -8                  # workspace over out
