@@ -322,9 +322,10 @@ int q8_moe_router(const q8_matrix *Wr, const void *x, int x_dt, int T, int topk,
  * gate is 1 / (1 + expf(-g)) in fp32. Each output is within the bound the
  * oracle propagates from the GEMV bounds (sigma' <= 1/4).
  *   ws [dev] at least q8_moe_shared_ws_bytes(F, H, T) bytes, 16-byte
- *   aligned, caller-owned scratch (h, the gate logits and the expert's
- *   output; no zero-fill needed). Launches: the SiLU pair and the gate
- *   GEMV per pass of up to 8 tokens, the down GEMV per pass, one add. */
+ *   aligned, caller-owned scratch (h and the expert's output; no zero-fill
+ *   needed). Launches: the SiLU pair per pass of up to 8 tokens, the down
+ *   GEMV per pass, then one launch that computes each token's gate dot and
+ *   adds the gated output. */
 size_t q8_moe_shared_ws_bytes(int64_t F, int64_t H, int T);
 int q8_moe_shared_expert(const q8_matrix *Wg, const q8_matrix *Wu, const q8_matrix *Wd,
                          const q8_matrix *Wsg, const void *x, int x_dt, int T, float *out,

@@ -498,19 +498,18 @@ int q8_moe_ffn(const q8_bank* gate, const q8_bank* up, const q8_bank* down,
 }
 
 // ------------------------------------------------------------ shared expert
-// Workspace: h [T][F], the gate logits [T] and the expert's output [T][H],
-// fp32, each area 256-byte aligned.
-static void shared_ws_layout(int64_t F, int64_t H, int T, size_t off[3], size_t* total) {
+// Workspace: h [T][F] and the expert's output [T][H], fp32, each area
+// 256-byte aligned.
+static void shared_ws_layout(int64_t F, int64_t H, int T, size_t off[2], size_t* total) {
   auto up = [](size_t b) { return (b + 255) / 256 * 256; };
   off[0] = 0;
   off[1] = up((size_t)T * F * 4);
-  off[2] = off[1] + up((size_t)T * 4);
-  *total = off[2] + up((size_t)T * H * 4);
+  *total = off[1] + up((size_t)T * H * 4);
 }
 
 size_t q8_moe_shared_ws_bytes(int64_t F, int64_t H, int T) {
   if (F < 1 || H < 1 || T < 1) return 0;
-  size_t off[3], total;
+  size_t off[2], total;
   shared_ws_layout(F, H, T, off, &total);
   return total;
 }
@@ -543,19 +542,16 @@ int q8_moe_shared_expert(const q8_matrix* Wg, const q8_matrix* Wu, const q8_matr
   const int pass_h = q8::max_tokens_per_pass(*dev, H, xf);
   const int pass_f = q8::max_tokens_per_pass(*dev, F, true);
   if (pass_h < 1 || pass_f < 1) return Q8_ERR_SHAPE;
-  size_t off[3], total;
+  size_t off[2], total;
   shared_ws_layout(F, H, T, off, &total);
   float* h = (float*)((char*)ws + off[0]);
-  float* gl = (float*)((char*)ws + off[1]);
-  float* sx = (float*)((char*)ws + off[2]);
+  float* sx = (float*)((char*)ws + off[1]);
   const HMat G = to_h(Wg), U = to_h(Wu), D = to_h(Wd), SG = to_h(Wsg);
   hipStream_t s = (hipStream_t)stream;
   for (int n0 = 0; n0 < T; n0 += pass_h) {
     const int nt = T - n0 < pass_h ? T - n0 : pass_h;
     const char* xp = (const char*)x + (size_t)n0 * H * xs;
-    if (q8::launch_glu(*dev, G, U, xp, xf, h + (size_t)n0 * F, false, nt, s) != hipSuccess ||
-        q8::launch_gemv(*dev, SG, nullptr, xp, xf, H, gl + n0, nullptr, false, nt, s) !=
-            hipSuccess)
+    if (q8::launch_glu(*dev, G, U, xp, xf, h + (size_t)n0 * F, false, nt, s) != hipSuccess)
       return Q8_ERR_LAUNCH;
   }
   for (int n0 = 0; n0 < T; n0 += pass_f) {
@@ -564,7 +560,7 @@ int q8_moe_shared_expert(const q8_matrix* Wg, const q8_matrix* Wu, const q8_matr
                         nullptr, false, nt, s) != hipSuccess)
       return Q8_ERR_LAUNCH;
   }
-  return launch_rc(q8::launch_shared_gate_add(gl, sx, out, T, H, s));
+  return launch_rc(q8::launch_shared_gate_add(SG, x, xf, sx, out, T, H, s));
 }
 
 // ------------------------------------------------------------ router

@@ -144,9 +144,10 @@ constexpr int kRouterFusedMinT = 9;
 constexpr int kRouterFusedMaxT = 64;
 hipError_t launch_router(const DevInfo& dev, const HMat& Wr, const void* x, bool x_f32, int T,
                          int topk, float* logits, int32_t* ids, float* gate_w, hipStream_t s);
-// Shared expert's last step: out[t][m] += sigmoid(gl[t]) * sx[t][m].
-hipError_t launch_shared_gate_add(const float* gl, const float* sx, float* out, int T, int64_t H,
-                                  hipStream_t s);
+// Shared expert's last step: out[t][m] += sigmoid(Wsg x_t) * sx[t][m], the
+// gate row's dot computed in the same launch (Wsg one row of H).
+hipError_t launch_shared_gate_add(const HMat& Wsg, const void* x, bool x_f32, const float* sx,
+                                  float* out, int T, int64_t H, hipStream_t s);
 // out[t] = sum_j gate_w[t][j] * y_pair[t*topk + j] (slots with invalid ids skipped).
 hipError_t launch_moe_combine(const int32_t* ids, int E, const float* gate_w,
                               const float* y_pair, float* out, int T, int topk, int64_t M,

@@ -269,7 +269,7 @@ def test_shared_expert_validation(L):
     g, u = _mat(M=F, K=H), _mat(M=F, K=H)
     dn, sg = _mat(M=H, K=F), _mat(M=1, K=H)
     n = L.q8_moe_shared_ws_bytes(F, H, T)
-    assert n >= 4 * (T * F + T + T * H)
+    assert n >= 4 * (T * F + T * H)  # h and the expert output, fp32
     assert L.q8_moe_shared_ws_bytes(0, H, T) == 0
     ok = dict(g=g, u=u, d=dn, s=sg, x=X, xdt=1, T=T, out=Y, ws=WS, nws=n)
 
