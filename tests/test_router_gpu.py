@@ -154,6 +154,8 @@ def test_routed_layer_graph_replays_match_eager(routed_layer):
     (12, 64, 2048, False, False, 4),    # 4 rows per team, keys in one register per lane
     (13, 200, 512, False, False, 16),   # 32 lanes per row, ragged last wave
     (17, 256, 256, False, False, 64),   # 16 lanes per row, topk at its maximum
+    (9, 9, 256, False, False, 9),       # topk = E = 9: three waves, every expert picked
+    (64, 256, 512, False, False, 64),   # 64 tokens, four keys per lane
     (7, 256, 256, False, False, 64),    # fewer than 9 tokens: two launches
     (65, 128, 2048, False, False, 8),   # one token more: GEMV then top-k launch
     (64, 128, 2048, False, True, 8),    # fp32 x: two launches
