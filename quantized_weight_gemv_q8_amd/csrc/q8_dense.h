@@ -106,7 +106,8 @@ hipError_t launch_gemv_once(int nt, const DevInfo& dev, const DenseMap& map, con
                             int fmt, int lpr, bool x_f32, const char* x, int64_t ldx_bytes, int C,
                             hipStream_t s);
 
-// The same for the gate/up + SiLU pair (2M virtual rows), nt = 1 or 2.
+// The same for the gate/up + SiLU pair (2M virtual rows), nt = 1..8 (from
+// 3 tokens only when every group fits in the resident waves).
 hipError_t launch_glu_once(int nt, const DevInfo& dev, const GluMap& map, const GluEpi& epi,
                            int fmt, int lpr, bool x_f32, const char* x, int64_t ldx_bytes, int C,
                            hipStream_t s);

@@ -118,7 +118,7 @@ hipError_t launch_glu(const DevInfo& dev, const HMat& Gm, const HMat& Um, const 
   const int C = (int)chunks_per_row(Gm.fmt, Gm.K);
   const int64_t ldx_bytes = Gm.K * (x_f32 ? 4 : 2);
   const char* xp = (const char*)x;
-  if (nt <= 2) {
+  {
     const hipError_t e = launch_glu_once(nt, dev, map, epi, Gm.fmt, lanes_for(Gm.fmt, Gm.K), x_f32,
                                          xp, ldx_bytes, C, s);
     if (e != hipErrorNotSupported) return e;

@@ -196,5 +196,17 @@ hipError_t launch_glu_once_nt1(const DevInfo&, const GluMap&, const GluEpi&, int
                               const char*, int64_t, int, hipStream_t);
 hipError_t launch_glu_once_nt2(const DevInfo&, const GluMap&, const GluEpi&, int, int, bool,
                               const char*, int64_t, int, hipStream_t);
+hipError_t launch_glu_once_nt3(const DevInfo&, const GluMap&, const GluEpi&, int, int, bool,
+                              const char*, int64_t, int, hipStream_t);
+hipError_t launch_glu_once_nt4(const DevInfo&, const GluMap&, const GluEpi&, int, int, bool,
+                              const char*, int64_t, int, hipStream_t);
+hipError_t launch_glu_once_nt5(const DevInfo&, const GluMap&, const GluEpi&, int, int, bool,
+                              const char*, int64_t, int, hipStream_t);
+hipError_t launch_glu_once_nt6(const DevInfo&, const GluMap&, const GluEpi&, int, int, bool,
+                              const char*, int64_t, int, hipStream_t);
+hipError_t launch_glu_once_nt7(const DevInfo&, const GluMap&, const GluEpi&, int, int, bool,
+                              const char*, int64_t, int, hipStream_t);
+hipError_t launch_glu_once_nt8(const DevInfo&, const GluMap&, const GluEpi&, int, int, bool,
+                              const char*, int64_t, int, hipStream_t);
 
 }  // namespace q8

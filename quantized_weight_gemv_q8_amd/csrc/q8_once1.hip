@@ -37,6 +37,12 @@ hipError_t launch_glu_once(int nt, const DevInfo& dev, const GluMap& map, const 
   switch (nt) {
     case 1: return launch_glu_once_nt1(dev, map, epi, fmt, lpr, x_f32, x, ldx_bytes, C, s);
     case 2: return launch_glu_once_nt2(dev, map, epi, fmt, lpr, x_f32, x, ldx_bytes, C, s);
+    case 3: return launch_glu_once_nt3(dev, map, epi, fmt, lpr, x_f32, x, ldx_bytes, C, s);
+    case 4: return launch_glu_once_nt4(dev, map, epi, fmt, lpr, x_f32, x, ldx_bytes, C, s);
+    case 5: return launch_glu_once_nt5(dev, map, epi, fmt, lpr, x_f32, x, ldx_bytes, C, s);
+    case 6: return launch_glu_once_nt6(dev, map, epi, fmt, lpr, x_f32, x, ldx_bytes, C, s);
+    case 7: return launch_glu_once_nt7(dev, map, epi, fmt, lpr, x_f32, x, ldx_bytes, C, s);
+    case 8: return launch_glu_once_nt8(dev, map, epi, fmt, lpr, x_f32, x, ldx_bytes, C, s);
   }
   return hipErrorNotSupported;
 }

@@ -1,4 +1,4 @@
-// q8_once8.hip -- one-group-per-wave dense GEMV kernels for 8-token passes.
+// q8_once8.hip -- one-group-per-wave dense GEMV and SiLU-pair kernels for 8-token passes.
 #include "q8_once.hpp"
 
 namespace q8 {
@@ -7,6 +7,12 @@ hipError_t launch_once_nt8(const DevInfo& dev, const DenseMap& map, const DenseE
                              int lpr, bool x_f32, const char* x, int64_t ldx_bytes, int C,
                              hipStream_t s) {
   return launch_once_nt<DenseKind, 8>(dev, map, epi, fmt, lpr, x_f32, x, ldx_bytes, C, s);
+}
+
+hipError_t launch_glu_once_nt8(const DevInfo& dev, const GluMap& map, const GluEpi& epi, int fmt,
+                              int lpr, bool x_f32, const char* x, int64_t ldx_bytes, int C,
+                              hipStream_t s) {
+  return launch_once_nt<GluKind, 8>(dev, map, epi, fmt, lpr, x_f32, x, ldx_bytes, C, s);
 }
 
 }  // namespace q8

@@ -149,3 +149,31 @@ def test_streaming_silu_pair():
     rows = sampled_rows(M, 2)
     r = oracle.gate_up_silu(qg[rows], dg[rows], qu[rows], du[rows], x[:2], threads())
     assert np.all(np.abs(h5[:2, rows] - r["h"]) <= r["bh"])
+
+
+@pytest.mark.parametrize("M,K,q4,xf32", [(768, 2048, False, False), (1408, 1024, True, False),
+                                         (300, 96, False, True)])
+def test_silu_pair_resident_3_to_8_tokens(M, K, q4, xf32):
+    """The SiLU pair's one-group kernel at 3-8 tokens (taken when every
+    group fits the resident waves): each token's h is bitwise its one-token
+    result, and all of h is within the oracle's propagated bound."""
+    note(f"one-group SiLU pair {M}x{K} q4={q4} xf32={xf32} N=3..8")
+    rng = np.random.default_rng(M + K)
+    draw = synth.draw_weights_q4_0 if q4 else synth.draw_weights
+    qg, dg = draw(rng, M, K)
+    qu, du = draw(rng, M, K)
+    x = synth.draw_x(rng, 8, K)
+    if xf32:
+        x = x.astype(np.float32)
+    if q4:
+        Wg = q8.pack_q4_0(synth.to_gguf_q4_0_blocks(qg, dg))
+        Wu = q8.pack_q4_0(synth.to_gguf_q4_0_blocks(qu, du))
+    else:
+        Wg, Wu = upload(qg, dg), upload(qu, du)
+    singles = [host(q8.gemv_pair_silu(Wg, Wu, dev(x[n:n + 1])))[0] for n in range(8)]
+    r = oracle.gate_up_silu(qg, dg, qu, du, x, threads())
+    for N in range(3, 9):
+        h = host(q8.gemv_pair_silu(Wg, Wu, dev(x[:N])))
+        for n in range(N):
+            assert np.array_equal(h[n].view(np.uint32), singles[n].view(np.uint32)), (N, n)
+        assert np.all(np.abs(h - r["h"][:N]) <= r["bh"][:N]), f"N={N}"
