@@ -22,6 +22,8 @@
 //  rows     the same over a bank: y_pair[p] = W[e] x_p (the down
 //           projection, or a single routed GEMV).
 //  combine  out[t] = sum_j gate_w[t][j] * y_pair[t*topk + j], ascending j.
+//  shared   the shared expert's last step: each token's gate dot w_sg . x_t,
+//           its sigmoid, and out[t] += sigmoid * (the dense expert's output).
 // Per-(row, token) arithmetic is the engine's, which does not depend on
 // how many tokens an expert received or which slot they landed in, so a
 // token's result is independent of the rest of the batch.

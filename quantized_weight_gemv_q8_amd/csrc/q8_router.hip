@@ -7,15 +7,18 @@
 // token: the topk experts with the largest router logits (descending,
 // equal logits to the lower expert index, -0 equal to +0) and softmax
 // weights over the picked logits. One wave owns one token, so a token's
-// result cannot depend on the batch.
+// result cannot depend on the batch. From a Q8_0 router matrix, 9 to 64
+// tokens run as one launch (router_kernel: one workgroup per token, the
+// logits kept in LDS); other shapes take the GEMV, then topk_softmax_kernel.
 //
 // Selection: every logit becomes a 64-bit key, (order-preserving bits of
 // the fp32 value) << 32 | ~expert, so the largest key is the largest
 // logit and, among equal logits, the lowest expert. Each lane keeps the
-// best key of its own experts (expert e belongs to lane e % 64); a pick is
-// a wave maximum, after which only the owner of the picked expert rescans
-// its (at most 64) experts. The wave maximum runs on DPP moves and
-// readlanes (wave_max_u64), not on shuffles through the LDS crossbar.
+// keys of its own experts (expert e belongs to lane e % 64); a pick is a
+// wave maximum, after which the owner of the picked expert drops it: up to
+// 256 experts the keys stay in registers, beyond that the owner rescans
+// its (at most 64) experts from LDS. The wave maximum runs on DPP moves
+// and readlanes (wave_max_u64), not on shuffles through the LDS crossbar.
 #include "q8_engine.hpp"
 #include "q8_internal.h"
 
