@@ -469,7 +469,9 @@ __device__ __forceinline__ void routed_slices(const int32_t* vslots, int nv, con
 // Occupancy request: 6 waves per SIMD (80 VGPRs) for Q8_0 with fp16
 // activations, which the kernels meet without spilling (measured faster
 // than the 5 waves the allocator picks unasked); 4 (128 VGPRs) for the
-// heavier fp32 or Q4_0 variants.
+// heavier fp32 or Q4_0 variants. For the fp32-activation down projection
+// of the E = 128 top-8 layer, 5 and 6 waves took the layer from 89.8 us
+// to 95.5 and 124.4 us (same-process A/B on MI355X).
 template <int F, bool XF32>
 constexpr int moe_waves() {
   return (XF32 || F == kFmtQ4) ? 4 : 6;
