@@ -479,8 +479,8 @@ def moe_shared_expert(Wg: PackedQ8, Wu: PackedQ8, Wd: PackedQ8, Wsg: PackedQ8, x
     import torch
     x = _as_2d(x, Wg.K)
     T = x.shape[0]
-    if out.dtype != torch.float32 or tuple(out.shape) != (T, Wg.K):
-        raise ValueError("out must be fp32 [T][H]")
+    if out.dtype != torch.float32 or tuple(out.shape) != (T, Wg.K) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous fp32 [T][H] tensor")
     nws = moe_shared_ws_bytes(Wg.M, Wg.K, T)
     if ws is None:
         ws = torch.empty((nws,), dtype=torch.uint8, device=x.device)

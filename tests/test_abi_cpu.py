@@ -294,3 +294,16 @@ def test_shared_expert_validation(L):
     assert rc(x=X + 8) == -3
     assert rc(out=X) == -8                 # out over x
     assert rc(ws=Y) == -8                  # workspace over out
+
+
+def test_shared_expert_binding_rejects_bad_out():
+    """The Python binding refuses an out that is not a contiguous fp32
+    [T][H] tensor before calling the library."""
+    import torch
+    W = q8.PackedQ8(torch.zeros(64 * 256, dtype=torch.int8), torch.zeros(64 * 8, dtype=torch.int16),
+                    64, 256)
+    x = torch.zeros((2, 256), dtype=torch.float16)
+    for bad in (torch.zeros((256, 2)).t(), torch.zeros((2, 256), dtype=torch.float16),
+                torch.zeros((3, 256))):
+        with pytest.raises(ValueError):
+            q8.moe_shared_expert(W, W, W, W, x, bad)
