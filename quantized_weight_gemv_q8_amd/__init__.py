@@ -282,6 +282,21 @@ def _stream(stream=None) -> int:
     return s.cuda_stream
 
 
+def _need(t, shape, dtypes, name):
+    """Caller-provided buffers must match what the call writes or reads:
+    a contiguous tensor of exactly this shape and one of these dtypes."""
+    import torch
+    if (not isinstance(t, torch.Tensor) or tuple(t.shape) != tuple(shape) or t.dtype not in dtypes
+            or not t.is_contiguous()):
+        names = "/".join(str(d).replace("torch.", "") for d in dtypes)
+        raise ValueError(f"{name} must be a contiguous {names} tensor of shape {tuple(shape)}")
+    return t
+
+
+def _f(torch):
+    return (torch.float32, torch.float16)
+
+
 def _as_2d(x, K):
     if x.dim() == 1:
         x = x.view(1, -1)
@@ -297,6 +312,7 @@ def gemv(W: PackedQ8, x, out=None, out_dtype=None, stream=None):
     N = x.shape[0]
     if out is None:
         out = torch.empty((N, W.M), dtype=out_dtype or torch.float32, device=x.device)
+    _need(out, (N, W.M), _f(torch), "out")
     _check(lib().q8_gemv(ctypes.byref(W.cmat()), x.data_ptr(), _dt(x), out.data_ptr(), _dt(out), N,
                          _stream(stream)), "q8_gemv")
     return out
@@ -314,6 +330,8 @@ def gemv_pair(Wa: PackedQ8, Wb: PackedQ8, x, out_a=None, out_b=None, out_dtype=N
         out_b = torch.empty((N, Wb.M), dtype=dt, device=x.device)
     if out_a.dtype != out_b.dtype:
         raise TypeError("out_a and out_b must share a dtype")
+    _need(out_a, (N, Wa.M), _f(torch), "out_a")
+    _need(out_b, (N, Wb.M), _f(torch), "out_b")
     _check(lib().q8_gemv_pair(ctypes.byref(Wa.cmat()), ctypes.byref(Wb.cmat()), x.data_ptr(),
                               _dt(x), out_a.data_ptr(), out_b.data_ptr(), _dt(out_a), N,
                               _stream(stream)), "q8_gemv_pair")
@@ -327,6 +345,7 @@ def gemv_pair_silu(Wg: PackedQ8, Wu: PackedQ8, x, out=None, out_dtype=None, stre
     N = x.shape[0]
     if out is None:
         out = torch.empty((N, Wg.M), dtype=out_dtype or torch.float32, device=x.device)
+    _need(out, (N, Wg.M), _f(torch), "out")
     _check(lib().q8_gemv_pair_silu(ctypes.byref(Wg.cmat()), ctypes.byref(Wu.cmat()), x.data_ptr(),
                                    _dt(x), out.data_ptr(), _dt(out), N, _stream(stream)),
            "q8_gemv_pair_silu")
@@ -350,17 +369,20 @@ def lmhead_argmax(W: PackedQ8, x, logits=True, ids=None, ws=None, stream=None, r
         logits = None
     if ids is None:
         ids = torch.empty((N,), dtype=torch.int32, device=x.device)
+    if logits is not None:
+        _need(logits, (N, W.M), (torch.float32,), "logits")
+    _need(ids, (N,), (torch.int32,), "ids")
     nws = lmhead_ws_bytes(W.M, N)
     if ws is None:
         ws = torch.zeros((nws,), dtype=torch.uint8, device=x.device)
+    _need(ws, (ws.numel(),), (torch.uint8,), "ws")
     lp = logits.data_ptr() if logits is not None else None
     nb = ws.numel() * ws.element_size()
     if row_ids is None:
         rc = lib().q8_lmhead_argmax(ctypes.byref(W.cmat()), x.data_ptr(), _dt(x), lp, ids.data_ptr(),
                                     N, ws.data_ptr(), nb, _stream(stream))
     else:
-        if row_ids.dtype != torch.int32 or row_ids.numel() != W.M:
-            raise ValueError("row_ids must be int32 with one entry per row of W")
+        _need(row_ids, (W.M,), (torch.int32,), "row_ids (one entry per row of W)")
         rc = lib().q8_lmhead_argmax_rows(ctypes.byref(W.cmat()), row_ids.data_ptr(), x.data_ptr(),
                                          _dt(x), lp, ids.data_ptr(), N, ws.data_ptr(), nb,
                                          _stream(stream))
@@ -402,12 +424,18 @@ def moe_gemv(W: PackedBank, expert_ids, x, gate_w=None, x_per_pair=False, out=No
     import torch
     T, topk = expert_ids.shape
     P = T * topk
+    _need(expert_ids, (T, topk), (torch.int32,), "expert_ids")
+    if gate_w is not None:
+        _need(gate_w, (T, topk), (torch.float32,), "gate_w")
+    _need(x, (P if x_per_pair else T, W.K), _f(torch), "x")
     if out is None:
         out = torch.empty((T if gate_w is not None else P, W.M), dtype=torch.float32,
                           device=x.device)
+    _need(out, (T if gate_w is not None else P, W.M), (torch.float32,), "out")
     nws = moe_ws_bytes(W.E, T, topk, 0, W.M)
     if ws is None:
         ws = torch.empty((nws,), dtype=torch.uint8, device=x.device)
+    _need(ws, (ws.numel(),), (torch.uint8,), "ws")
     _check(lib().q8_moe_gemv(ctypes.byref(W.cbank()), expert_ids.data_ptr(),
                              gate_w.data_ptr() if gate_w is not None else None, x.data_ptr(),
                              _dt(x), int(bool(x_per_pair)), out.data_ptr(), T, topk, ws.data_ptr(),
@@ -421,11 +449,16 @@ def moe_ffn(gate: PackedBank, up: PackedBank, down: PackedBank, expert_ids, gate
     import torch
     T, topk = expert_ids.shape
     H = gate.K
+    _need(expert_ids, (T, topk), (torch.int32,), "expert_ids")
+    _need(gate_w, (T, topk), (torch.float32,), "gate_w")
+    _need(x, (T, H), _f(torch), "x")
     if out is None:
         out = torch.empty((T, H), dtype=torch.float32, device=x.device)
+    _need(out, (T, H), (torch.float32,), "out")
     nws = moe_ws_bytes(gate.E, T, topk, gate.M, H)
     if ws is None:
         ws = torch.empty((nws,), dtype=torch.uint8, device=x.device)
+    _need(ws, (ws.numel(),), (torch.uint8,), "ws")
     _check(lib().q8_moe_ffn(ctypes.byref(gate.cbank()), ctypes.byref(up.cbank()),
                             ctypes.byref(down.cbank()), expert_ids.data_ptr(), gate_w.data_ptr(),
                             x.data_ptr(), _dt(x), out.data_ptr(), T, topk, ws.data_ptr(),
@@ -444,6 +477,8 @@ def moe_topk_softmax(logits, topk: int, ids=None, gate_w=None, stream=None):
         ids = torch.empty((T, topk), dtype=torch.int32, device=logits.device)
     if gate_w is None:
         gate_w = torch.empty((T, topk), dtype=torch.float32, device=logits.device)
+    _need(ids, (T, topk), (torch.int32,), "ids")
+    _need(gate_w, (T, topk), (torch.float32,), "gate_w")
     _check(lib().q8_moe_topk_softmax(logits.data_ptr(), T, E, topk, ids.data_ptr(),
                                      gate_w.data_ptr(), _stream(stream)), "q8_moe_topk_softmax")
     return ids, gate_w
@@ -461,6 +496,9 @@ def moe_router(Wr: PackedQ8, x, topk: int, logits=None, ids=None, gate_w=None, s
         ids = torch.empty((T, topk), dtype=torch.int32, device=x.device)
     if gate_w is None:
         gate_w = torch.empty((T, topk), dtype=torch.float32, device=x.device)
+    _need(logits, (T, Wr.M), (torch.float32,), "logits")
+    _need(ids, (T, topk), (torch.int32,), "ids")
+    _need(gate_w, (T, topk), (torch.float32,), "gate_w")
     _check(lib().q8_moe_router(ctypes.byref(Wr.cmat()), x.data_ptr(), _dt(x), T, topk,
                                logits.data_ptr(), ids.data_ptr(), gate_w.data_ptr(),
                                _stream(stream)), "q8_moe_router")

@@ -307,3 +307,31 @@ def test_shared_expert_binding_rejects_bad_out():
                 torch.zeros((3, 256))):
         with pytest.raises(ValueError):
             q8.moe_shared_expert(W, W, W, W, x, bad)
+
+
+def test_bindings_reject_mismatched_buffers():
+    """Every binding refuses a caller-provided buffer of the wrong shape,
+    dtype or layout before the library is called (a short buffer would
+    otherwise be written past its end)."""
+    import torch
+    W = q8.PackedQ8(torch.zeros(64 * 256, dtype=torch.int8), torch.zeros(64 * 8, dtype=torch.int16),
+                    64, 256)
+    x = torch.zeros((2, 256), dtype=torch.float16)
+    for bad in (torch.zeros((2, 63)), torch.zeros((64, 2)).t(), torch.zeros((2, 64), dtype=torch.int32)):
+        with pytest.raises(ValueError):
+            q8.gemv(W, x, out=bad)
+        with pytest.raises(ValueError):
+            q8.gemv_pair_silu(W, W, x, out=bad)
+        with pytest.raises(ValueError):
+            q8.gemv_pair(W, W, x, out_a=bad, out_b=bad)
+    with pytest.raises(ValueError):
+        q8.lmhead_argmax(W, x, logits=torch.zeros((2, 63)))
+    with pytest.raises(ValueError):
+        q8.lmhead_argmax(W, x, ids=torch.zeros((2,), dtype=torch.int64))
+    with pytest.raises(ValueError):
+        q8.lmhead_argmax(W, x, row_ids=torch.zeros((63,), dtype=torch.int32))
+    L = torch.zeros((2, 64))
+    with pytest.raises(ValueError):
+        q8.moe_topk_softmax(L, 8, ids=torch.zeros((2, 7), dtype=torch.int32))
+    with pytest.raises(ValueError):
+        q8.moe_router(W, x, 8, logits=torch.zeros((2, 63)))
