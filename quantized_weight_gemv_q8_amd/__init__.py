@@ -293,6 +293,18 @@ def _need(t, shape, dtypes, name):
     return t
 
 
+def _on_gpu(*args):
+    """Every tensor handed to a kernel (packed weights included) must live
+    in device memory: a host address would be read or written by the GPU."""
+    for a in args:
+        if a is None:
+            continue
+        ts = (a.qs, a.d) if isinstance(a, (PackedQ8, PackedBank)) else (a,)
+        for t in ts:
+            if not t.is_cuda:
+                raise ValueError("every tensor argument must be on the GPU")
+
+
 def _f(torch):
     return (torch.float32, torch.float16)
 
@@ -313,6 +325,7 @@ def gemv(W: PackedQ8, x, out=None, out_dtype=None, stream=None):
     if out is None:
         out = torch.empty((N, W.M), dtype=out_dtype or torch.float32, device=x.device)
     _need(out, (N, W.M), _f(torch), "out")
+    _on_gpu(W, x, out)
     _check(lib().q8_gemv(ctypes.byref(W.cmat()), x.data_ptr(), _dt(x), out.data_ptr(), _dt(out), N,
                          _stream(stream)), "q8_gemv")
     return out
@@ -332,6 +345,7 @@ def gemv_pair(Wa: PackedQ8, Wb: PackedQ8, x, out_a=None, out_b=None, out_dtype=N
         raise TypeError("out_a and out_b must share a dtype")
     _need(out_a, (N, Wa.M), _f(torch), "out_a")
     _need(out_b, (N, Wb.M), _f(torch), "out_b")
+    _on_gpu(Wa, Wb, x, out_a, out_b)
     _check(lib().q8_gemv_pair(ctypes.byref(Wa.cmat()), ctypes.byref(Wb.cmat()), x.data_ptr(),
                               _dt(x), out_a.data_ptr(), out_b.data_ptr(), _dt(out_a), N,
                               _stream(stream)), "q8_gemv_pair")
@@ -346,6 +360,7 @@ def gemv_pair_silu(Wg: PackedQ8, Wu: PackedQ8, x, out=None, out_dtype=None, stre
     if out is None:
         out = torch.empty((N, Wg.M), dtype=out_dtype or torch.float32, device=x.device)
     _need(out, (N, Wg.M), _f(torch), "out")
+    _on_gpu(Wg, Wu, x, out)
     _check(lib().q8_gemv_pair_silu(ctypes.byref(Wg.cmat()), ctypes.byref(Wu.cmat()), x.data_ptr(),
                                    _dt(x), out.data_ptr(), _dt(out), N, _stream(stream)),
            "q8_gemv_pair_silu")
@@ -378,11 +393,13 @@ def lmhead_argmax(W: PackedQ8, x, logits=True, ids=None, ws=None, stream=None, r
     _need(ws, (ws.numel(),), (torch.uint8,), "ws")
     lp = logits.data_ptr() if logits is not None else None
     nb = ws.numel() * ws.element_size()
+    if row_ids is not None:
+        _need(row_ids, (W.M,), (torch.int32,), "row_ids (one entry per row of W)")
+    _on_gpu(W, x, logits, ids, ws, row_ids)
     if row_ids is None:
         rc = lib().q8_lmhead_argmax(ctypes.byref(W.cmat()), x.data_ptr(), _dt(x), lp, ids.data_ptr(),
                                     N, ws.data_ptr(), nb, _stream(stream))
     else:
-        _need(row_ids, (W.M,), (torch.int32,), "row_ids (one entry per row of W)")
         rc = lib().q8_lmhead_argmax_rows(ctypes.byref(W.cmat()), row_ids.data_ptr(), x.data_ptr(),
                                          _dt(x), lp, ids.data_ptr(), N, ws.data_ptr(), nb,
                                          _stream(stream))
@@ -436,6 +453,7 @@ def moe_gemv(W: PackedBank, expert_ids, x, gate_w=None, x_per_pair=False, out=No
     if ws is None:
         ws = torch.empty((nws,), dtype=torch.uint8, device=x.device)
     _need(ws, (ws.numel(),), (torch.uint8,), "ws")
+    _on_gpu(W, expert_ids, gate_w, x, out, ws)
     _check(lib().q8_moe_gemv(ctypes.byref(W.cbank()), expert_ids.data_ptr(),
                              gate_w.data_ptr() if gate_w is not None else None, x.data_ptr(),
                              _dt(x), int(bool(x_per_pair)), out.data_ptr(), T, topk, ws.data_ptr(),
@@ -459,6 +477,7 @@ def moe_ffn(gate: PackedBank, up: PackedBank, down: PackedBank, expert_ids, gate
     if ws is None:
         ws = torch.empty((nws,), dtype=torch.uint8, device=x.device)
     _need(ws, (ws.numel(),), (torch.uint8,), "ws")
+    _on_gpu(gate, up, down, expert_ids, gate_w, x, out, ws)
     _check(lib().q8_moe_ffn(ctypes.byref(gate.cbank()), ctypes.byref(up.cbank()),
                             ctypes.byref(down.cbank()), expert_ids.data_ptr(), gate_w.data_ptr(),
                             x.data_ptr(), _dt(x), out.data_ptr(), T, topk, ws.data_ptr(),
@@ -479,6 +498,7 @@ def moe_topk_softmax(logits, topk: int, ids=None, gate_w=None, stream=None):
         gate_w = torch.empty((T, topk), dtype=torch.float32, device=logits.device)
     _need(ids, (T, topk), (torch.int32,), "ids")
     _need(gate_w, (T, topk), (torch.float32,), "gate_w")
+    _on_gpu(logits, ids, gate_w)
     _check(lib().q8_moe_topk_softmax(logits.data_ptr(), T, E, topk, ids.data_ptr(),
                                      gate_w.data_ptr(), _stream(stream)), "q8_moe_topk_softmax")
     return ids, gate_w
@@ -499,6 +519,7 @@ def moe_router(Wr: PackedQ8, x, topk: int, logits=None, ids=None, gate_w=None, s
     _need(logits, (T, Wr.M), (torch.float32,), "logits")
     _need(ids, (T, topk), (torch.int32,), "ids")
     _need(gate_w, (T, topk), (torch.float32,), "gate_w")
+    _on_gpu(Wr, x, logits, ids, gate_w)
     _check(lib().q8_moe_router(ctypes.byref(Wr.cmat()), x.data_ptr(), _dt(x), T, topk,
                                logits.data_ptr(), ids.data_ptr(), gate_w.data_ptr(),
                                _stream(stream)), "q8_moe_router")
@@ -522,6 +543,8 @@ def moe_shared_expert(Wg: PackedQ8, Wu: PackedQ8, Wd: PackedQ8, Wsg: PackedQ8, x
     nws = moe_shared_ws_bytes(Wg.M, Wg.K, T)
     if ws is None:
         ws = torch.empty((nws,), dtype=torch.uint8, device=x.device)
+    _need(ws, (ws.numel(),), (torch.uint8,), "ws")
+    _on_gpu(Wg, Wu, Wd, Wsg, x, out, ws)
     _check(lib().q8_moe_shared_expert(ctypes.byref(Wg.cmat()), ctypes.byref(Wu.cmat()),
                                       ctypes.byref(Wd.cmat()), ctypes.byref(Wsg.cmat()),
                                       x.data_ptr(), _dt(x), T, out.data_ptr(), ws.data_ptr(),

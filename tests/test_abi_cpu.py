@@ -335,3 +335,22 @@ def test_bindings_reject_mismatched_buffers():
         q8.moe_topk_softmax(L, 8, ids=torch.zeros((2, 7), dtype=torch.int32))
     with pytest.raises(ValueError):
         q8.moe_router(W, x, 8, logits=torch.zeros((2, 63)))
+
+
+def test_bindings_refuse_host_tensors():
+    """A host tensor handed to a kernel would be dereferenced by the GPU:
+    the bindings refuse it (checked last, after the shape checks)."""
+    import torch
+    W = q8.PackedQ8(torch.zeros(64 * 256, dtype=torch.int8), torch.zeros(64 * 8, dtype=torch.int16),
+                    64, 256)
+    x = torch.zeros((2, 256), dtype=torch.float16)
+    with pytest.raises(ValueError, match="on the GPU"):
+        q8.gemv(W, x)
+    with pytest.raises(ValueError, match="on the GPU"):
+        q8.gemv_pair_silu(W, W, x)
+    with pytest.raises(ValueError, match="on the GPU"):
+        q8.moe_topk_softmax(torch.zeros((2, 64)), 8)
+    with pytest.raises(ValueError, match="on the GPU"):
+        q8.moe_router(W, x, 8)
+    with pytest.raises(ValueError, match="on the GPU"):
+        q8.lmhead_argmax(W, x)
