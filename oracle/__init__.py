@@ -265,15 +265,81 @@ def silu(z: np.ndarray) -> np.ndarray:
     return np.where(z >= 0, z / (1.0 + np.exp(-np.maximum(z, 0.0))), z * ez / (1.0 + ez))
 
 
+# ---------------------------------------------------------------- propagated bounds
+# Each step after a GEMV receives inputs that are only known to lie within
+# their own bounds; these functions carry those bounds through the step
+# (first-order terms with the derivative's maximum, the second-order cross
+# term, and a relative allowance for the step's own fp32 rounding taken on
+# the magnitudes the device may see). Each is pinned by an adversarial
+# construction that reaches it and by an fp32 emulation that stays inside.
+
+def silu_mul_bound(g, u, bg, bu):
+    """Bound on h' - silu(g)*u for h' = silu(g')*u' evaluated in fp32, when
+    |g' - g| <= bg and |u' - u| <= bu.
+
+    silu(g') u' - silu(g) u = (silu(g') - silu(g)) u + silu(g') (u' - u),
+    with |silu'| <= 1.0999 < 1.1 (its maximum, near z = 2.4) and
+    |silu(g')| <= |silu(g)| + 1.1 bg, so the exact part is at most
+    P = 1.1 bg |u| + |silu(g)| bu + 1.1 bg bu. The fp32 evaluation (exp,
+    add, divide, multiply: a few units of 2^-24 each) adds at most
+    1e-6 (|h| + P), h = silu(g) u.
+    """
+    g = np.asarray(g, np.float64)
+    u = np.asarray(u, np.float64)
+    sg = silu(g)
+    P = 1.1 * bg * np.abs(u) + np.abs(sg) * bu + 1.1 * bg * bu
+    return P + 1e-6 * (np.abs(sg * u) + P)
+
+
+def down_bound(qd, dd, A_down, bh):
+    """Bound on a GEMV W_down h' whose input h' is within bh of h.
+
+    |W h' - W h| <= |W| bh (|W| the elementwise absolute dequantized
+    weights); the GEMV's own error is at most 1e-3 * A(h') and
+    A(h') <= A(h) + |W| bh, so the total is
+    1e-3 * A(h) + (1 + 1e-3) |W| bh. A_down [N][M] is A(h) from ``gemv``;
+    bh is [N][K].
+    """
+    M = qd.shape[0]
+    wabs = (np.abs(np.asarray(qd).astype(np.int32)).astype(np.float64).reshape(M, -1, QK)
+            * np.asarray(dd, np.float64)[:, :, None]).reshape(M, -1)
+    return REL_TOL * np.asarray(A_down, np.float64) + (1.0 + REL_TOL) * (np.asarray(bh) @ wabs.T)
+
+
+def combine_bound(gate_w, per_pair, S):
+    """Bound on sum_j w_j y'_j (fp32, ascending j) when each y'_j is within
+    per_pair[:, j] of y_j: sum_j w_j per_pair_j, plus 1e-6 of the magnitude
+    the fp32 sum may see, S + that sum (S = sum_j |w_j y_j|). per_pair is
+    [T][topk][M]; S is [T][M]."""
+    gw = np.asarray(gate_w, np.float64)
+    prop = (np.abs(gw)[:, :, None] * np.asarray(per_pair, np.float64)).sum(axis=1)
+    return prop + 1e-6 * (np.asarray(S, np.float64) + prop)
+
+
+def sigmoid_bound(sg, b_arg):
+    """Bound on an fp32 sigmoid(z') when |z' - z| <= b_arg and sg =
+    sigmoid(z): |sigma'| <= 1/4 gives L = b_arg / 4; exp, add and
+    reciprocal in fp32 add at most 1e-6 (sg + L)."""
+    L = 0.25 * np.asarray(b_arg, np.float64)
+    return L + 1e-6 * (np.asarray(sg, np.float64) + L)
+
+
+def gated_add_bound(base, sg, bsg, s, bs):
+    """Bound on base + sg' * s' (fp32 fused multiply-add) when |sg' - sg| <=
+    bsg and |s' - s| <= bs: the product's error sg bs + bsg |s| + bsg bs,
+    plus 1e-6 of the magnitude the fp32 result may see."""
+    s = np.asarray(s, np.float64)
+    P = sg * bs + bsg * np.abs(s) + bsg * bs
+    return P + 1e-6 * (np.abs(np.asarray(base, np.float64)) + sg * np.abs(s) + P)
+
+
 def moe_gate_up(case, threads: int = 1):
     """Stage 1 of the routed FFN: per pair p=(t,j) with e = ids[t,j]:
     g = W_gate[e] x_t, u = W_up[e] x_t (fp64), their A sums, and
     h = silu(g) * u with a propagated bound.
 
-    Bound on h (fp32 GPU h vs this fp64 h): with b_g, b_u the GEMV bounds,
-    |dh| <= 1.1*b_g*|u| + |silu(g)|*b_u + b_g*b_u*1.1 + 1e-6*|h|: 1.1 bounds
-    |silu'|, the last term covers fp32 exp, division and products.
-    Returns dict of [P][F] arrays in pair order p = t*topk + j.
+    Bound on h (fp32 GPU h vs this fp64 h): ``silu_mul_bound`` of the two
+    GEMV bounds. Returns dict of [P][F] arrays in pair order p = t*topk + j.
     """
     T, topk = case.expert_ids.shape
     F = case.q_gate.shape[1]
@@ -287,8 +353,7 @@ def moe_gate_up(case, threads: int = 1):
         p = tj[:, 0] * topk + tj[:, 1]
         g[p], Ag[p], u[p], Au[p] = ge, age, ue, aue
     h = silu(g) * u
-    bg, bu = REL_TOL * Ag, REL_TOL * Au
-    bh = 1.1 * bg * np.abs(u) + np.abs(silu(g)) * bu + 1.1 * bg * bu + 1e-6 * np.abs(h)
+    bh = silu_mul_bound(g, u, REL_TOL * Ag, REL_TOL * Au)
     return dict(g=g, u=u, Ag=Ag, Au=Au, h=h, bh=bh)
 
 
@@ -333,25 +398,21 @@ def moe_ffn(case, threads: int = 1):
     The down stage consumes h rounded to fp32 (the activation dtype the
     GPU's down GEMV reads); that rounding (<= 2^-24 |h|) is inside the
     1e-6*|h| term of the h bound. Also returns a propagated bound for an
-    fp32 GPU result: per pair, the down GEMV bound (1e-3 * A_down) plus
-    |W_down| applied to the h bound, gate-weighted and summed over j, plus
-    1e-6 of the combine magnitude.
+    fp32 GPU result: per pair ``down_bound`` (the down GEMV's own bound plus
+    |W_down| applied to the h bound), then ``combine_bound`` over the
+    gate-weighted pairs.
     """
     s1 = moe_gate_up(case, threads)
     y, Ay = moe_down(case, s1["h"].astype(np.float32), threads)
     T, topk = case.expert_ids.shape
     H = case.q_down.shape[1]
-    prop = np.zeros((T * topk, H))
+    per_pair = np.zeros((T * topk, H))
     for e in np.unique(case.expert_ids):
         tj = np.argwhere(case.expert_ids == e)
         p = tj[:, 0] * topk + tj[:, 1]
-        qa = np.abs(case.q_down[e].astype(np.int32)).astype(np.float64)
-        wabs = (qa.reshape(H, -1, QK) * case.d_down[e].astype(np.float64)[:, :, None]).reshape(H, -1)
-        prop[p] = s1["bh"][p] @ wabs.T
+        per_pair[p] = down_bound(case.q_down[e], case.d_down[e], Ay[p], s1["bh"][p])
     out, S = moe_combine(case.gate_w, y)
-    per_pair = REL_TOL * Ay + prop
-    gw = np.asarray(case.gate_w, np.float64)
-    b = (gw[:, :, None] * per_pair.reshape(T, topk, H)).sum(axis=1) + 1e-6 * S
+    b = combine_bound(case.gate_w, per_pair.reshape(T, topk, H), S)
     return dict(out=out, bound=b, stage1=s1, y_pair=y, A_pair=Ay)
 
 
@@ -400,10 +461,13 @@ def topk_softmax_bound(w: np.ndarray, dl: np.ndarray) -> np.ndarray:
     An fp32 evaluation rounds l_j - l_0 (relative 2^-24, so an absolute
     2^-24*dl_j in the exponent), evaluates exp (a few ulps), sums topk
     positive terms (at most (topk-1)*2^-24 relative) and divides (2^-24):
-    |dw_j| <= 2^-23 * (dl_j + 2*topk + 8) * w_j, with margin.
+    |dw_j| <= 2^-23 * (dl_j + 2*topk + 8) * w_j, with margin. Weights
+    below fp32's smallest normal number (exp(l_j - l_0) under about
+    e^-87) carry no relative precision (subnormal, or flushed to zero by
+    the device's exp): they get an absolute allowance of 2^-126.
     """
     topk = w.shape[-1]
-    return 2.0 ** -23 * (dl + 2 * topk + 8) * w
+    return 2.0 ** -23 * (dl + 2 * topk + 8) * w + 2.0 ** -126
 
 
 # ---------------------------------------------------------------- dense gate/up
@@ -411,18 +475,15 @@ def gate_up_silu(qg, dg, qu, du, x, threads: int = 1, out_dtype: str = "f32"):
     """Dense SiLU-gated pair of an MLP: h = silu(W_gate x) * (W_up x), fp64.
 
     The MLP step after the fused gate+up pair (memra performance, qwen/silu
-    class): silu(z) = z / (1 + exp(-z)). Bound on an fp32 (or fp16) GPU h,
-    propagated from the two GEMV bounds as in ``moe_gate_up``:
-    |dh| <= 1.1*b_g*|u| + |silu(g)|*b_u + 1.1*b_g*b_u + 1e-6*|h| (+ half an
-    fp16 ulp of h for fp16 output); 1.1 bounds |silu'|.
+    class): silu(z) = z / (1 + exp(-z)). Bound on an fp32 (or fp16) GPU h:
+    ``silu_mul_bound`` of the two GEMV bounds (+ half an fp16 ulp of h for
+    fp16 output).
     Returns dict(h, bh, g, u) of [N][M] arrays.
     """
     g, Ag = gemv(qg, dg, x, threads)
     u, Au = gemv(qu, du, x, threads)
-    sg = silu(g)
-    h = sg * u
-    bg, bu = REL_TOL * Ag, REL_TOL * Au
-    bh = 1.1 * bg * np.abs(u) + np.abs(sg) * bu + 1.1 * bg * bu + 1e-6 * np.abs(h)
+    h = silu(g) * u
+    bh = silu_mul_bound(g, u, REL_TOL * Ag, REL_TOL * Au)
     if out_dtype == "f16":
         bh = bh + 0.5 * fp16_ulp(h)
     return dict(h=h, bh=bh, g=g, u=u)
@@ -452,26 +513,20 @@ def shared_expert(qg, dg, qu, du, qd, dd, qsg, dsg, x, base, threads: int = 1):
 
     fp64 throughout; the down GEMV takes h rounded to fp32 (the GPU's
     activation dtype; the rounding is inside the 1e-6 * |h| term of h's
-    bound). Bound on an fp32 GPU result: with sg = sigmoid(gl) and b_sg =
-    0.25 * 1e-3 * A_gl + 1e-6 * sg (|sigma'| <= 1/4, plus fp32 exp, add and
-    division), and b_s = 1e-3 * A_down + |W_down| b_h (b_h from
-    gate_up_silu): |dout| <= sg * b_s + b_sg * |s| + b_sg * b_s
-    + 1e-6 * (|base| + sg * |s|).
-    Returns dict(out, bound, s, gate, h) with out [T][H], gate [T].
+    bound). Bound on an fp32 GPU result: ``gated_add_bound`` of the gate's
+    ``sigmoid_bound`` and the down projection's ``down_bound`` (b_h from
+    gate_up_silu). Returns dict(out, bound, s, gate, h) with out [T][H],
+    gate [T].
     """
     st = gate_up_silu(qg, dg, qu, du, x, threads)
     s, As = gemv(qd, dd, st["h"].astype(np.float32), threads)
-    H = qd.shape[0]
-    wabs = (np.abs(qd.astype(np.int32)).astype(np.float64).reshape(H, -1, QK)
-            * dd.astype(np.float64)[:, :, None]).reshape(H, -1)
-    bs = REL_TOL * As + st["bh"] @ wabs.T
+    bs = down_bound(qd, dd, As, st["bh"])
     gl, Agl = gemv(qsg, dsg, x, threads)
     sg = sigmoid(gl[:, 0])
-    bsg = 0.25 * REL_TOL * Agl[:, 0] + 1e-6 * sg
+    bsg = sigmoid_bound(sg, REL_TOL * Agl[:, 0])
     base = np.asarray(base, np.float64)
     out = base + sg[:, None] * s
-    bound = (sg[:, None] * bs + bsg[:, None] * np.abs(s) + bsg[:, None] * bs
-             + 1e-6 * (np.abs(base) + sg[:, None] * np.abs(s)))
+    bound = gated_add_bound(base, sg[:, None], bsg[:, None], s, bs)
     return dict(out=out, bound=bound, s=s, gate=sg, h=st["h"])
 
 
