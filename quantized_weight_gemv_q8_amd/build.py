@@ -20,9 +20,14 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libq8gemv.so")
 
-SOURCES = ["q8_api.cpp", "q8_gemv.hip", "q8_lmhead.hip", "q8_moe.hip", "q8_router.hip",
-           "q8_once1.hip", "q8_once2.hip", "q8_once3.hip", "q8_once4.hip", "q8_once5.hip",
-           "q8_once6.hip", "q8_once7.hip", "q8_once8.hip"]
+# (source, object name, defines): q8_once.hip is built once per kind and
+# token count of the one-group kernels, the largest units of the library,
+# so that they compile in parallel.
+SOURCES = [(src, os.path.splitext(src)[0], ()) for src in
+           ("q8_api.cpp", "q8_gemv.hip", "q8_lmhead.hip", "q8_moe.hip", "q8_router.hip")]
+SOURCES += [("q8_once.hip", f"q8_once_{'glu' if glu else 'dense'}{nt}",
+             (f"-DQ8_ONCE_NT={nt}", f"-DQ8_ONCE_GLU={glu}"))
+            for nt in range(8, 0, -1) for glu in (0, 1)]
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 COMMON = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-function",
           "-I", INCLUDE, "-I", CSRC]
@@ -35,10 +40,11 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libq8gemv.so)")
 
 
-def _compile(src: str) -> str:
+def _compile(unit) -> str:
+    src, name, defines = unit
     os.makedirs(BUILD_DIR, exist_ok=True)
-    obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *COMMON, "-c", os.path.join(CSRC, src), "-o", obj]
+    obj = os.path.join(BUILD_DIR, name + ".o")
+    cmd = [hipcc(), *COMMON, *defines, "-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".hip"):
         cmd[1:1] = ["-x", "hip"] + DEVICE_FLAGS
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -49,7 +55,7 @@ def _compile(src: str) -> str:
 
 def build(verbose: bool = False) -> str:
     """Compile every source and link the shared library; returns its path."""
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
+    with cf.ThreadPoolExecutor(max_workers=min(os.cpu_count() or 8, 16, len(SOURCES))) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB + ".tmp"
     cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]

@@ -394,6 +394,72 @@ __device__ __forceinline__ void stage_fmt(const char* const rows[NT], int C, uin
   stage_planes<NT, ChunkPlanes<F, XF32>::P, KBMAX>(rows, C, lds, nt);
 }
 
+// ---------------------------------------------------------------- staging orders
+// A one-group kernel (run_once) calls stage.issue() before its first scale
+// or weight load and stage.finish() once the weight loads of its window are
+// in flight; finish() leaves the x image in LDS and ends at the workgroup
+// barrier.
+//
+// LateStage: everything in finish() (the image's loads then come after
+// the weights, and the barrier after the weights' round trip).
+template <class Fn>
+struct LateStage {
+  Fn fn;
+  __device__ __forceinline__ void issue() {}
+  __device__ __forceinline__ void finish() { fn(); }
+};
+template <class Fn>
+__device__ __forceinline__ LateStage<Fn> late_stage(Fn fn) {
+  return LateStage<Fn>{fn};
+}
+
+// EarlyStage: issue() loads this thread's pieces of the x image (XB per
+// token, pieces t, t + blockDim, ...) into registers ahead of every weight
+// load. Vector memory loads return in issue order, so the image is the
+// first data back; finish() writes it to LDS and reaches the barrier while
+// the weights are still on their way, instead of after they arrived. The
+// loads are unconditional (a piece past the end re-reads the first piece
+// and is dropped): no branch, so no wait is forced between them. The LDS
+// writes are unconditional too (a dropped piece goes to lds[NT * P * C],
+// the first slot past the image, which the caller may reuse only after
+// finish()): a conditional write would let the compiler sink the load into
+// its branch, behind the weight loads. The launch keeps C * P <= XB *
+// blockDim.x. Token n's row starts at x + n * ldx (16-byte aligned).
+template <int NT, int P, int XB, bool SYNC = false>
+struct EarlyStage {
+  const char* x;
+  int64_t ldx;  // bytes
+  int C;
+  int nt;
+  uint4* lds;
+  uint4 v[NT][XB];
+  __device__ __forceinline__ void issue() {
+    const int per_tok = C * P;
+#pragma unroll
+    for (int n = 0; n < NT; ++n)
+#pragma unroll
+      for (int i = 0; i < XB; ++i) {
+        const int k = (int)threadIdx.x + i * (int)blockDim.x;
+        const bool live = n < nt && k < per_tok;
+        v[n][i] = *reinterpret_cast<const uint4*>(live ? x + n * ldx + 16 * (int64_t)k : x);
+      }
+    if constexpr (SYNC) __builtin_amdgcn_s_barrier();
+  }
+  __device__ __forceinline__ void finish() {
+    const int per_tok = C * P;
+#pragma unroll
+    for (int n = 0; n < NT; ++n)
+#pragma unroll
+      for (int i = 0; i < XB; ++i) {
+        const int k = (int)threadIdx.x + i * (int)blockDim.x;
+        const int c = k / P, h = k - c * P;
+        const bool live = n < nt && k < per_tok;
+        lds[live ? (n * P + h) * C + c : NT * P * C] = v[n][i];
+      }
+    __syncthreads();
+  }
+};
+
 // ---------------------------------------------------------------- wave maximum
 // Maximum of a 64-bit key over the 64 lanes, returned in every lane. DPP
 // moves inside each 16-lane row (quad permutes [1,0,3,2] and [2,3,0,1],
@@ -676,16 +742,18 @@ __device__ __forceinline__ void run_rows(const Map& map, Epi& epi, const uint4* 
 //
 // Scales: the team fetches each of its rows' whole scale row with 16-byte
 // loads (once_scale_pieces pieces, lane p takes pieces p, p + LPR, ...),
-// issued before the first weight load, and writes it after stage() to the
-// wave's own LDS area lds_s + wave * G * pieces (no barrier: only this wave
-// reads it); every chunk then reads its scale from LDS. One or two loads
-// per row instead of one 2-byte load per chunk. lds_s holds
+// issued before the first weight load, and writes it after stage.finish()
+// to the wave's own LDS area lds_s + wave * G * pieces (no barrier: only
+// this wave reads it); every chunk then reads its scale from LDS. One or
+// two loads per row instead of one 2-byte load per chunk. lds_s holds
 // waves-per-workgroup * G * once_scale_pieces(F, CPL * LPR) pieces.
+// Order of the loads: stage.issue() (x, for an EarlyStage), the scale rows,
+// then the first D weight chunks.
 template <int NT, int LPR, int R, int CPL, int D, int MINC, bool XF32, int F, class Map, class Epi,
           class Stage>
 __device__ __forceinline__ void run_once(const Map& map, Epi& epi, const uint4* lds,
                                          uint4* lds_s, int64_t n_groups, int64_t g,
-                                         int64_t row_origin, int64_t last_row, Stage&& stage,
+                                         int64_t row_origin, int64_t last_row, Stage& stage,
                                          int nt = NT) {
   constexpr int RPW = kWave / LPR;
   constexpr int G = RPW * R;
@@ -708,6 +776,10 @@ __device__ __forceinline__ void run_once(const Map& map, Epi& epi, const uint4* 
     const int64_t i = rbase + r;
     map.row(i < last_row ? i : last_row, q[r], d[r]);
   }
+  stage.issue();
+  // Keep the issue order (x, scales, weights): loads return in that order,
+  // and the scheduler would otherwise interleave them freely.
+  __builtin_amdgcn_sched_barrier(0);
   // Scale rows: unconditional loads, lanes past the last piece re-read it
   // (same line, no extra traffic).
   uint4 srow[R][NSP];
@@ -719,15 +791,21 @@ __device__ __forceinline__ void run_once(const Map& map, Epi& epi, const uint4* 
       srow[r][k] = load_stream16(reinterpret_cast<const int8_t*>(d[r]) +
                                  16 * (piece < SP ? piece : SP - 1));
     }
+  __builtin_amdgcn_sched_barrier(0);
   Slot<R> slot[D];
   auto issue = [&](Slot<R>& sl, int j) {
     const int c = p + LPR * j;
 #pragma unroll
     for (int r = 0; r < R; ++r) sl.q[r] = load_stream16(q[r] + (int64_t)c * 16);
   };
+  // The window's loads in chunk order (each wait below then covers only the
+  // chunks before the one it needs).
 #pragma unroll
-  for (int s = 0; s < D; ++s) issue(slot[s], s);
-  stage();
+  for (int s = 0; s < D; ++s) {
+    issue(slot[s], s);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  stage.finish();
   uint4* const srow_lds = lds_s + ((int)(threadIdx.x / kWave) * G + team * R) * SP;
 #pragma unroll
   for (int r = 0; r < R; ++r)

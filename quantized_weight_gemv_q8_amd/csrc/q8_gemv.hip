@@ -15,8 +15,36 @@
 #include "q8_dense.h"
 #include "q8_engine.hpp"
 #include "q8_internal.h"
+#include "q8_once.hpp"
 
 namespace q8 {
+
+// One-group-per-wave launches by token count (instantiated in q8_once.hip).
+hipError_t launch_gemv_once(int nt, const DevInfo& dev, const DenseMap& map, const DenseEpi& epi,
+                            int fmt, int lpr, bool x_f32, const char* x, int64_t ldx_bytes, int C,
+                            hipStream_t s) {
+  switch (nt) {
+#define Q8_ONCE_CASE(N) \
+  case N: return launch_once_nt<DenseKind, N>(dev, map, epi, fmt, lpr, x_f32, x, ldx_bytes, C, s);
+    Q8_ONCE_CASE(1) Q8_ONCE_CASE(2) Q8_ONCE_CASE(3) Q8_ONCE_CASE(4)
+    Q8_ONCE_CASE(5) Q8_ONCE_CASE(6) Q8_ONCE_CASE(7) Q8_ONCE_CASE(8)
+#undef Q8_ONCE_CASE
+  }
+  return hipErrorNotSupported;
+}
+
+hipError_t launch_glu_once(int nt, const DevInfo& dev, const GluMap& map, const GluEpi& epi,
+                           int fmt, int lpr, bool x_f32, const char* x, int64_t ldx_bytes, int C,
+                           hipStream_t s) {
+  switch (nt) {
+#define Q8_ONCE_CASE(N) \
+  case N: return launch_once_nt<GluKind, N>(dev, map, epi, fmt, lpr, x_f32, x, ldx_bytes, C, s);
+    Q8_ONCE_CASE(1) Q8_ONCE_CASE(2) Q8_ONCE_CASE(3) Q8_ONCE_CASE(4)
+    Q8_ONCE_CASE(5) Q8_ONCE_CASE(6) Q8_ONCE_CASE(7) Q8_ONCE_CASE(8)
+#undef Q8_ONCE_CASE
+  }
+  return hipErrorNotSupported;
+}
 
 template <int F, int NT, int LPR, bool XF32, int MODE>
 __global__ __launch_bounds__(kBlock) void gemv_kernel(DenseMap map, DenseEpi epi, const char* x,

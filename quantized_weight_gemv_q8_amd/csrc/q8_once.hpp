@@ -1,7 +1,8 @@
 // q8_once.hpp -- the dense GEMV with one row group per wave (run_once) for
 // passes of 1 to 8 tokens: kernels, their launch shape and the launcher.
-// Each q8_once<N>.hip instantiates it for N tokens (separate translation
-// units so the build compiles them in parallel).
+// q8_once.hip instantiates it for one kind and token count per build of
+// that file (separate translation units so the build compiles them in
+// parallel).
 #pragma once
 #include <algorithm>
 #include <type_traits>
@@ -45,51 +46,69 @@ struct GluKind {
 };
 
 // NT tokens, at most one row group per wave, C = CPL * LPR: run_once. The
-// workgroup size is chosen per launch (once_waves), up to 16 waves.
-template <class K, int F, int NT, int LPR, bool XF32, int CPL>
+// workgroup size is chosen per launch (once_waves), up to 16 waves. XB = 0
+// stages x after the weight loads of the window are issued (LateStage);
+// XB >= 1 loads it first, XB pieces per thread and token (EarlyStage).
+template <class K, int F, int NT, int LPR, bool XF32, int CPL, int XB = 0,
+          int D = once_depth(CPL), int RT = K::rows_per_team(NT), bool SYNC = false>
 __device__ __forceinline__ void once_body(const typename K::Map& map, typename K::Epi& epi,
                                           const char* x, int64_t ldx_bytes, int C) {
   extern __shared__ uint4 lds_x[];
-  constexpr int R = K::rows_per_team(NT);
+  constexpr int R = RT;
   constexpr int G = kWave / LPR * R;
+  constexpr int P = ChunkPlanes<F, XF32>::P;
   const int64_t rows = K::rows(map);
   const int64_t n_groups = (rows + G - 1) / G;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int waves = __builtin_amdgcn_readfirstlane(blockDim.x / kWave);
-  auto stage = [=]() {
-    const char* xr[NT];
-#pragma unroll
-    for (int n = 0; n < NT; ++n) xr[n] = x + n * ldx_bytes;
-    stage_fmt<F, NT, XF32>(xr, C, lds_x);
-    __syncthreads();
-  };
   const int64_t g = (int64_t)blockIdx.x * waves + wave;
-  run_once<NT, LPR, R, CPL, once_depth(CPL), K::kMinc, XF32, F>(
-      map, epi, lds_x, lds_x + NT * CPL * LPR * ChunkPlanes<F, XF32>::P, n_groups, g, 0,
-      rows - 1, stage);
+  uint4* const lds_s = lds_x + NT * CPL * LPR * P;
+  if constexpr (XB > 0) {
+    EarlyStage<NT, P, XB, SYNC> stage{x, ldx_bytes, C, NT, lds_x};
+    run_once<NT, LPR, R, CPL, D, K::kMinc, XF32, F>(map, epi, lds_x, lds_s, n_groups, g, 0,
+                                                    rows - 1, stage);
+  } else {
+    auto stage = late_stage([=]() {
+      const char* xr[NT];
+#pragma unroll
+      for (int n = 0; n < NT; ++n) xr[n] = x + n * ldx_bytes;
+      stage_fmt<F, NT, XF32>(xr, C, lds_x);
+      __syncthreads();
+    });
+    run_once<NT, LPR, R, CPL, D, K::kMinc, XF32, F>(map, epi, lds_x, lds_s, n_groups, g, 0,
+                                                    rows - 1, stage);
+  }
 }
 
-template <int F, int NT, int LPR, bool XF32, int CPL>
+template <int F, int NT, int LPR, bool XF32, int CPL, int XB = 0>
 __global__ __launch_bounds__(kOnceMaxBlock) void gemv_once_kernel(DenseMap map, DenseEpi epi,
                                                                   const char* x,
                                                                   int64_t ldx_bytes, int C) {
-  once_body<DenseKind, F, NT, LPR, XF32, CPL>(map, epi, x, ldx_bytes, C);
+  once_body<DenseKind, F, NT, LPR, XF32, CPL, XB>(map, epi, x, ldx_bytes, C);
 }
 
-template <int F, int NT, int LPR, bool XF32, int CPL>
+template <int F, int NT, int LPR, bool XF32, int CPL, int XB = 0>
 __global__ __launch_bounds__(kOnceMaxBlock) void glu_once_kernel(GluMap map, GluEpi epi,
                                                                  const char* x, int64_t ldx_bytes,
                                                                  int C) {
-  once_body<GluKind, F, NT, LPR, XF32, CPL>(map, epi, x, ldx_bytes, C);
+  once_body<GluKind, F, NT, LPR, XF32, CPL, XB>(map, epi, x, ldx_bytes, C);
 }
 
-template <class K, int F, int NT, int LPR, bool XF32, int CPL>
+template <class K, int F, int NT, int LPR, bool XF32, int CPL, int XB = 0>
 constexpr const void* once_fn() {
   if constexpr (std::is_same_v<K, GluKind>)
-    return (const void*)glu_once_kernel<F, NT, LPR, XF32, CPL>;
+    return (const void*)glu_once_kernel<F, NT, LPR, XF32, CPL, XB>;
   else
-    return (const void*)gemv_once_kernel<F, NT, LPR, XF32, CPL>;
+    return (const void*)gemv_once_kernel<F, NT, LPR, XF32, CPL, XB>;
 }
+
+// Two-token passes load x ahead of the weights (EarlyStage, one piece per
+// thread and token) when a workgroup has a thread for every piece of a
+// token's image. Measured on MI355X (same-process A/B, graph replay):
+// 5120 x 5120 N = 2 7.48 -> 7.01 us; at N = 1 neither order is faster
+// (6.42 against 6.45 us: there the barrier waits on the memory queue of the
+// compute unit either way), so one-token passes keep the late staging.
+constexpr bool once_early(int nt) { return nt == 2; }
 
 // Waves per workgroup for a one-group-per-wave launch of n_groups waves: 8,
 // unless the launch gives the compute units at least 8 waves each and
@@ -139,14 +158,26 @@ static hipError_t once_launch_t(const DevInfo& dev, typename K::Map map, typenam
   const size_t lds_x = (size_t)NT * C * 16 * ChunkPlanes<F, XF32>::P;
   const size_t lds_wave = (size_t)G * row_scale_pieces(F, C) * 16;  // a wave's scale rows
   const void* fn = once_fn<K, F, NT, LPR, XF32, CPL>();
-  if (hipError_t e = allow_dynamic_lds(
-          fn, std::min(lds_x + kOnceMaxBlock / kWave * lds_wave, dev.lds_per_block)))
-    return e;
+  const size_t lds_max = std::min(lds_x + kOnceMaxBlock / kWave * lds_wave, dev.lds_per_block);
+  if (hipError_t e = allow_dynamic_lds(fn, lds_max)) return e;
   const int64_t n_groups = (K::rows(map) + G - 1) / G;
   const int w = once_waves(dev, fn, n_groups, lds_x, lds_wave, NT <= 2);
   if (w == 0) return hipErrorNotSupported;
   const size_t lds = lds_x + (size_t)w * lds_wave;
   const int64_t blocks = (n_groups + w - 1) / w;
+  if constexpr (once_early(NT)) {
+    // The early image needs a thread per piece of a token and the same
+    // residency (its registers differ slightly from the late kernel's).
+    const void* fe = once_fn<K, F, NT, LPR, XF32, CPL, 1>();
+    const int64_t per_cu = (blocks + dev.cus - 1) / dev.cus;
+    const int res_late = blocks_per_cu(fn, lds, w * kWave);
+    const int res_early = blocks_per_cu(fe, lds, w * kWave);
+    if ((int64_t)C * ChunkPlanes<F, XF32>::P <= (int64_t)w * kWave &&
+        (per_cu <= res_early || per_cu > res_late)) {
+      if (hipError_t e = allow_dynamic_lds(fe, lds_max)) return e;
+      fn = fe;
+    }
+  }
   void* args[] = {&map, &epi, (void*)&x, &ldx_bytes, &C};
   return hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(w * kWave), args, lds, s);
 }
@@ -176,37 +207,20 @@ hipError_t launch_once_nt(const DevInfo& dev, const typename K::Map& map,
   });
 }
 
-hipError_t launch_once_nt1(const DevInfo&, const DenseMap&, const DenseEpi&, int, int, bool,
-                          const char*, int64_t, int, hipStream_t);
-hipError_t launch_once_nt2(const DevInfo&, const DenseMap&, const DenseEpi&, int, int, bool,
-                          const char*, int64_t, int, hipStream_t);
-hipError_t launch_once_nt3(const DevInfo&, const DenseMap&, const DenseEpi&, int, int, bool,
-                          const char*, int64_t, int, hipStream_t);
-hipError_t launch_once_nt4(const DevInfo&, const DenseMap&, const DenseEpi&, int, int, bool,
-                          const char*, int64_t, int, hipStream_t);
-hipError_t launch_once_nt5(const DevInfo&, const DenseMap&, const DenseEpi&, int, int, bool,
-                          const char*, int64_t, int, hipStream_t);
-hipError_t launch_once_nt6(const DevInfo&, const DenseMap&, const DenseEpi&, int, int, bool,
-                          const char*, int64_t, int, hipStream_t);
-hipError_t launch_once_nt7(const DevInfo&, const DenseMap&, const DenseEpi&, int, int, bool,
-                          const char*, int64_t, int, hipStream_t);
-hipError_t launch_once_nt8(const DevInfo&, const DenseMap&, const DenseEpi&, int, int, bool,
-                          const char*, int64_t, int, hipStream_t);
-hipError_t launch_glu_once_nt1(const DevInfo&, const GluMap&, const GluEpi&, int, int, bool,
-                              const char*, int64_t, int, hipStream_t);
-hipError_t launch_glu_once_nt2(const DevInfo&, const GluMap&, const GluEpi&, int, int, bool,
-                              const char*, int64_t, int, hipStream_t);
-hipError_t launch_glu_once_nt3(const DevInfo&, const GluMap&, const GluEpi&, int, int, bool,
-                              const char*, int64_t, int, hipStream_t);
-hipError_t launch_glu_once_nt4(const DevInfo&, const GluMap&, const GluEpi&, int, int, bool,
-                              const char*, int64_t, int, hipStream_t);
-hipError_t launch_glu_once_nt5(const DevInfo&, const GluMap&, const GluEpi&, int, int, bool,
-                              const char*, int64_t, int, hipStream_t);
-hipError_t launch_glu_once_nt6(const DevInfo&, const GluMap&, const GluEpi&, int, int, bool,
-                              const char*, int64_t, int, hipStream_t);
-hipError_t launch_glu_once_nt7(const DevInfo&, const GluMap&, const GluEpi&, int, int, bool,
-                              const char*, int64_t, int, hipStream_t);
-hipError_t launch_glu_once_nt8(const DevInfo&, const GluMap&, const GluEpi&, int, int, bool,
-                              const char*, int64_t, int, hipStream_t);
+// Each (kind, token count) is instantiated in its own translation unit
+// (q8_once.hip, built once per pair so the build runs them in parallel);
+// everywhere else these instantiations are only declared.
+#define Q8_ONCE_DECLARE(KIND, N)                                                              \
+  extern template hipError_t launch_once_nt<KIND, N>(const DevInfo&, const KIND::Map&,       \
+                                                     const KIND::Epi&, int, int, bool,         \
+                                                     const char*, int64_t, int, hipStream_t);
+#define Q8_ONCE_DECLARE_ALL(KIND)                                                             \
+  Q8_ONCE_DECLARE(KIND, 1) Q8_ONCE_DECLARE(KIND, 2) Q8_ONCE_DECLARE(KIND, 3)                  \
+  Q8_ONCE_DECLARE(KIND, 4) Q8_ONCE_DECLARE(KIND, 5) Q8_ONCE_DECLARE(KIND, 6)                  \
+  Q8_ONCE_DECLARE(KIND, 7) Q8_ONCE_DECLARE(KIND, 8)
+Q8_ONCE_DECLARE_ALL(DenseKind)
+Q8_ONCE_DECLARE_ALL(GluKind)
+#undef Q8_ONCE_DECLARE_ALL
+#undef Q8_ONCE_DECLARE
 
 }  // namespace q8

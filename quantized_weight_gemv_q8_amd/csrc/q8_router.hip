@@ -198,11 +198,11 @@ __global__ __launch_bounds__(kRouterMaxWaves * kWave) void router_kernel(
   epi.lds = lds_logits;
   epi.E = E;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  auto stage = [=]() {
+  auto stage = late_stage([=]() {
     const char* rows[1] = {x + t * ldx_bytes};
     stage_fmt<F, 1, false>(rows, C, lds_x);
     __syncthreads();
-  };
+  });
   run_once<1, LPR, RR, CPL, CPL, 1, false, F>(map, epi, lds_x, lds_s, (E + G - 1) / G, wave, 0,
                                                E - 1, stage);
   __syncthreads();
