@@ -106,10 +106,20 @@ typedef struct q8_bank {
     int32_t E;
 } q8_bank;
 
-/* Human-readable name of a status code (static string). */
+/* Human-readable name of a status code: a static string, never NULL
+ * ("unknown status" for a value outside q8_status). Every failure of this
+ * library is a named status the caller can report, never a silent
+ * fallback (topairepos memra listing, which asks for useful failures over
+ * silent fallbacks). No device is touched; callable on any host. */
 const char *q8_status_str(int status);
 
-/* Q8_OK iff HIP device `device` is a gfx950 part. */
+/* Q8_OK iff HIP device `device` (an index as for hipSetDevice) exists and
+ * is a gfx950 part; Q8_ERR_DEVICE otherwise. The answer is probed once per
+ * device and cached (thread-safe). Call it at start-up to fail early, as
+ * the pages' engine does when its binary does not match the GPU (memra
+ * wiki: it checks the device at start-up and refuses to run on a
+ * mismatch); every hot-path call makes the same check on the current
+ * device. */
 int q8_device_check(int device);
 
 /* ------------------------------------------------------------ packing (host)
@@ -145,9 +155,16 @@ int q8_gemv(const q8_matrix *W, const void *x, int x_dt, void *y, int y_dt, int 
             void *stream);
 
 /* Fused pair: ya = Wa x and yb = Wb x in one launch sharing one staging of
- * x (an MLP's gate and up projections). Wa->K == Wb->K; M may differ.
- * ya [N][Wa->M], yb [N][Wb->M]. Results are bitwise equal to two q8_gemv
- * calls. No activation is applied. */
+ * x: the gate and up projections of a SiLU-gated MLP, which the pages'
+ * decode runs as one fused matvec (memra performance, the qwen/silu MLP
+ * class of the decode kernels). Wa->K == Wb->K; M may differ; both
+ * matrices have one format.
+ *   x [dev] [N][K] of x_dt, contiguous, 16-byte aligned;
+ *   ya [dev] [N][Wa->M], yb [dev] [N][Wb->M], both of y_dt, must not
+ *   overlap x or each other (Q8_ERR_ALIAS).
+ * Results are bitwise equal to two q8_gemv calls (same per-row
+ * arithmetic). No activation is applied (q8_gemv_pair_silu applies it).
+ * N >= 1, passes of up to 8 tokens as for q8_gemv. */
 int q8_gemv_pair(const q8_matrix *Wa, const q8_matrix *Wb, const void *x, int x_dt,
                  void *ya, void *yb, int y_dt, int N, void *stream);
 
@@ -240,16 +257,22 @@ int q8_lmhead_argmax_rows(const q8_matrix *W, const int32_t *row_ids, const void
  * (memra performance, serving exactness arc).
  *
  * expert_ids [dev] int32 [T][topk]: expert of slot j of token t; the
- *   topk ids of one token must be distinct and in [0, E). Ids are trusted
- *   (checking them would need a synchronisation); out-of-range ids are
- *   skipped by the kernels and their outputs are left as zero.
+ *   topk ids of one token must be distinct and in [0, E). Checking them on
+ *   the host would need a synchronisation, so the check runs on the
+ *   device: a pair whose id is out of range is left out (its per-pair
+ *   output row is zero and it adds nothing to the combine), and the number
+ *   of such pairs is written to the workspace error word (below). Every
+ *   call writes the word (0 for valid ids), so it needs no clearing, also
+ *   under graph replay; read it after the call to detect bad routing.
  * gate_w [dev] fp32 [T][topk]: combine weights (e.g. softmax router output).
  * Pair p = t*topk + j.
  *
  * Workspace layout (q8_moe_ws_layout gives byte offsets; all int32 unless
  * noted): [0] counts[E], [1] offsets[E+1], [2] pairs[T*topk] (pair ids in
  * expert-major order, ascending p inside an expert), [3] active[E]
- * (experts with count > 0, ascending), [4] n_active[1], [5] h fp32
+ * (experts with count > 0, ascending), [4] n_active, then (int32 [1] of
+ * area [4]) the routed-slot count, then (int32 [2] of area [4]) the error
+ * word: the number of pairs whose expert id was out of range, [5] h fp32
  * [T*topk][F] (q8_moe_ffn only), [6] y_pair fp32 [T*topk][Mout].
  * The caller may read these after the call for inspection. */
 

@@ -293,9 +293,37 @@ def _need(t, shape, dtypes, name):
     return t
 
 
+def _check_packed(W):
+    """A packed matrix or bank must hold the planes its header fields
+    describe: qs int8/uint8 with M rows of at least the row's bytes (K, or
+    K/2 for Q4_0) and d int16 with M rows of at least K/32 scales, each
+    with unit inner stride ([E][M][...] for a bank). The library reads
+    M * ld bytes from each plane, so a short or column-sliced plane would
+    be read past its end or at the wrong bytes."""
+    import torch
+    row_bytes = W.K // 2 if W.fmt == Q8_FMT_Q4_0 else W.K
+    lead = (W.E,) if isinstance(W, PackedBank) else ()
+    for t, name, dts, width in ((W.qs, "qs", (torch.int8, torch.uint8), row_bytes),
+                                (W.d, "d", (torch.int16,), W.K // 32)):
+        ok = (isinstance(t, torch.Tensor) and t.dtype in dts and t.dim() == len(lead) + 2
+              and tuple(t.shape[:-1]) == lead + (W.M,) and t.shape[-1] >= width
+              and t.stride(-1) == 1 and t.stride(-2) >= width)
+        if ok and lead:
+            ok = W.E == 1 or t.stride(0) >= W.M * t.stride(1)
+        if not ok:
+            kind = "bank" if lead else "matrix"
+            raise ValueError(f"packed {kind} plane {name} must be a {'/'.join(str(d)[6:] for d in dts)} "
+                             f"tensor of shape {lead + (W.M,)} x >={width} with unit inner stride "
+                             f"(got {tuple(t.shape) if isinstance(t, torch.Tensor) else type(t)})")
+
+
 def _on_gpu(*args):
     """Every tensor handed to a kernel (packed weights included) must live
-    in device memory: a host address would be read or written by the GPU."""
+    in device memory: a host address would be read or written by the GPU.
+    Packed weights are first checked against their own shape fields."""
+    for a in args:
+        if isinstance(a, (PackedQ8, PackedBank)):
+            _check_packed(a)
     for a in args:
         if a is None:
             continue
@@ -430,6 +458,8 @@ def moe_ws_views(ws, E: int, T: int, topk: int, F: int, M: int) -> dict:
     v = dict(counts=view(0, E, torch.int32), offsets=view(1, E + 1, torch.int32),
              pairs=view(2, P, torch.int32), active=view(3, E, torch.int32),
              n_active=view(4, 1, torch.int32), y_pair=view(6, P * M, torch.float32).view(P, M))
+    # the error word: pairs whose expert id was out of range in the last call
+    v["n_bad_ids"] = ws[off[4] + 8:off[4] + 12].view(torch.int32)
     if F > 0:
         v["h"] = view(5, P * F, torch.float32).view(P, F)
     return v

@@ -399,6 +399,7 @@ static q8::MoeWs moe_ws_ptrs(void* ws, int E, int T, int topk, int64_t F, int64_
   w.active = (int32_t*)(b + off[3]);
   w.n_active = (int32_t*)(b + off[4]);
   w.n_vslots = w.n_active + 1;
+  w.n_bad_ids = w.n_active + 2;
   w.h = F > 0 ? (float*)(b + off[5]) : nullptr;
   w.y_pair = (float*)(b + off[6]);
   w.vslots = (int32_t*)(b + off[7]);

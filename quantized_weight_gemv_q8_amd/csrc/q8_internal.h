@@ -93,6 +93,7 @@ struct MoeWs {
   int32_t* active;   // [E]
   int32_t* n_active; // [1]
   int32_t* n_vslots; // [1], after n_active
+  int32_t* n_bad_ids; // [1], after n_vslots: pairs with an out-of-range expert id
   float* h;          // [P][F] or null
   float* y_pair;     // [P][Mout] or null
   int32_t* vslots;   // [moe_max_vslots(E, P)][8]: expert, token count, pair ids

@@ -13,7 +13,10 @@
 //  route    one workgroup: counts, offsets, expert-major pair list (stable:
 //           ascending pair id inside an expert), the active-expert list and
 //           the virtual slots: an active expert with up to kMoeNT of its
-//           pairs (an expert with more pairs gets several slots).
+//           pairs (an expert with more pairs gets several slots). Pairs
+//           whose expert id is out of range are left out, and their number
+//           is written to the workspace error word (a failure the caller
+//           can read, not a silent fallback).
 //  gate_up  the rows of all virtual slots form one row space (a team's two
 //           rows are the gate and up rows of one output index, so the
 //           epilogue has both sums in one lane and writes h = silu(g) * u);
@@ -101,18 +104,24 @@ __device__ __forceinline__ void route_block(const int32_t* ids, int E, int P, in
                                             const MoeWs& ws, bool write_ws, int32_t* vslots_out,
                                             int32_t* nv_out, float* zero_rows, int64_t zero_ld) {
   __shared__ int wtot[THREADS / kWave][3];
+  __shared__ int n_bad;
   int32_t* cnt = sm;              // [E]
   int32_t* off = cnt + E;         // [E+1]
   int32_t* cur = off + E + 1;     // [E]
   int32_t* sid = cur + E;         // [P]
   int32_t* tmp = sid + P;         // [P]
   const int t = threadIdx.x;
+  if (t == 0) n_bad = 0;
   for (int e = t; e < E; e += THREADS) cnt[e] = 0;
+  int my_bad = 0;
   for (int p = t; p < P; p += THREADS) {
     const int e = ids[p];
-    sid[p] = (e >= 0 && e < E) ? e : -1;
+    const bool ok = e >= 0 && e < E;
+    sid[p] = ok ? e : -1;
+    my_bad += ok ? 0 : 1;
   }
   __syncthreads();
+  if (my_bad) atomicAdd(&n_bad, my_bad);
   for (int p = t; p < P; p += THREADS)
     if (sid[p] >= 0) atomicAdd(&cnt[sid[p]], 1);
   __syncthreads();
@@ -148,6 +157,7 @@ __device__ __forceinline__ void route_block(const int32_t* ids, int E, int P, in
       ws.offsets[E] = total[0];
       *ws.n_active = total[1];
       *ws.n_vslots = total[2];
+      *ws.n_bad_ids = n_bad;  // the workspace error word: written by every routed call
     }
   }
   __syncthreads();
@@ -692,7 +702,7 @@ size_t moe_ws_layout(int E, int T, int topk, int64_t F, int64_t M, size_t off[kM
   off[1] = take(4 * (size_t)(E + 1));
   off[2] = take(4 * (size_t)P);
   off[3] = take(4 * (size_t)E);
-  off[4] = take(8);  // n_active, n_vslots
+  off[4] = take(12);  // n_active, n_vslots, n_bad_ids (the error word)
   off[5] = take(F > 0 ? 4 * (size_t)P * (size_t)F : 0);
   off[6] = take(4 * (size_t)P * (size_t)M);
   off[7] = take(4 * (size_t)kVSlotInts * (size_t)moe_max_vslots(E, (int)P));

@@ -300,8 +300,8 @@ def test_shared_expert_binding_rejects_bad_out():
     """The Python binding refuses an out that is not a contiguous fp32
     [T][H] tensor before calling the library."""
     import torch
-    W = q8.PackedQ8(torch.zeros(64 * 256, dtype=torch.int8), torch.zeros(64 * 8, dtype=torch.int16),
-                    64, 256)
+    W = q8.PackedQ8(torch.zeros((64, 256), dtype=torch.int8),
+                    torch.zeros((64, 8), dtype=torch.int16), 64, 256)
     x = torch.zeros((2, 256), dtype=torch.float16)
     for bad in (torch.zeros((256, 2)).t(), torch.zeros((2, 256), dtype=torch.float16),
                 torch.zeros((3, 256))):
@@ -314,8 +314,8 @@ def test_bindings_reject_mismatched_buffers():
     dtype or layout before the library is called (a short buffer would
     otherwise be written past its end)."""
     import torch
-    W = q8.PackedQ8(torch.zeros(64 * 256, dtype=torch.int8), torch.zeros(64 * 8, dtype=torch.int16),
-                    64, 256)
+    W = q8.PackedQ8(torch.zeros((64, 256), dtype=torch.int8),
+                    torch.zeros((64, 8), dtype=torch.int16), 64, 256)
     x = torch.zeros((2, 256), dtype=torch.float16)
     for bad in (torch.zeros((2, 63)), torch.zeros((64, 2)).t(), torch.zeros((2, 64), dtype=torch.int32)):
         with pytest.raises(ValueError):
@@ -341,8 +341,8 @@ def test_bindings_refuse_host_tensors():
     """A host tensor handed to a kernel would be dereferenced by the GPU:
     the bindings refuse it (checked last, after the shape checks)."""
     import torch
-    W = q8.PackedQ8(torch.zeros(64 * 256, dtype=torch.int8), torch.zeros(64 * 8, dtype=torch.int16),
-                    64, 256)
+    W = q8.PackedQ8(torch.zeros((64, 256), dtype=torch.int8),
+                    torch.zeros((64, 8), dtype=torch.int16), 64, 256)
     x = torch.zeros((2, 256), dtype=torch.float16)
     with pytest.raises(ValueError, match="on the GPU"):
         q8.gemv(W, x)
@@ -354,3 +354,40 @@ def test_bindings_refuse_host_tensors():
         q8.moe_router(W, x, 8)
     with pytest.raises(ValueError, match="on the GPU"):
         q8.lmhead_argmax(W, x)
+
+
+def test_bindings_check_packed_planes():
+    """Packed weights whose planes do not match their shape fields are
+    refused before any launch: a short quant plane, a column-sliced scale
+    plane, a wrong dtype, a bank with too few experts."""
+    import torch
+    x = torch.zeros((2, 256), dtype=torch.float16)
+    good_q = torch.zeros((64, 256), dtype=torch.int8)
+    good_d = torch.zeros((64, 8), dtype=torch.int16)
+    bad = [
+        q8.PackedQ8(torch.zeros((63, 256), dtype=torch.int8), good_d, 64, 256),  # short qs
+        q8.PackedQ8(good_q, torch.zeros((64, 16), dtype=torch.int16)[:, ::2], 64, 256),  # strided d
+        q8.PackedQ8(good_q[:, :128], good_d, 64, 256),  # rows shorter than K
+        q8.PackedQ8(good_q, torch.zeros((64, 8), dtype=torch.float16), 64, 256),  # d dtype
+        q8.PackedQ8(good_q.view(-1), good_d, 64, 256),  # flat qs
+        q8.PackedQ8(good_q[:, :128], good_d, 64, 256, q8.Q8_FMT_Q8_0),
+    ]
+    for W in bad:
+        with pytest.raises(ValueError, match="packed matrix plane"):
+            q8.gemv(W, x)
+    # Q4_0 rows hold K/2 bytes: the same [64][128] plane is valid for it
+    ok = q8.PackedQ8(torch.zeros((64, 128), dtype=torch.int8), good_d, 64, 256, q8.Q8_FMT_Q4_0)
+    with pytest.raises(ValueError, match="on the GPU"):
+        q8.gemv(ok, x)
+    bank_q = torch.zeros((4, 64, 256), dtype=torch.int8)
+    bank_d = torch.zeros((4, 64, 8), dtype=torch.int16)
+    ids = torch.zeros((2, 2), dtype=torch.int32)
+    gw = torch.zeros((2, 2), dtype=torch.float32)
+    for B in (q8.PackedBank(bank_q[:3], bank_d, 64, 256, 4),
+              q8.PackedBank(bank_q, bank_d[:, :, :4], 64, 256, 4),
+              q8.PackedBank(bank_q[:, :32], bank_d, 64, 256, 4)):
+        with pytest.raises(ValueError, match="packed bank plane"):
+            q8.moe_gemv(B, ids, x.view(2, 256), gate_w=gw)
+    good = q8.PackedBank(bank_q, bank_d, 64, 256, 4)
+    with pytest.raises(ValueError, match="on the GPU"):
+        q8.moe_gemv(good, ids, x, gate_w=gw)

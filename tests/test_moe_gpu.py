@@ -150,17 +150,41 @@ def test_routed_gemv_fp32_per_pair_inputs():
     assert_parity(yp, ref, A, what="per-pair fp32")
 
 
-def test_invalid_ids_are_skipped():
+def test_invalid_ids_are_skipped_and_counted():
+    """Out-of-range expert ids: the pair is left out (zero row) and the
+    workspace error word counts it; a later valid call writes 0 again, also
+    when the same workspace is replayed in a graph."""
     note("moe invalid ids")
     c = synth.moe_case(E=5, F=64, H=128, T=3, topk=2, seed=1)
     W = upload_bank(c.q_gate, c.d_gate)
+    ws = torch.full((q8.moe_ws_bytes(c.E, 3, 2, 0, 64),), 0x7F, dtype=torch.uint8, device="cuda")
+    views = q8.moe_ws_views(ws, c.E, 3, 2, 0, 64)
     ids = c.expert_ids.copy()
     ids[1, 1] = 99
-    yp = host(q8.moe_gemv(W, dev(ids), dev(c.x)))
-    assert np.all(yp[1 * 2 + 1] == 0)
+    ids[2, 0] = -3
+    yp = host(q8.moe_gemv(W, dev(ids), dev(c.x), ws=ws))
+    assert int(host(views["n_bad_ids"])[0]) == 2
+    assert np.all(yp[1 * 2 + 1] == 0) and np.all(yp[2 * 2 + 0] == 0)
     e = int(ids[1, 0])
     ref, A = oracle.gemv(c.q_gate[e], c.d_gate[e], c.x[1:2])
     assert_parity(yp[2:3], ref, A, what="valid slot next to invalid one")
+    good = dev(c.expert_ids)
+    q8.moe_gemv(W, good, dev(c.x), ws=ws)
+    assert int(host(views["n_bad_ids"])[0]) == 0
+    # under graph replay: the word follows the ids of each replay
+    idt = dev(ids)
+    xt = dev(c.x)
+    out = torch.empty((6, 64), dtype=torch.float32, device="cuda")
+    q8.moe_gemv(W, idt, xt, out=out, ws=ws)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        q8.moe_gemv(W, idt, xt, out=out, ws=ws)
+    for bad, want in ((ids, 2), (c.expert_ids, 0), (ids, 2)):
+        idt.copy_(torch.from_numpy(np.ascontiguousarray(bad)).cuda())
+        torch.cuda.synchronize()
+        g.replay()
+        assert int(host(views["n_bad_ids"])[0]) == want
 
 
 def test_many_experts_route_in_its_own_launch():
@@ -173,8 +197,10 @@ def test_many_experts_route_in_its_own_launch():
     W = upload_bank(c.q_gate, c.d_gate)
     ids = c.expert_ids.copy()
     ids[7, 3] = -1
-    yp = host(q8.moe_gemv(W, dev(ids), dev(c.x)))
+    ws = torch.zeros((q8.moe_ws_bytes(c.E, c.T, c.topk, 0, c.F),), dtype=torch.uint8, device="cuda")
+    yp = host(q8.moe_gemv(W, dev(ids), dev(c.x), ws=ws))
     assert np.all(yp[7 * 8 + 3] == 0)
+    assert int(host(q8.moe_ws_views(ws, c.E, c.T, c.topk, 0, c.F)["n_bad_ids"])[0]) == 1
     e = int(ids[7, 2])
     ref, A = oracle.gemv(c.q_gate[e], c.d_gate[e], c.x[7:8])
     assert_parity(yp[7 * 8 + 2:7 * 8 + 3], ref, A, what="valid slot next to invalid one")
