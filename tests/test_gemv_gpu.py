@@ -93,6 +93,36 @@ def test_random_parity(M, K, N):
     assert_parity(y, ref, A, what=f"{M}x{K} N={N}")
 
 
+@pytest.mark.parametrize("M,K,N", [(300, 5120, 3), (1000, 768, 1), (64, 96, 8)])
+def test_zero_blocks_in_random_rows(M, K, N):
+    """Zero blocks inside random rows (scale 0, quants 0, or both) and an
+    all-zero row: within the bound of the oracle, the zero row exactly 0,
+    and the result does not depend on how a block is zero (each such block
+    adds exactly nothing to its lane's sum), bitwise."""
+    note(f"zero blocks {M}x{K} N={N}")
+    rng = np.random.default_rng(M + K)
+    q, d = synth.draw_weights(rng, M, K)
+    x = synth.draw_x(rng, N, K)
+    nb = K // 32
+    zero = rng.random((M, nb)) < 0.25
+    zero[M // 2] = True  # an all-zero row
+    variants = []
+    for how in ("d", "q", "both"):
+        qv, dv = q.copy(), d.copy()
+        for m, b in zip(*np.nonzero(zero)):
+            if how in ("d", "both"):
+                dv[m, b] = 0.0
+            if how in ("q", "both"):
+                qv[m, b * 32:(b + 1) * 32] = 0
+        y = host(q8.gemv(upload(qv, dv), dev(x)))
+        ref, A = oracle.gemv(qv, dv, x, threads())
+        assert_parity(y, ref, A, what=f"zero blocks ({how})")
+        assert np.all(y[:, M // 2] == 0)
+        variants.append(y)
+    assert np.array_equal(variants[0].view(np.uint32) & 0x7FFFFFFF, variants[1].view(np.uint32) & 0x7FFFFFFF)
+    assert np.array_equal(variants[1].view(np.uint32), variants[2].view(np.uint32))
+
+
 def test_config_5120_n1_full():
     note("5120x5120 N=1 full oracle")
     c = synth.gemv_case(5120, 5120, 1, seed=0)

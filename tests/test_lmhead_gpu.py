@@ -69,6 +69,63 @@ def test_planted_margin_is_at_least_3_sigma(vocab):
         assert ref[n, r] - others.max() >= 3 * others.std()
 
 
+def test_full_vocab_planted_at_3_sigma(vocab):
+    """The gate near its edge: token 0's planted row is re-planted to lead
+    the runner-up by the +3 sigma margin (sigma the population std of the
+    other logits), with the smallest fp16 scale that reaches it; the token
+    is gated and the GPU returns that row."""
+    note("lmhead 151936x5120 planted at +3 sigma")
+    c4, _ = vocab
+    c = synth.LmHeadCase(c4.q.copy(), c4.d.copy(), c4.x[:2].copy(), c4.planted_rows[:2].copy(),
+                         c4.planted_target[:2].copy())
+    r = int(c.planted_rows[0])
+    L, _ = oracle.gemv(c.q, c.d, c.x[:1], threads())
+    others = np.delete(L[0], r)
+    sigma = others.std()
+    xn = c.x[0].astype(np.float64)
+    s_abs = np.abs(xn).sum()
+    c.q[r] = (np.sign(xn) * 127).astype(np.int8)
+    c.d[r] = synth.fp16_at_least((others.max() + 3 * sigma) / (127.0 * s_abs))
+    ref, A = oracle.gemv(c.q, c.d, c.x, threads())
+    margin = ref[0, r] - np.delete(ref[0], r).max()
+    step = 127.0 * s_abs * float(np.spacing(c.d[r, 0]))  # one fp16 step of the scale
+    assert 3 * sigma <= margin < 3 * sigma + step
+    logits, ids = q8.lmhead_argmax(upload(c.q, c.d), dev(c.x))
+    gated = check_lmhead(c, host(logits), host(ids))
+    assert gated[0] and int(host(ids)[0]) == r
+
+
+def test_token_outside_gate_set_takes_a_candidate():
+    """Two rows whose logits differ by less than the bound: the token is not
+    gated, so any id of its candidate set is correct; the GPU must return
+    one of them, the first maximum of its own logits. A third token with
+    two identical top rows must return the lower index."""
+    note("lmhead candidate-set rule")
+    c = synth.lmhead_case(8192, 2048, 3, seed=17)
+    V = c.q.shape[0]
+    for n in range(3):
+        r = int(c.planted_rows[n])
+        twin = (r + 1) % V if n < 2 else (r + 4096) % V
+        c.q[twin] = c.q[r]
+        c.d[twin] = c.d[r]
+        if n < 2:
+            # one quant one step smaller where |x| is smallest: the twin trails
+            # by d * |x_k|, far inside the bound
+            k = int(np.argmin(np.abs(c.x[n].astype(np.float64)) + (c.q[r] == 0) * 1e9))
+            c.q[twin, k] = c.q[r, k] - np.sign(c.q[r, k])
+    ref, A = oracle.gemv(c.q, c.d, c.x, threads())
+    istar, gated, cands = oracle.argmax_gate(ref, A)
+    assert not gated.any()
+    logits, ids = q8.lmhead_argmax(upload(c.q, c.d), dev(c.x))
+    logits, ids = host(logits), host(ids)
+    check_lmhead(c, logits, ids)
+    for n in range(3):
+        r = int(c.planted_rows[n])
+        assert int(ids[n]) in set(cands[n].tolist()) and int(ids[n]) in {r, (r + 1) % V, (r + 4096) % V}
+    r2 = int(c.planted_rows[2])
+    assert int(ids[2]) == min(r2, (r2 + 4096) % V)  # exact tie: the lower index
+
+
 @pytest.mark.parametrize("V,K,N", [(4096, 1024, 3), (1000, 768, 8), (333, 96, 11), (1, 32, 1)])
 def test_small_vocab_full_oracle(V, K, N):
     note(f"lmhead small V={V} K={K} N={N}")

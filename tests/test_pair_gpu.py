@@ -1,9 +1,9 @@
 """Parity of the fused gate+up pair (q8_gemv_pair) with the oracle.
 
 Full-size workload: two [17408][5120] Q8_0 matrices sharing x, N = 1, 2, 4,
-8 (speculative-verify widths). The oracle checks a sample of rows from
-both matrices (first, last and 1500 random rows each, plus every row of a
-smaller pair); the pair must equal two single q8_gemv calls bitwise.
+8 (speculative-verify widths). The oracle checks every row of both
+matrices at N = 1 and 8 (a sample of rows at 2 and 4, and every row of
+smaller pairs); the pair must equal two single q8_gemv calls bitwise.
 The fused SiLU pair (q8_gemv_pair_silu) is gated against the oracle's
 propagated bound on h = silu(g) * u, against silu of the pair's own g and
 u within fp32 rounding, for fp16 output, multi-pass N and N-invariance.
@@ -31,7 +31,8 @@ def full_pair():
 
 
 @pytest.mark.parametrize("N", [1, 2, 4, 8])
-def test_full_size_pair_sampled_rows(full_pair, N):
+def test_full_size_pair(full_pair, N):
+    """Every row of both matrices at N = 1 and 8; a sample of rows at 2, 4."""
     note(f"pair 17408x5120 N={N}")
     c, Wa, Wb = full_pair
     x = c.x[:N]
@@ -40,8 +41,12 @@ def test_full_size_pair_sampled_rows(full_pair, N):
     rng = np.random.default_rng(N)
     rows = np.unique(np.concatenate([[0, 1, 17407], rng.choice(17408, 1500, replace=False)]))
     for q, d, y, name in ((c.qa, c.da, ya, "gate"), (c.qb, c.db, yb, "up")):
-        ref, A = oracle.gemv_rows(q, d, x, rows, threads())
-        assert_parity(y[:, rows], ref, A, what=f"{name} N={N}")
+        if N in (1, 8):
+            ref, A = oracle.gemv(q, d, x, threads())
+            assert_parity(y, ref, A, what=f"{name} N={N} all rows")
+        else:
+            ref, A = oracle.gemv_rows(q, d, x, rows, threads())
+            assert_parity(y[:, rows], ref, A, what=f"{name} N={N}")
     # the pair equals two single GEMVs bitwise
     sa = host(q8.gemv(Wa, dev(x)))
     sb = host(q8.gemv(Wb, dev(x)))
@@ -81,15 +86,20 @@ def check_silu(h, r, what):
 
 
 @pytest.mark.parametrize("N", [1, 4, 8])
-def test_full_size_silu_sampled_rows(full_pair, N):
+def test_full_size_silu(full_pair, N):
+    """Every output at N = 1 and 8; a sample of rows at 4."""
     note(f"pair+silu 17408x5120 N={N}")
     c, Wa, Wb = full_pair
     x = c.x[:N]
     h = host(q8.gemv_pair_silu(Wa, Wb, dev(x)))
-    rng = np.random.default_rng(100 + N)
-    rows = np.unique(np.concatenate([[0, 1, 17407], rng.choice(17408, 1500, replace=False)]))
-    r = oracle.gate_up_silu(c.qa[rows], c.da[rows], c.qb[rows], c.db[rows], x, threads())
-    check_silu(h[:, rows], r, f"N={N}")
+    if N in (1, 8):
+        r = oracle.gate_up_silu(c.qa, c.da, c.qb, c.db, x, threads())
+        check_silu(h, r, f"N={N} all rows")
+    else:
+        rng = np.random.default_rng(100 + N)
+        rows = np.unique(np.concatenate([[0, 1, 17407], rng.choice(17408, 1500, replace=False)]))
+        r = oracle.gate_up_silu(c.qa[rows], c.da[rows], c.qb[rows], c.db[rows], x, threads())
+        check_silu(h[:, rows], r, f"N={N}")
     # h is silu of the pair's own g and u, within fp32 rounding of the epilogue
     ya, yb = (host(t).astype(np.float64) for t in q8.gemv_pair(Wa, Wb, dev(x)))
     ref = oracle.silu(ya) * yb

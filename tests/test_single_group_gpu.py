@@ -152,7 +152,8 @@ def test_streaming_silu_pair():
 
 
 @pytest.mark.parametrize("M,K,q4,xf32", [(768, 2048, False, False), (1408, 1024, True, False),
-                                         (300, 96, False, True)])
+                                         (300, 96, False, True), (768, 2048, False, True),
+                                         (256, 512, False, True), (512, 1024, True, True)])
 def test_silu_pair_resident_3_to_8_tokens(M, K, q4, xf32):
     """The SiLU pair's one-group kernel at 3-8 tokens (taken when every
     group fits the resident waves): each token's h is bitwise its one-token
