@@ -300,6 +300,26 @@ int q8_moe_ffn(const q8_bank *gate, const q8_bank *up, const q8_bank *down,
                const int32_t *expert_ids, const float *gate_w, const void *x, int x_dt,
                float *out, int T, int topk, void *ws, size_t ws_bytes, void *stream);
 
+/* The same routed FFN for callers that cannot allocate or hand over a
+ * workspace (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the workspace is the library's own scratch array
+ * of q8_noalloc_scratch_bytes() bytes (8 MiB) per GPU, a static device
+ * array allocated with the library's code object on each GPU it runs on
+ * and held until the process ends. The call allocates nothing and calls
+ * no allocating routine. Arguments, results and errors are those of
+ * q8_moe_ffn (bitwise the same outputs), except:
+ *   - Q8_ERR_WORKSPACE when the workspace this shape needs,
+ *     q8_moe_ws_bytes(E, T, topk, F, H), exceeds the scratch size
+ *     (e.g. E = 128, F = 768, H = 2048, top-8: up to 88 tokens);
+ *   - all calls on one GPU share that GPU's array, which keeps the last
+ *     call's contents: calls that overlap on one GPU (concurrent streams,
+ *     threads) race and must be serialised by the caller. Every call
+ *     rewrites everything it reads, so nothing needs clearing. */
+size_t q8_noalloc_scratch_bytes(void);
+int q8_moe_ffn_noalloc(const q8_bank *gate, const q8_bank *up, const q8_bank *down,
+                       const int32_t *expert_ids, const float *gate_w, const void *x, int x_dt,
+                       float *out, int T, int topk, void *stream);
+
 /* ------------------------------------------------------------ router
  * The step upstream of the routed experts, kept on the device so the
  * routed layer replays as a graph with no host round-trip (memra wiki,

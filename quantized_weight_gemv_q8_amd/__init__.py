@@ -34,6 +34,7 @@ EXPORTS = (
     "q8_lmhead_argmax_rows",
     "q8_moe_ws_bytes", "q8_moe_ws_layout", "q8_moe_gemv", "q8_moe_ffn", "q8_moe_topk_softmax",
     "q8_moe_router", "q8_moe_shared_ws_bytes", "q8_moe_shared_expert",
+    "q8_noalloc_scratch_bytes", "q8_moe_ffn_noalloc",
 )
 
 
@@ -94,6 +95,8 @@ def lib() -> ctypes.CDLL:
             "q8_moe_router": ([pm, vp, i32, i32, i32, vp, vp, vp, vp], i32),
             "q8_moe_shared_ws_bytes": ([i64, i64, i32], sz),
             "q8_moe_shared_expert": ([pm, pm, pm, pm, vp, i32, i32, vp, vp, sz, vp], i32),
+            "q8_noalloc_scratch_bytes": ([], sz),
+            "q8_moe_ffn_noalloc": ([pb, pb, pb, vp, vp, vp, i32, vp, i32, i32, vp], i32),
         }
         for name, (args, res) in sig.items():
             fn = getattr(L, name)
@@ -512,6 +515,31 @@ def moe_ffn(gate: PackedBank, up: PackedBank, down: PackedBank, expert_ids, gate
                             ctypes.byref(down.cbank()), expert_ids.data_ptr(), gate_w.data_ptr(),
                             x.data_ptr(), _dt(x), out.data_ptr(), T, topk, ws.data_ptr(),
                             ws.numel(), _stream(stream)), "q8_moe_ffn")
+    return out
+
+
+def noalloc_scratch_bytes() -> int:
+    return lib().q8_noalloc_scratch_bytes()
+
+
+def moe_ffn_noalloc(gate: PackedBank, up: PackedBank, down: PackedBank, expert_ids, gate_w, x,
+                    out=None, stream=None):
+    """q8_moe_ffn on the library's own scratch array (no workspace; calls on
+    one GPU must not overlap). Returns out fp32 [T][H]."""
+    import torch
+    T, topk = expert_ids.shape
+    H = gate.K
+    _need(expert_ids, (T, topk), (torch.int32,), "expert_ids")
+    _need(gate_w, (T, topk), (torch.float32,), "gate_w")
+    _need(x, (T, H), _f(torch), "x")
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.float32, device=x.device)
+    _need(out, (T, H), (torch.float32,), "out")
+    _on_gpu(gate, up, down, expert_ids, gate_w, x, out)
+    _check(lib().q8_moe_ffn_noalloc(ctypes.byref(gate.cbank()), ctypes.byref(up.cbank()),
+                                    ctypes.byref(down.cbank()), expert_ids.data_ptr(),
+                                    gate_w.data_ptr(), x.data_ptr(), _dt(x), out.data_ptr(), T,
+                                    topk, _stream(stream)), "q8_moe_ffn_noalloc")
     return out
 
 

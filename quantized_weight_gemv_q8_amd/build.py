@@ -24,7 +24,8 @@ LIB = os.path.join(PKG, "libq8gemv.so")
 # token count of the one-group kernels, the largest units of the library,
 # so that they compile in parallel.
 SOURCES = [(src, os.path.splitext(src)[0], ()) for src in
-           ("q8_api.cpp", "q8_gemv.hip", "q8_lmhead.hip", "q8_moe.hip", "q8_router.hip")]
+           ("q8_api.cpp", "q8_gemv.hip", "q8_lmhead.hip", "q8_moe.hip", "q8_router.hip",
+            "q8_noalloc.hip")]
 SOURCES += [("q8_once.hip", f"q8_once_{'glu' if glu else 'dense'}{nt}",
              (f"-DQ8_ONCE_NT={nt}", f"-DQ8_ONCE_GLU={glu}"))
             for nt in range(8, 0, -1) for glu in (0, 1)]

@@ -454,9 +454,13 @@ int q8_moe_gemv(const q8_bank* W, const int32_t* expert_ids, const float* gate_w
   return Q8_OK;
 }
 
-int q8_moe_ffn(const q8_bank* gate, const q8_bank* up, const q8_bank* down,
-               const int32_t* expert_ids, const float* gate_w, const void* x, int x_dt,
-               float* out, int T, int topk, void* ws, size_t ws_bytes, void* stream) {
+// The routed FFN on a workspace ws of ws_bytes; no_alloc: ws is the
+// library's scratch array (its size is checked here, before the runtime is
+// touched, and it cannot alias the caller's buffers).
+static int moe_ffn_impl(const q8_bank* gate, const q8_bank* up, const q8_bank* down,
+                        const int32_t* expert_ids, const float* gate_w, const void* x, int x_dt,
+                        float* out, int T, int topk, void* ws, size_t ws_bytes, bool no_alloc,
+                        void* stream) {
   int rc = check_bank(gate);
   if (rc) return rc;
   if ((rc = check_bank(up)) || (rc = check_bank(down))) return rc;
@@ -473,15 +477,20 @@ int q8_moe_ffn(const q8_bank* gate, const q8_bank* up, const q8_bank* down,
   const size_t xs = dt_size(x_dt);
   if (!xs) return Q8_ERR_DTYPE;
   if (!aligned(x, 16) || !aligned(out, 4)) return Q8_ERR_ALIGN;
-  if (!ws || !aligned(ws, 16) || ws_bytes < q8_moe_ws_bytes(E, T, topk, F, H))
+  const size_t need = q8_moe_ws_bytes(E, T, topk, F, H);
+  if (no_alloc) {
+    if (need > q8::kNoAllocScratchBytes) return Q8_ERR_WORKSPACE;
+  } else if (!ws || !aligned(ws, 16) || ws_bytes < need) {
     return Q8_ERR_WORKSPACE;
+  }
   const size_t xbytes = (size_t)T * H * xs, obytes = (size_t)T * H * 4;
-  if (overlap(x, xbytes, out, obytes) || overlap(ws, ws_bytes, x, xbytes) ||
-      overlap(ws, ws_bytes, out, obytes))
+  if (overlap(x, xbytes, out, obytes) ||
+      (!no_alloc && (overlap(ws, ws_bytes, x, xbytes) || overlap(ws, ws_bytes, out, obytes))))
     return Q8_ERR_ALIAS;
   const DevInfo* dev = nullptr;
   rc = current_device(&dev);
   if (rc) return rc;
+  if (no_alloc && q8::noalloc_scratch(dev->device, &ws) != hipSuccess) return Q8_ERR_DEVICE;
   const bool xf = x_dt == Q8_DT_F32;
   if (!q8::moe_fits(*dev, H, xf) || !q8::moe_fits(*dev, F, true)) return Q8_ERR_SHAPE;
   const int P = T * topk;
@@ -496,6 +505,22 @@ int q8_moe_ffn(const q8_bank* gate, const q8_bank* up, const q8_bank* down,
       hipSuccess)
     return Q8_ERR_LAUNCH;
   return launch_rc(q8::launch_moe_combine(expert_ids, E, gate_w, w.y_pair, out, T, topk, H, s));
+}
+
+int q8_moe_ffn(const q8_bank* gate, const q8_bank* up, const q8_bank* down,
+               const int32_t* expert_ids, const float* gate_w, const void* x, int x_dt,
+               float* out, int T, int topk, void* ws, size_t ws_bytes, void* stream) {
+  return moe_ffn_impl(gate, up, down, expert_ids, gate_w, x, x_dt, out, T, topk, ws, ws_bytes,
+                      false, stream);
+}
+
+size_t q8_noalloc_scratch_bytes(void) { return q8::kNoAllocScratchBytes; }
+
+int q8_moe_ffn_noalloc(const q8_bank* gate, const q8_bank* up, const q8_bank* down,
+                       const int32_t* expert_ids, const float* gate_w, const void* x, int x_dt,
+                       float* out, int T, int topk, void* stream) {
+  return moe_ffn_impl(gate, up, down, expert_ids, gate_w, x, x_dt, out, T, topk, nullptr, 0,
+                      true, stream);
 }
 
 // ------------------------------------------------------------ shared expert

@@ -85,6 +85,13 @@ hipError_t launch_lmhead(const DevInfo& dev, const HMat& W, const int32_t* row_i
                          bool x_f32, float* logits, int64_t ld_logits, int32_t* ids, char* ws,
                          int nt, hipStream_t s);
 
+// The scratch array of the entry points that allocate nothing: its
+// address on device `device`, which must be the current device (taken
+// once per device with hipGetSymbolAddress, q8_noalloc.hip).
+// kNoAllocScratchBytes is its size.
+constexpr size_t kNoAllocScratchBytes = (size_t)8 << 20;
+hipError_t noalloc_scratch(int device, void** ptr);
+
 // Routed experts.
 struct MoeWs {
   int32_t* counts;   // [E]

@@ -391,3 +391,25 @@ def test_bindings_check_packed_planes():
     good = q8.PackedBank(bank_q, bank_d, 64, 256, 4)
     with pytest.raises(ValueError, match="on the GPU"):
         q8.moe_gemv(good, ids, x, gate_w=gw)
+
+
+def test_moe_noalloc_validation(L):
+    """The no-allocation routed FFN validates like q8_moe_ffn and refuses a
+    shape whose workspace exceeds the library's scratch array before it
+    touches the runtime; a shape that fits gets as far as the device check."""
+    assert L.q8_noalloc_scratch_bytes() == 8 << 20
+    E, topk = 8, 2
+    IDS, GW, XX, OUT = 0x800000, 0x810000, 0x820000, 0x90000000
+
+    def rc(T, F, H):
+        g = _bank(_mat(M=F, K=H), E)
+        u = _bank(_mat(qs=0x4000000, d=0x5000000, M=F, K=H), E)
+        dn = _bank(_mat(qs=0x6000000, d=0x7000000, M=H, K=F), E)
+        return L.q8_moe_ffn_noalloc(ctypes.byref(g), ctypes.byref(u), ctypes.byref(dn), IDS, GW,
+                                    XX, 1, OUT, T, topk, None)
+    assert L.q8_moe_ws_bytes(E, 1024, topk, 1024, 2048) > L.q8_noalloc_scratch_bytes()
+    assert rc(1024, 1024, 2048) == -5
+    assert rc(4, 64, 128) == -6  # fits; no gfx950 device on this host
+    g = _bank(_mat(M=64, K=128), E)
+    assert L.q8_moe_ffn_noalloc(ctypes.byref(g), ctypes.byref(g), ctypes.byref(g), 0, GW, XX, 1,
+                                OUT, 4, topk, None) in (-1, -2)
