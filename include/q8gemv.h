@@ -148,9 +148,14 @@ int q8_unpack_host(const int8_t *qs, int64_t ld_qs, const uint16_t *d, int64_t l
  *     16-byte aligned.
  *   y [dev] [N][W->M], dtype y_dt (Q8_DT_F32, or Q8_DT_F16 rounded to
  *     nearest even), contiguous; must not overlap x.
- *   N >= 1. N > 8 runs as consecutive passes of at most 8 tokens; per-token
- *   results stay bitwise identical to N = 1.
- * Every weight byte is read once per pass of up to 8 tokens. */
+ *   N >= 1. Tokens run in passes, every weight byte read once per pass:
+ *   passes of up to 16 tokens for Q8_0 weights and fp16 x with rows of
+ *   64 lanes (K a multiple of 1024, e.g. 5120) and at least 12 row groups
+ *   of 4 rows per CU (rows >= 12288 on a 256-CU MI355X; the 9..16-token
+ *   verify of the pages' K+1 speculative step, memra wiki feature list),
+ *   passes of up to 8 tokens otherwise;
+ *   fewer if the x image of a pass would not fit the LDS. Per-token
+ *   results are bitwise identical to N = 1 whatever the pass size. */
 int q8_gemv(const q8_matrix *W, const void *x, int x_dt, void *y, int y_dt, int N,
             void *stream);
 
@@ -164,7 +169,7 @@ int q8_gemv(const q8_matrix *W, const void *x, int x_dt, void *y, int y_dt, int 
  *   overlap x or each other (Q8_ERR_ALIAS).
  * Results are bitwise equal to two q8_gemv calls (same per-row
  * arithmetic). No activation is applied (q8_gemv_pair_silu applies it).
- * N >= 1, passes of up to 8 tokens as for q8_gemv. */
+ * N >= 1, passes as for q8_gemv (rows = Wa->M + Wb->M). */
 int q8_gemv_pair(const q8_matrix *Wa, const q8_matrix *Wb, const void *x, int x_dt,
                  void *ya, void *yb, int y_dt, int N, void *stream);
 
@@ -176,7 +181,8 @@ int q8_gemv_pair(const q8_matrix *Wa, const q8_matrix *Wb, const void *x, int x_
  * (fp32, or fp16 rounded to nearest even), so the MLP's down projection
  * reads N*M values instead of 2*N*M. Wg and Wu have the same M and K.
  * x [dev] [N][K] of x_dt; h [dev] [N][M] of h_dt, must not overlap x.
- * N >= 1 (passes of up to 8 tokens, per-token results N-invariant). */
+ * N >= 1 (passes as for q8_gemv with rows = 2 * M; per-token results
+ * N-invariant). */
 int q8_gemv_pair_silu(const q8_matrix *Wg, const q8_matrix *Wu, const void *x, int x_dt,
                       void *h, int h_dt, int N, void *stream);
 

@@ -255,7 +255,10 @@ static int gemv_impl(const q8_matrix* Wa, const q8_matrix* Wb, const void* x, in
   rc = current_device(&dev);
   if (rc) return rc;
   const bool xf = x_dt == Q8_DT_F32;
-  const int per_pass = q8::max_tokens_per_pass(*dev, Wa->K, xf);
+  const int64_t rows = Wa->M + (Wb ? Wb->M : 0);
+  const int per_pass = q8::wide_pass_applies(*dev, Wa->format, Wa->K, xf, rows)
+                           ? q8::max_tokens_per_pass_wide(*dev, Wa->K, xf)
+                           : q8::max_tokens_per_pass(*dev, Wa->K, xf);
   if (per_pass < 1) return Q8_ERR_SHAPE;
   const HMat A = to_h(Wa);
   HMat B;
@@ -299,7 +302,9 @@ int q8_gemv_pair_silu(const q8_matrix* Wg, const q8_matrix* Wu, const void* x, i
   rc = current_device(&dev);
   if (rc) return rc;
   const bool xf = x_dt == Q8_DT_F32;
-  const int per_pass = q8::max_tokens_per_pass(*dev, Wg->K, xf);
+  const int per_pass = q8::wide_pass_applies(*dev, Wg->format, Wg->K, xf, 2 * Wg->M)
+                           ? q8::max_tokens_per_pass_wide(*dev, Wg->K, xf)
+                           : q8::max_tokens_per_pass(*dev, Wg->K, xf);
   if (per_pass < 1) return Q8_ERR_SHAPE;
   const HMat G = to_h(Wg), U = to_h(Wu);
   for (int n0 = 0; n0 < N; n0 += per_pass) {

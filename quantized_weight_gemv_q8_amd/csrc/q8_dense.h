@@ -35,6 +35,7 @@ struct DenseEpi {
   char* yb;
   int64_t Ma, Mtot;
   bool f16;
+  int nt = kMaxNTWide;  // live tokens: only a kernel whose token count is a runtime value sets it
   template <int NT, int R, int CNT>
   __device__ __forceinline__ void emit(int64_t rbase, int base, bool owner, const float* v) {
     if (!owner) return;
@@ -44,7 +45,7 @@ struct DenseEpi {
       if (idx >= NT * R) continue;
       const int n = idx / R, r = idx - (idx / R) * R;
       const int64_t row = rbase + r;
-      if (row >= Mtot) continue;
+      if (row >= Mtot || n >= nt) continue;
       char* y;
       int64_t col, ld;
       if (row < Ma) { y = ya; col = row; ld = Ma; }
@@ -82,13 +83,14 @@ struct GluEpi {
   char* h;
   int64_t M;
   bool f16;
+  int nt = kMaxNTWide;  // live tokens, as for DenseEpi
   template <int NT, int R, int CNT>
   __device__ __forceinline__ void emit(int64_t rbase, int base, bool owner, const float* v) {
     static_assert(R % 2 == 0 && CNT == 2, "gate/up pairs");
     if (!owner || base >= NT * R) return;
     const int n = base / R, r = base - (base / R) * R;
     const int64_t row = rbase + r;  // the gate row of the pair (even)
-    if (row >= 2 * M) return;
+    if (row >= 2 * M || n >= nt) return;
     const float g = v[0], u = v[1];
     const float val = g / (1.0f + expf(-g)) * u;
     const int64_t o = (int64_t)n * M + (row >> 1);

@@ -228,7 +228,7 @@ __device__ __forceinline__ void chunk_fma(const uint4* q, const uint32_t* d, con
     for (int r = 0; r < R; ++r) quants_to_h2(q[r], qh[r]);
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
-      if (n >= nt) break;
+      if (n >= nt) continue;  // not break: a fixed trip count keeps acc[] in registers
       const uint4 xlo = xb[(n * P + 0) * C + c];
       const uint4 xhi = xb[(n * P + 1) * C + c];
 #pragma unroll
@@ -243,7 +243,7 @@ __device__ __forceinline__ void chunk_fma(const uint4* q, const uint32_t* d, con
     for (int r = 0; r < R; ++r) quants_to_f32(q[r], qf[r]);
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
-      if (n >= nt) break;
+      if (n >= nt) continue;  // not break: a fixed trip count keeps acc[] in registers
       const float4 x0 = __builtin_bit_cast(float4, xb[(n * P + 0) * C + c]);
       const float4 x1 = __builtin_bit_cast(float4, xb[(n * P + 1) * C + c]);
       const float4 x2 = __builtin_bit_cast(float4, xb[(n * P + 2) * C + c]);
@@ -260,7 +260,7 @@ __device__ __forceinline__ void chunk_fma(const uint4* q, const uint32_t* d, con
     for (int r = 0; r < R; ++r) nibbles_to_h2(q[r], qh[r]);
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
-      if (n >= nt) break;
+      if (n >= nt) continue;  // not break: a fixed trip count keeps acc[] in registers
       uint4 xs[4];
 #pragma unroll
       for (int h = 0; h < 4; ++h) xs[h] = xb[(n * P + h) * C + c];
@@ -283,7 +283,7 @@ __device__ __forceinline__ void chunk_fma(const uint4* q, const uint32_t* d, con
     for (int half = 0; half < 2; ++half) {
 #pragma unroll
       for (int n = 0; n < NT; ++n) {
-        if (n >= nt) break;
+        if (n >= nt) continue;  // not break: a fixed trip count keeps acc[] in registers
         uint4 xv[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) xv[i] = xb[(n * P + 4 * half + i) * C + c];
@@ -293,7 +293,7 @@ __device__ __forceinline__ void chunk_fma(const uint4* q, const uint32_t* d, con
     }
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
-      if (n >= nt) break;
+      if (n >= nt) continue;  // not break: a fixed trip count keeps acc[] in registers
 #pragma unroll
       for (int r = 0; r < R; ++r) acc[n * R + r] = __builtin_fmaf(df[r], sum[n][r], acc[n * R + r]);
     }
@@ -515,12 +515,32 @@ __device__ __forceinline__ float xor_lane(float v) {
   return __builtin_bit_cast(float, r);
 }
 
+// v + (the v of lane ^ DELTA), the same bits in both lanes of each pair
+// (fp32 addition is commutative).
+template <int DELTA>
+__device__ __forceinline__ float pair_sum(float v) {
+  return v + xor_lane<DELTA>(v);
+}
+
+// One halving level over a pair of values (a, b): a lane whose DELTA bit is
+// clear returns a + (its partner's a), one whose bit is set b + (its
+// partner's b); the lane selects what to send and what to keep. (Adding
+// the two results of one permlane swap of a against b would give the same
+// sums without the selects, but this compiler folds that sum into twice
+// the first result, so the swap's results are only ever selected.)
+template <int DELTA>
+__device__ __forceinline__ float half_sum(float a, float b, bool hi) {
+  const float send = hi ? a : b;
+  const float keep = hi ? b : a;
+  return keep + xor_lane<DELTA>(send);
+}
+
 // ---------------------------------------------------------------- team reduction
 // Butterfly over the LPR lanes of a team, xor distances LPR/2, LPR/4, ..., 1.
 // While a lane carries more than MINC values, each level halves them
 // (the lane keeps the half selected by its distance bit and receives the
 // partner's copy of that half), so R*NT sums cost about R*NT shuffles
-// instead of log2(LPR) each (the exchanges use xor_lane). Every value is
+// instead of log2(LPR) each (the exchanges use half_sum and pair_sum). Every value is
 // summed over the same pairing
 // tree (partners differing in bit LPR/2, then LPR/4, ...), whatever the
 // number of values carried, so the result of each (row, token) does not
@@ -536,18 +556,14 @@ struct TeamReduce {
       const bool hi = (p & DELTA) != 0;
       float nv[H];
 #pragma unroll
-      for (int i = 0; i < H; ++i) {
-        const float send = hi ? v[i] : v[i + H];
-        const float keep = hi ? v[i + H] : v[i];
-        nv[i] = keep + xor_lane<DELTA>(send);
-      }
+      for (int i = 0; i < H; ++i) nv[i] = half_sum<DELTA>(v[i], v[i + H], hi);
 #pragma unroll
       for (int i = 0; i < H; ++i) v[i] = nv[i];
       if (hi) base += H;
       TeamReduce<H, MINC, DELTA / 2>::run(v, p, base);
     } else {
 #pragma unroll
-      for (int i = 0; i < CNT; ++i) v[i] = v[i] + xor_lane<DELTA>(v[i]);
+      for (int i = 0; i < CNT; ++i) v[i] = pair_sum<DELTA>(v[i]);
       TeamReduce<CNT, MINC, DELTA / 2>::run(v, p, base);
     }
   }

@@ -66,6 +66,93 @@ __global__ __launch_bounds__(kBlock) void gemv_kernel(DenseMap map, DenseEpi epi
                                             (int64_t)gridDim.x * kWavesPerBlock, 0, stage);
 }
 
+// ---------------------------------------------------------------- 9..16 tokens
+// Passes of 9 to 16 tokens (the K+1 verify at K = 8 and wider batched
+// decode) run one persistent kernel per kind whose token count nt is a
+// runtime value: tokens n >= nt are neither staged, computed nor stored, so
+// every weight byte is read once for all of them instead of once per pass
+// of 8. Four rows per team (so each LDS read of x serves four rows), two
+// for the SiLU pair's 16-lane teams (whose reduction must leave one gate/up
+// pair per lane). Per (row, token) the arithmetic is that of every other
+// dense kernel, so the results stay bitwise N-invariant.
+template <int LPR, bool GLU>
+constexpr int wide_rows() { return GLU && LPR == 16 ? 2 : 4; }
+// One workgroup per CU (a 16-token image of a 5120-wide x takes the whole
+// LDS), so the workgroup holds as many waves as the registers allow. Q8_0
+// weights, fp16 activations and 64-lane rows: two chunks in flight per
+// wave (D = 2, 140 registers a lane) and 12 waves; measured on MI355X for
+// the 2 x 17408 x 5120 pair, 16 waves with one chunk in flight take 81.6
+// (N = 9) and 114.4 us (N = 16), 12 waves with two 70.2 and 96.7 us. Other
+// formats and row widths (wider chunk or reduction state): one chunk in
+// flight and 8 waves.
+template <int F, int LPR, bool XF32>
+constexpr bool wide_deep() { return F == kFmtQ8 && !XF32 && LPR == 64; }
+template <int F, int LPR, bool XF32>
+constexpr int wide_depth() { return wide_deep<F, LPR, XF32>() ? 2 : 1; }
+template <int F, int LPR, bool XF32>
+constexpr int wide_block() { return wide_deep<F, LPR, XF32>() ? 768 : 512; }
+
+template <int F, int LPR, bool XF32, int MINC, int R, class Map, class Epi>
+__device__ __forceinline__ void wide_body(const Map& map, Epi& epi, int64_t rows, const char* x,
+                                          int64_t ldx_bytes, int C, int nt) {
+  extern __shared__ uint4 lds_x[];
+  constexpr int NT = kMaxNTWide;
+  constexpr int G = (kWave / LPR) * R;
+  const int64_t n_groups = (rows + G - 1) / G;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  auto stage = [=]() {
+    const char* xr[NT];
+#pragma unroll
+    for (int n = 0; n < NT; ++n) xr[n] = x + (n < nt ? n : 0) * ldx_bytes;
+    stage_fmt<F, NT, XF32>(xr, C, lds_x, nt);
+    __syncthreads();
+  };
+  const int wpb = (int)(blockDim.x / kWave);
+  run_rows<NT, LPR, R, wide_depth<F, LPR, XF32>(), MINC, XF32, F>(map, epi, lds_x, C, n_groups,
+                                              (int64_t)blockIdx.x * wpb + wave,
+                                              (int64_t)gridDim.x * wpb, 0, stage, nt);
+}
+
+template <int F, int LPR, bool XF32>
+__global__ __launch_bounds__((wide_block<F, LPR, XF32>())) void gemv_wide_kernel(DenseMap map, DenseEpi epi,
+                                                           const char* x, int64_t ldx_bytes, int C,
+                                                           int nt) {
+  wide_body<F, LPR, XF32, 1, wide_rows<LPR, false>()>(map, epi, map.Mtot, x, ldx_bytes, C, nt);
+}
+
+template <int F, int LPR, bool XF32>
+__global__ __launch_bounds__((wide_block<F, LPR, XF32>())) void glu_wide_kernel(GluMap map, GluEpi epi, const char* x,
+                                                          int64_t ldx_bytes, int C, int nt) {
+  wide_body<F, LPR, XF32, 2, wide_rows<LPR, true>()>(map, epi, map.M2, x, ldx_bytes, C, nt);
+}
+
+// Persistent launch of a wide kernel over `rows` virtual rows (nt tokens
+// staged: nt * C * 16 * P bytes of LDS).
+template <int F, int LPR, bool XF32, class Map, class Epi>
+static hipError_t wide_launch(const DevInfo& dev, const void* fn, int G, Map map, Epi epi,
+                              int64_t rows, const char* x, int64_t ldx_bytes, int C, int nt,
+                              hipStream_t s) {
+  const size_t lds = (size_t)nt * C * 16 * ChunkPlanes<F, XF32>::P;
+  if (nt <= kMaxNT || nt > kMaxNTWide || lds > dev.lds_per_block) return hipErrorInvalidValue;
+  if (hipError_t e = allow_dynamic_lds(fn, lds)) return e;
+  // Waves per workgroup: as many as the row groups need for one workgroup
+  // per CU, up to the kernel's maximum (a small matrix then still spreads
+  // over every CU instead of filling a few CUs with 16 waves each).
+  constexpr int WMAX = wide_block<F, LPR, XF32>() / kWave;
+  const int64_t groups = (rows + G - 1) / G;
+  int64_t w = (groups + dev.cus - 1) / dev.cus;
+  if (w > WMAX) w = WMAX;
+  if (w < 1) w = 1;
+  const int threads = (int)w * kWave;
+  const int64_t need = (groups + w - 1) / w;
+  int64_t blocks = (int64_t)dev.cus * blocks_per_cu(fn, lds, threads);
+  if (blocks > need) blocks = need;
+  if (blocks < 1) blocks = 1;
+  epi.nt = nt;
+  void* args[] = {&map, &epi, (void*)&x, &ldx_bytes, &C, &nt};
+  return hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(threads), args, lds, s);
+}
+
 // ---------------------------------------------------------------- gate/up + SiLU
 template <int NT, bool BIG>
 struct GluTune {
@@ -146,6 +233,12 @@ hipError_t launch_glu(const DevInfo& dev, const HMat& Gm, const HMat& Um, const 
   const int C = (int)chunks_per_row(Gm.fmt, Gm.K);
   const int64_t ldx_bytes = Gm.K * (x_f32 ? 4 : 2);
   const char* xp = (const char*)x;
+  if (nt > kMaxNT) {
+    if (!wide_pass_applies(dev, Gm.fmt, Gm.K, x_f32, map.M2)) return hipErrorInvalidValue;
+    return wide_launch<kFmtQ8, 64, false>(dev, (const void*)glu_wide_kernel<kFmtQ8, 64, false>,
+                                          wide_rows<64, true>(), map, epi, map.M2, xp, ldx_bytes,
+                                          C, nt, s);
+  }
   {
     const hipError_t e = launch_glu_once(nt, dev, map, epi, Gm.fmt, lanes_for(Gm.fmt, Gm.K), x_f32,
                                          xp, ldx_bytes, C, s);
@@ -294,6 +387,28 @@ int max_tokens_per_pass(const DevInfo& dev, int64_t K, bool x_f32) {
   return (int)n;
 }
 
+int max_tokens_per_pass_wide(const DevInfo& dev, int64_t K, bool x_f32) {
+  const size_t per = x_lds_bytes(1, K, x_f32);
+  if (per == 0) return kMaxNTWide;
+  size_t n = dev.lds_per_block / per;
+  if (n > (size_t)kMaxNTWide) n = kMaxNTWide;
+  return (int)n;
+}
+
+// Passes of 9..16 tokens run the wide kernel for Q8_0 weights, fp16
+// activations and 64-lane rows, and only when the matrix has row groups for
+// a full workgroup on every CU (groups of four rows, twelve waves): below
+// that, the one-row-group-per-wave kernels of two passes of at most 8 are
+// faster (measured on MI355X at 5120 x 5120: N = 9 and 16 in 21.4 and
+// 27.6 us wide, against 17.4 and 23.7 us as two passes; the 2 x 17408 x
+// 5120 pair, 34 row groups per CU, takes 70.2 and 96.7 us wide against 85
+// and 114 us as two passes).
+bool wide_pass_applies(const DevInfo& dev, int fmt, int64_t K, bool x_f32, int64_t rows) {
+  if (fmt != kFmtQ8 || x_f32 || lanes_for(fmt, K) != 64) return false;
+  const int64_t groups = (rows + 3) / 4;
+  return groups >= (int64_t)(wide_block<kFmtQ8, 64, false>() / kWave) * dev.cus;
+}
+
 hipError_t launch_gemv(const DevInfo& dev, const HMat& A, const HMat* B, const void* x,
                        bool x_f32, int64_t ldx, void* ya, void* yb, bool y_f16, int nt,
                        hipStream_t s) {
@@ -317,6 +432,12 @@ hipError_t launch_gemv(const DevInfo& dev, const HMat& A, const HMat* B, const v
   const int C = (int)chunks_per_row(A.fmt, A.K);
   const int64_t ldx_bytes = ldx * (x_f32 ? 4 : 2);
   const char* xp = (const char*)x;
+  if (nt > kMaxNT) {
+    if (!wide_pass_applies(dev, A.fmt, A.K, x_f32, map.Mtot)) return hipErrorInvalidValue;
+    return wide_launch<kFmtQ8, 64, false>(dev, (const void*)gemv_wide_kernel<kFmtQ8, 64, false>,
+                                          wide_rows<64, false>(), map, epi, map.Mtot, xp,
+                                          ldx_bytes, C, nt, s);
+  }
   return dispatch_chunks(A.fmt, lanes_for(A.fmt, A.K), x_f32, [&](auto f, auto l, auto xf) {
     return launch_nt<decltype(f)::value, decltype(l)::value, decltype(xf)::value>(
         dev, nt, map, epi, xp, ldx_bytes, C, s);

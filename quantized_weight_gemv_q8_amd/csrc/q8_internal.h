@@ -12,6 +12,11 @@
 
 namespace q8 {
 
+// Tokens per pass of the dense GEMV, the pair and the SiLU pair (passes of
+// 9..16 tokens run a kernel with a runtime token count; other kernels take
+// passes of at most 8).
+constexpr int kMaxNTWide = 16;
+
 struct DevInfo {
   int device;
   int cus;             // compute units
@@ -71,8 +76,15 @@ inline size_t x_lds_bytes(int nt, int64_t K, bool x_f32) {
 
 // Largest token count per pass that fits the LDS limit (<= 8), 0 if none.
 int max_tokens_per_pass(const DevInfo& dev, int64_t K, bool x_f32);
+// The same for the dense GEMV, the pair and the SiLU pair, whose passes of
+// 9..16 tokens run one kernel with the token count as a runtime value
+// (<= 16), when wide_pass_applies.
+int max_tokens_per_pass_wide(const DevInfo& dev, int64_t K, bool x_f32);
+// Whether passes of 9..16 tokens over `rows` rows (2M for the SiLU pair)
+// take the wide kernel; otherwise passes are of at most 8 tokens.
+bool wide_pass_applies(const DevInfo& dev, int fmt, int64_t K, bool x_f32, int64_t rows);
 
-// y[n] = A x[n] (and yb[n] = B x[n] when B != nullptr) for nt <= 8 tokens.
+// y[n] = A x[n] (and yb[n] = B x[n] when B != nullptr) for nt <= 16 tokens.
 hipError_t launch_gemv(const DevInfo& dev, const HMat& A, const HMat* B, const void* x,
                        bool x_f32, int64_t ldx, void* ya, void* yb, bool y_f16, int nt,
                        hipStream_t s);

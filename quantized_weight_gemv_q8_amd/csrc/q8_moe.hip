@@ -647,12 +647,12 @@ __global__ __launch_bounds__(256) void shared_gate_add_kernel(const int8_t* gq, 
     }
     acc = __builtin_fmaf(half_bits_to_float(gd[k0 / 32]), s, acc);
   }
-  acc += xor_lane<32>(acc);
-  acc += xor_lane<16>(acc);
-  acc += xor_lane<8>(acc);
-  acc += xor_lane<4>(acc);
-  acc += xor_lane<2>(acc);
-  acc += xor_lane<1>(acc);
+  acc = pair_sum<32>(acc);
+  acc = pair_sum<16>(acc);
+  acc = pair_sum<8>(acc);
+  acc = pair_sum<4>(acc);
+  acc = pair_sum<2>(acc);
+  acc = pair_sum<1>(acc);
   if ((threadIdx.x & (kWave - 1)) == 0) part[threadIdx.x / kWave] = acc;
   __syncthreads();
   float gsum = 0.0f;

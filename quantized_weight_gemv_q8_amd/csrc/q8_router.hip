@@ -48,12 +48,12 @@ __device__ __forceinline__ void softmax_picks(float mine, int topk, int64_t t, f
       float, __builtin_amdgcn_readlane(__builtin_bit_cast(unsigned, mine), 0));
   const float z = lane < topk ? expf(mine - top) : 0.0f;
   float s = z;
-  s += xor_lane<32>(s);
-  s += xor_lane<16>(s);
-  s += xor_lane<8>(s);
-  s += xor_lane<4>(s);
-  s += xor_lane<2>(s);
-  s += xor_lane<1>(s);
+  s = pair_sum<32>(s);
+  s = pair_sum<16>(s);
+  s = pair_sum<8>(s);
+  s = pair_sum<4>(s);
+  s = pair_sum<2>(s);
+  s = pair_sum<1>(s);
   if (lane < topk) gate_w[t * topk + lane] = z / s;
 }
 
