@@ -364,17 +364,20 @@ int q8_moe_router(const q8_matrix *Wr, const void *x, int x_dt, int T, int topk,
  * fused dot: memra wiki, board notes on the 35B MoE decode; memra
  * performance, flip history). For every token t:
  *   out[t] += sigmoid(Wsg x_t) * Wd (silu(Wg x_t) * (Wu x_t))
- * Wg, Wu [F][H] (one format), Wd [H][F], Wsg [1][H] (the gate row), any
- * of Q8_0 / Q4_0. x [dev] [T][H] of x_dt; out [dev] fp32 [T][H], read and
- * written (pass the routed output of q8_moe_ffn, or zeros); T >= 1.
+ * Wg, Wu [F][H] and Wsg [1][H] (the gate row) share one format, Wd [H][F]
+ * any: Q8_0 or Q4_0 (Q8_ERR_DTYPE if Wg, Wu and Wsg differ). x [dev]
+ * [T][H] of x_dt; out [dev] fp32 [T][H], read and written (pass the routed
+ * output of q8_moe_ffn, or zeros); T >= 1.
  * h = silu(g) * u is kept in fp32 and fed to Wd as fp32 activations; the
- * gate is 1 / (1 + expf(-g)) in fp32. Each output is within the bound the
+ * gate dot Wsg x_t is a GEMV row like any other (the same per-row
+ * arithmetic), its sigmoid 1 / (1 + expf(-g)) in fp32, and each output is
+ * out = fma(sigmoid, (Wd h)[m], out). Each output is within the bound the
  * oracle propagates from the GEMV bounds (sigma' <= 1/4).
  *   ws [dev] at least q8_moe_shared_ws_bytes(F, H, T) bytes, 16-byte
- *   aligned, caller-owned scratch (h and the expert's output; no zero-fill
- *   needed). Launches: the SiLU pair per pass of up to 8 tokens, the down
- *   GEMV per pass, then one launch that computes each token's gate dot and
- *   adds the gated output. */
+ *   aligned, caller-owned scratch (h and the gate dots; no zero-fill
+ *   needed). Launches per pass of up to 8 tokens: the SiLU pair with the
+ *   gate row as one more row (the fused gate dot), then the down GEMV whose
+ *   epilogue applies the gate and adds into out. */
 size_t q8_moe_shared_ws_bytes(int64_t F, int64_t H, int T);
 int q8_moe_shared_expert(const q8_matrix *Wg, const q8_matrix *Wu, const q8_matrix *Wd,
                          const q8_matrix *Wsg, const void *x, int x_dt, int T, float *out,

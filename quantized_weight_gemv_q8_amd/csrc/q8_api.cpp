@@ -532,10 +532,11 @@ int q8_moe_ffn_noalloc(const q8_bank* gate, const q8_bank* up, const q8_bank* do
 // Workspace: h [T][F] and the expert's output [T][H], fp32, each area
 // 256-byte aligned.
 static void shared_ws_layout(int64_t F, int64_t H, int T, size_t off[2], size_t* total) {
+  (void)H;
   auto up = [](size_t b) { return (b + 255) / 256 * 256; };
-  off[0] = 0;
-  off[1] = up((size_t)T * F * 4);
-  *total = off[1] + up((size_t)T * H * 4);
+  off[0] = 0;                            // h [T][F] fp32
+  off[1] = up((size_t)T * F * 4);        // gate dots [T] fp32
+  *total = off[1] + up((size_t)T * 4);
 }
 
 size_t q8_moe_shared_ws_bytes(int64_t F, int64_t H, int T) {
@@ -554,7 +555,7 @@ int q8_moe_shared_expert(const q8_matrix* Wg, const q8_matrix* Wu, const q8_matr
   const int64_t F = Wg->M, H = Wg->K;
   if (Wu->M != F || Wu->K != H || Wd->M != H || Wd->K != F || Wsg->M != 1 || Wsg->K != H)
     return Q8_ERR_SHAPE;
-  if (Wu->format != Wg->format) return Q8_ERR_DTYPE;
+  if (Wu->format != Wg->format || Wsg->format != Wg->format) return Q8_ERR_DTYPE;
   if (!x || !out) return Q8_ERR_NULL;
   if (T < 1) return Q8_ERR_SHAPE;
   const size_t xs = dt_size(x_dt);
@@ -576,22 +577,26 @@ int q8_moe_shared_expert(const q8_matrix* Wg, const q8_matrix* Wu, const q8_matr
   size_t off[2], total;
   shared_ws_layout(F, H, T, off, &total);
   float* h = (float*)((char*)ws + off[0]);
-  float* sx = (float*)((char*)ws + off[1]);
+  float* gd = (float*)((char*)ws + off[1]);
   const HMat G = to_h(Wg), U = to_h(Wu), D = to_h(Wd), SG = to_h(Wsg);
   hipStream_t s = (hipStream_t)stream;
+  // Two kinds of launch per pass: the gate/up pair with the gate row as an
+  // extra row (h and the gate dots), then the down projection whose
+  // epilogue adds sigmoid(gate dot) * (Wd h) into out.
   for (int n0 = 0; n0 < T; n0 += pass_h) {
     const int nt = T - n0 < pass_h ? T - n0 : pass_h;
     const char* xp = (const char*)x + (size_t)n0 * H * xs;
-    if (q8::launch_glu(*dev, G, U, xp, xf, h + (size_t)n0 * F, false, nt, s) != hipSuccess)
+    if (q8::launch_glu(*dev, G, U, xp, xf, h + (size_t)n0 * F, false, nt, s, &SG, gd + n0) !=
+        hipSuccess)
       return Q8_ERR_LAUNCH;
   }
   for (int n0 = 0; n0 < T; n0 += pass_f) {
     const int nt = T - n0 < pass_f ? T - n0 : pass_f;
-    if (q8::launch_gemv(*dev, D, nullptr, h + (size_t)n0 * F, true, F, sx + (size_t)n0 * H,
-                        nullptr, false, nt, s) != hipSuccess)
+    if (q8::launch_gemv(*dev, D, nullptr, h + (size_t)n0 * F, true, F, out + (size_t)n0 * H,
+                        nullptr, false, nt, s, gd + n0) != hipSuccess)
       return Q8_ERR_LAUNCH;
   }
-  return launch_rc(q8::launch_shared_gate_add(SG, x, xf, sx, out, T, H, s));
+  return Q8_OK;
 }
 
 // ------------------------------------------------------------ router

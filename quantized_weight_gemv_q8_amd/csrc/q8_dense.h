@@ -36,6 +36,10 @@ struct DenseEpi {
   int64_t Ma, Mtot;
   bool f16;
   int nt = kMaxNTWide;  // live tokens: only a kernel whose token count is a runtime value sets it
+  // Gated accumulate (the shared expert's last step): with gate set, y is
+  // fp32 and read-modify-written, y[n][m] += sigmoid(gate[n]) * v, with
+  // sigmoid(z) = 1 / (1 + expf(-z)); gate[n] is the raw gate dot of token n.
+  const float* gate = nullptr;
   template <int NT, int R, int CNT>
   __device__ __forceinline__ void emit(int64_t rbase, int base, bool owner, const float* v) {
     if (!owner) return;
@@ -50,8 +54,15 @@ struct DenseEpi {
       int64_t col, ld;
       if (row < Ma) { y = ya; col = row; ld = Ma; }
       else { y = yb; col = row - Ma; ld = Mtot - Ma; }
-      if (f16) reinterpret_cast<_Float16*>(y)[n * ld + col] = (_Float16)v[i];
-      else reinterpret_cast<float*>(y)[n * ld + col] = v[i];
+      if (gate) {
+        float* o = reinterpret_cast<float*>(y) + n * ld + col;
+        const float g = 1.0f / (1.0f + expf(-gate[n]));
+        *o = __builtin_fmaf(g, v[i], *o);
+      } else if (f16) {
+        reinterpret_cast<_Float16*>(y)[n * ld + col] = (_Float16)v[i];
+      } else {
+        reinterpret_cast<float*>(y)[n * ld + col] = v[i];
+      }
     }
   }
 };
@@ -67,7 +78,13 @@ struct GluMap {
   const int8_t* qu;
   const uint16_t* du;
   int64_t ldqg, lddg, ldqu, lddu;
-  int64_t M2;  // 2 * M virtual rows
+  int64_t M2;  // 2 * M virtual rows, 2 * M + 2 with an extra row
+  // Optional extra row (the shared expert's gate row, one row of the same
+  // K): virtual rows 2M and 2M + 1 both read it, so its dot with x lands in
+  // the lane that would hold an output's gate and up sums.
+  const int8_t* qx = nullptr;
+  const uint16_t* dx = nullptr;
+  int64_t M = 0;
   __device__ __forceinline__ bool row(int64_t i, const int8_t*& q, const uint16_t*& d) const {
     const int64_t rho = i >> 1;
     const bool up = (i & 1) != 0;
@@ -75,6 +92,10 @@ struct GluMap {
     const int64_t ldd = up ? lddu : lddg;
     q = (up ? qu : qg) + rho * ldq;
     d = (up ? du : dg) + rho * ldd;
+    if (qx != nullptr && rho == M) {
+      q = qx;
+      d = dx;
+    }
     return i < M2;
   }
 };
@@ -84,13 +105,18 @@ struct GluEpi {
   int64_t M;
   bool f16;
   int nt = kMaxNTWide;  // live tokens, as for DenseEpi
+  float* xdot = nullptr;  // with an extra row: its dot with token n goes to xdot[n]
   template <int NT, int R, int CNT>
   __device__ __forceinline__ void emit(int64_t rbase, int base, bool owner, const float* v) {
     static_assert(R % 2 == 0 && CNT == 2, "gate/up pairs");
     if (!owner || base >= NT * R) return;
     const int n = base / R, r = base - (base / R) * R;
     const int64_t row = rbase + r;  // the gate row of the pair (even)
-    if (row >= 2 * M || n >= nt) return;
+    if (n >= nt) return;
+    if (row >= 2 * M) {
+      if (xdot != nullptr && row == 2 * M) xdot[n] = v[0];
+      return;
+    }
     const float g = v[0], u = v[1];
     const float val = g / (1.0f + expf(-g)) * u;
     const int64_t o = (int64_t)n * M + (row >> 1);

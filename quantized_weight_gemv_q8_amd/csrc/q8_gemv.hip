@@ -215,7 +215,8 @@ static hipError_t glu_launch_nt(const DevInfo& dev, int nt, GluMap map, GluEpi e
 }
 
 hipError_t launch_glu(const DevInfo& dev, const HMat& Gm, const HMat& Um, const void* x,
-                      bool x_f32, void* h, bool h_f16, int nt, hipStream_t s) {
+                      bool x_f32, void* h, bool h_f16, int nt, hipStream_t s, const HMat* extra,
+                      float* xdot) {
   GluMap map;
   map.qg = Gm.qs;
   map.dg = Gm.d;
@@ -226,10 +227,17 @@ hipError_t launch_glu(const DevInfo& dev, const HMat& Gm, const HMat& Um, const 
   map.ldqu = Um.ld_qs;
   map.lddu = Um.ld_d;
   map.M2 = 2 * Gm.M;
+  if (extra) {
+    map.qx = extra->qs;
+    map.dx = extra->d;
+    map.M = Gm.M;
+    map.M2 += 2;
+  }
   GluEpi epi;
   epi.h = (char*)h;
   epi.M = Gm.M;
   epi.f16 = h_f16;
+  epi.xdot = extra ? xdot : nullptr;
   const int C = (int)chunks_per_row(Gm.fmt, Gm.K);
   const int64_t ldx_bytes = Gm.K * (x_f32 ? 4 : 2);
   const char* xp = (const char*)x;
@@ -411,7 +419,7 @@ bool wide_pass_applies(const DevInfo& dev, int fmt, int64_t K, bool x_f32, int64
 
 hipError_t launch_gemv(const DevInfo& dev, const HMat& A, const HMat* B, const void* x,
                        bool x_f32, int64_t ldx, void* ya, void* yb, bool y_f16, int nt,
-                       hipStream_t s) {
+                       hipStream_t s, const float* gate) {
   DenseMap map;
   map.qa = A.qs;
   map.da = A.d;
@@ -429,6 +437,7 @@ hipError_t launch_gemv(const DevInfo& dev, const HMat& A, const HMat* B, const v
   epi.Ma = map.Ma;
   epi.Mtot = map.Mtot;
   epi.f16 = y_f16;
+  epi.gate = gate;
   const int C = (int)chunks_per_row(A.fmt, A.K);
   const int64_t ldx_bytes = ldx * (x_f32 ? 4 : 2);
   const char* xp = (const char*)x;

@@ -85,9 +85,10 @@ int max_tokens_per_pass_wide(const DevInfo& dev, int64_t K, bool x_f32);
 bool wide_pass_applies(const DevInfo& dev, int fmt, int64_t K, bool x_f32, int64_t rows);
 
 // y[n] = A x[n] (and yb[n] = B x[n] when B != nullptr) for nt <= 16 tokens.
+// With gate set (fp32 y, no B): y[n] += sigmoid(gate[n]) * (A x[n]).
 hipError_t launch_gemv(const DevInfo& dev, const HMat& A, const HMat* B, const void* x,
                        bool x_f32, int64_t ldx, void* ya, void* yb, bool y_f16, int nt,
-                       hipStream_t s);
+                       hipStream_t s, const float* gate = nullptr);
 
 // LM head pass: logits (may be null) and ids [nt]. The workspace holds the
 // argmax slots and counters; it must be zero before the first pass and is
@@ -149,8 +150,11 @@ hipError_t launch_moe_gate_up(const DevInfo& dev, const HBank& G, const HBank& U
                               const MoeWs& ws, int topk, const void* x, bool x_f32, float* h,
                               const RouteReq& rq, hipStream_t s);
 // h[n][m] = silu(G x_n)[m] * (U x_n)[m]; G, U of one shape; h fp32 or fp16.
+// With extra (one row of the same K and format): xdot[n] = extra . x_n too,
+// in the same launch.
 hipError_t launch_glu(const DevInfo& dev, const HMat& G, const HMat& U, const void* x,
-                      bool x_f32, void* h, bool h_f16, int nt, hipStream_t s);
+                      bool x_f32, void* h, bool h_f16, int nt, hipStream_t s,
+                      const HMat* extra = nullptr, float* xdot = nullptr);
 // Router: ids [T][topk] and softmax weights [T][topk] from logits [T][E].
 constexpr int kRouterMaxE = 4096;  // 64 experts per lane of the token's wave
 constexpr int kRouterMaxK = 64;    // one picked logit per lane
@@ -164,10 +168,6 @@ constexpr int kRouterFusedMinT = 9;
 constexpr int kRouterFusedMaxT = 64;
 hipError_t launch_router(const DevInfo& dev, const HMat& Wr, const void* x, bool x_f32, int T,
                          int topk, float* logits, int32_t* ids, float* gate_w, hipStream_t s);
-// Shared expert's last step: out[t][m] += sigmoid(Wsg x_t) * sx[t][m], the
-// gate row's dot computed in the same launch (Wsg one row of H).
-hipError_t launch_shared_gate_add(const HMat& Wsg, const void* x, bool x_f32, const float* sx,
-                                  float* out, int T, int64_t H, hipStream_t s);
 // out[t] = sum_j gate_w[t][j] * y_pair[t*topk + j] (slots with invalid ids skipped).
 hipError_t launch_moe_combine(const int32_t* ids, int E, const float* gate_w,
                               const float* y_pair, float* out, int T, int topk, int64_t M,

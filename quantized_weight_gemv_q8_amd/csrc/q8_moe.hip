@@ -25,8 +25,6 @@
 //  rows     the same over a bank: y_pair[p] = W[e] x_p (the down
 //           projection, or a single routed GEMV).
 //  combine  out[t] = sum_j gate_w[t][j] * y_pair[t*topk + j], ascending j.
-//  shared   the shared expert's last step: each token's gate dot w_sg . x_t,
-//           its sigmoid, and out[t] += sigmoid * (the dense expert's output).
 // Per-(row, token) arithmetic is the engine's, which does not depend on
 // how many tokens an expert received or which slot they landed in, so a
 // token's result is independent of the rest of the batch.
@@ -608,74 +606,6 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(const int32_t* ids, in
   for (int i = 0; i < nv; ++i) out[(int64_t)t * M + m0 + i] = acc[i];
 }
 
-// Shared expert, last step: out[t][m] += sigmoid(g_t) * s[t][m], where
-// g_t = w_sg . x_t is computed here, by every workgroup of token t (the
-// gate row is one short row; recomputing it costs less than a launch).
-// Thread i takes the 16-element chunks i, i + 256, ... of the row (fp32
-// chunk sum, times the block's scale, accumulated), then a wave butterfly
-// and the four waves' sums in LDS; the sigmoid is 1 / (1 + expf(-g)).
-// Four outputs per thread.
-template <int F, bool XF32>
-__global__ __launch_bounds__(256) void shared_gate_add_kernel(const int8_t* gq, const uint16_t* gd,
-                                                             const char* x, const float* sx,
-                                                             float* out, int64_t H) {
-  __shared__ float part[256 / kWave];
-  const int64_t t = blockIdx.y;
-  float acc = 0.0f;
-  for (int64_t c = threadIdx.x; c < H / 16; c += 256) {
-    const int64_t k0 = c * 16;
-    float q[16];
-    if constexpr (F == kFmtQ8) {
-      const int8_t* src = gq + k0;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) q[e] = (float)src[e];
-    } else {
-      const uint8_t* src = reinterpret_cast<const uint8_t*>(gq) + (k0 / 32) * 16;
-      const int sh = (int)((k0 / 16) & 1) * 4;  // low nibbles: elements 0-15 of the block
-#pragma unroll
-      for (int e = 0; e < 16; ++e) q[e] = (float)((int)((src[e] >> sh) & 0xF) - 8);
-    }
-    float s = 0.0f;
-    if constexpr (XF32) {
-      const float* xv = reinterpret_cast<const float*>(x) + t * H + k0;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) s = __builtin_fmaf(q[e], xv[e], s);
-    } else {
-      const _Float16* xv = reinterpret_cast<const _Float16*>(x) + t * H + k0;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) s = __builtin_fmaf(q[e], (float)xv[e], s);
-    }
-    acc = __builtin_fmaf(half_bits_to_float(gd[k0 / 32]), s, acc);
-  }
-  acc = pair_sum<32>(acc);
-  acc = pair_sum<16>(acc);
-  acc = pair_sum<8>(acc);
-  acc = pair_sum<4>(acc);
-  acc = pair_sum<2>(acc);
-  acc = pair_sum<1>(acc);
-  if ((threadIdx.x & (kWave - 1)) == 0) part[threadIdx.x / kWave] = acc;
-  __syncthreads();
-  float gsum = 0.0f;
-#pragma unroll
-  for (int w = 0; w < 256 / kWave; ++w) gsum += part[w];
-  const float g = 1.0f / (1.0f + expf(-gsum));
-
-  const int64_t m0 = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
-  if (m0 >= H) return;
-  const float* src = sx + t * H + m0;
-  float* dst = out + t * H + m0;
-  const int n = H - m0 < 4 ? (int)(H - m0) : 4;
-  float v[4], o[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    v[i] = i < n ? src[i] : 0.0f;
-    o[i] = i < n ? dst[i] : 0.0f;
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    if (i < n) dst[i] = __builtin_fmaf(g, v[i], o[i]);
-}
-
 // ---------------------------------------------------------------- host side
 static int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
 
@@ -810,20 +740,6 @@ hipError_t launch_moe_gate_up(const DevInfo& dev, const HBank& G, const HBank& U
           dev, G, U, ws, topk, xp, ldx_bytes, h, rq, s);
     }
   });
-}
-
-hipError_t launch_shared_gate_add(const HMat& Wsg, const void* x, bool x_f32, const float* sx,
-                                  float* out, int T, int64_t H, hipStream_t s) {
-  const int8_t* gq = Wsg.qs;
-  const uint16_t* gd = Wsg.d;
-  void* args[] = {(void*)&gq, (void*)&gd, (void*)&x, (void*)&sx, &out, &H};
-  const unsigned gx = (unsigned)(((H + 3) / 4 + 255) / 256);
-  const void* fn = Wsg.fmt == kFmtQ4
-                       ? (x_f32 ? (const void*)shared_gate_add_kernel<kFmtQ4, true>
-                                : (const void*)shared_gate_add_kernel<kFmtQ4, false>)
-                       : (x_f32 ? (const void*)shared_gate_add_kernel<kFmtQ8, true>
-                                : (const void*)shared_gate_add_kernel<kFmtQ8, false>);
-  return hipLaunchKernel(fn, dim3(gx, (unsigned)T), dim3(256), args, 0, s);
 }
 
 hipError_t launch_moe_combine(const int32_t* ids, int E, const float* gate_w,

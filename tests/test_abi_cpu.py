@@ -263,13 +263,13 @@ def test_valid_call_without_gfx950_is_refused(L):
 def test_shared_expert_validation(L):
     """q8_moe_shared_expert refuses bad arguments before touching the
     device: shapes that do not chain (Wg/Wu [F][H], Wd [H][F], Wsg [1][H]),
-    mixed gate/up formats, null pointers, a short or misaligned workspace
-    and overlapping buffers."""
+    mixed gate/up/gate-row formats, null pointers, a short or misaligned
+    workspace and overlapping buffers."""
     F, H, T = 64, 256, 3
     g, u = _mat(M=F, K=H), _mat(M=F, K=H)
     dn, sg = _mat(M=H, K=F), _mat(M=1, K=H)
     n = L.q8_moe_shared_ws_bytes(F, H, T)
-    assert n >= 4 * (T * F + T * H)  # h and the expert output, fp32
+    assert n >= 4 * (T * F + T)  # h and the gate dots, fp32
     assert L.q8_moe_shared_ws_bytes(0, H, T) == 0
     ok = dict(g=g, u=u, d=dn, s=sg, x=X, xdt=1, T=T, out=Y, ws=WS, nws=n)
 
@@ -288,6 +288,9 @@ def test_shared_expert_validation(L):
     q4u = _mat(M=F, K=H)
     q4u.format = q8.Q8_FMT_Q4_0
     assert rc(u=q4u) == -4                 # gate and up in one format
+    q4s = _mat(M=1, K=H)
+    q4s.format = q8.Q8_FMT_Q4_0
+    assert rc(s=q4s) == -4                 # the gate row is the pair's extra row
     assert rc(ws=0) == -5
     assert rc(nws=n - 1) == -5
     assert rc(ws=WS + 8) == -5
