@@ -194,21 +194,34 @@ __device__ __forceinline__ float dot32_f16(const h2_t q[16], const uint4 xs[4]) 
   return s;
 }
 
-// fp32 activations: nibble - 8 as fp32 (exact), then an FMA chain in K
-// order. One half of a Q4_0 block: elements 16*half .. 16*half + 15 (the
-// low nibbles for half 0, the high ones for half 1) against x[0..3], the
-// chain continuing from s.
-__device__ __forceinline__ float dot16_f32_q4(const uint4 q, const uint4 x[4], int half, float s) {
+// fp32 activations: one half of a Q4_0 block (elements 16*half ..
+// 16*half + 15: the low nibbles for half 0, the high ones for half 1) as
+// exact fp16 values (nibble + 1024 under the 0x64 exponent byte, minus 1032),
+// converted once per chunk and row for all tokens.
+__device__ __forceinline__ void half_nibbles_to_h2(const uint4 q, int half, h2_t out[8]) {
   const unsigned w[4] = {q.x, q.y, q.z, q.w};
+  const h2_t bias = {(_Float16)1032.0f, (_Float16)1032.0f};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const unsigned nib = (w[i] >> (4 * half)) & 0x0F0F0F0Fu;
+    out[2 * i] = __builtin_bit_cast(h2_t, __builtin_amdgcn_perm(0x64646464u, nib, 0x04010400u)) - bias;
+    out[2 * i + 1] =
+        __builtin_bit_cast(h2_t, __builtin_amdgcn_perm(0x64646464u, nib, 0x04030402u)) - bias;
+  }
+}
+
+// sum over the 16 elements of that half of q_i * x_i, an fp32 FMA chain in K
+// order continuing from s (each fp16 value widens exactly; the FMA is the
+// one a converted nibble would take, so the result is bit for bit the same
+// as converting each nibble on the spot).
+__device__ __forceinline__ float dot16_f32_h(const h2_t w[8], const uint4 x[4], float s) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const float4 xv = __builtin_bit_cast(float4, x[i]);
-    const float xe[4] = {xv.x, xv.y, xv.z, xv.w};
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const int nib = (int)((w[i] >> (8 * b + 4 * half)) & 0xFu) - 8;
-      s = __builtin_fmaf((float)nib, xe[b], s);
-    }
+    s = __builtin_fmaf((float)w[2 * i][0], xv.x, s);
+    s = __builtin_fmaf((float)w[2 * i][1], xv.y, s);
+    s = __builtin_fmaf((float)w[2 * i + 1][0], xv.z, s);
+    s = __builtin_fmaf((float)w[2 * i + 1][1], xv.w, s);
   }
   return s;
 }
@@ -273,7 +286,8 @@ __device__ __forceinline__ void chunk_fma(const uint4* q, const uint32_t* d, con
   } else {
     // Half a block (16 activations) of a token at a time, each (row, token)
     // chain carried across the halves: the same FMA order as one pass over
-    // the block, with a quarter of the activation registers live.
+    // the block, with a quarter of the activation registers live; the half's
+    // nibbles are converted once for all tokens.
     float sum[NT][R];
 #pragma unroll
     for (int n = 0; n < NT; ++n)
@@ -281,6 +295,9 @@ __device__ __forceinline__ void chunk_fma(const uint4* q, const uint32_t* d, con
       for (int r = 0; r < R; ++r) sum[n][r] = 0.0f;
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
+      h2_t qh[R][8];
+#pragma unroll
+      for (int r = 0; r < R; ++r) half_nibbles_to_h2(q[r], half, qh[r]);
 #pragma unroll
       for (int n = 0; n < NT; ++n) {
         if (n >= nt) continue;  // not break: a fixed trip count keeps acc[] in registers
@@ -288,7 +305,7 @@ __device__ __forceinline__ void chunk_fma(const uint4* q, const uint32_t* d, con
 #pragma unroll
         for (int i = 0; i < 4; ++i) xv[i] = xb[(n * P + 4 * half + i) * C + c];
 #pragma unroll
-        for (int r = 0; r < R; ++r) sum[n][r] = dot16_f32_q4(q[r], xv, half, sum[n][r]);
+        for (int r = 0; r < R; ++r) sum[n][r] = dot16_f32_h(qh[r], xv, sum[n][r]);
       }
     }
 #pragma unroll
