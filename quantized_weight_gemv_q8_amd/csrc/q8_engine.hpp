@@ -45,6 +45,17 @@ constexpr int kWave = 64;
 constexpr int kBlock = 512;  // threads per workgroup for every row kernel
 constexpr int kWavesPerBlock = kBlock / kWave;
 constexpr int kOnceMaxBlock = 1024;  // largest workgroup of the one-group-per-wave kernels
+
+// Threads per workgroup of the persistent row kernels. Passes of 4 to 8
+// tokens use 12-wave workgroups: the 2 x 17408 x 5120 pair at N = 4 runs
+// two per CU (24 waves) in 35.0 us against 38.5 us for three 8-wave ones
+// (also 24 waves), and at N = 8 (LDS for one workgroup per CU) 53.2 us
+// against 54.9 for two 8-wave ones; 6-, 10- and 16-wave workgroups were
+// 10-20% slower (measured on MI355X, same-process A/B). Q4_0 17408 x 5120
+// at N = 4: 6% faster.
+template <int NT>
+constexpr int narrow_block() { return NT >= 4 ? 12 * kWave : kBlock; }
+
 constexpr int kMaxNT = 8;    // tokens per pass
 
 __device__ __forceinline__ float half_bits_to_float(uint16_t b) {
@@ -69,10 +80,28 @@ __device__ __forceinline__ void quants_to_h2(const uint4 q, h2_t out[8]) {
   }
 }
 
+// The first pair of a dot-product chain, a*b summed onto a zero. With ZA
+// it is v_dot2_f32_f16 taking the zero as an inline constant; the builtin
+// given a zero accumulator becomes a move of 0 plus the two-address v_dot2c
+// form, one more VALU op per chain for the same operation (measured on
+// MI355X: 3% off the 2 x 17408 x 5120 pair at 4-16 tokens, where the
+// dot products bound the kernel; at 1-2 tokens the asm block's scheduling
+// barrier costs more than the op, so those kernels keep the builtin).
+template <bool ZA>
+__device__ __forceinline__ float dot2_from_zero(h2_t a, h2_t b) {
+  if constexpr (ZA) {
+    float s;
+    asm("v_dot2_f32_f16 %0, %1, %2, 0" : "=v"(s) : "v"(a), "v"(b));
+    return s;
+  } else {
+    return __builtin_amdgcn_fdot2(a, b, 0.0f, false);
+  }
+}
+
 // sum_{i<16} q_i * x_i in fp32, sequential over the 8 pairs in K order.
+template <bool ZA>
 __device__ __forceinline__ float dot16_f16(const h2_t q[8], const uint4 xlo, const uint4 xhi) {
-  float s = 0.0f;
-  s = __builtin_amdgcn_fdot2(q[0], __builtin_bit_cast(h2_t, xlo.x), s, false);
+  float s = dot2_from_zero<ZA>(q[0], __builtin_bit_cast(h2_t, xlo.x));
   s = __builtin_amdgcn_fdot2(q[1], __builtin_bit_cast(h2_t, xlo.y), s, false);
   s = __builtin_amdgcn_fdot2(q[2], __builtin_bit_cast(h2_t, xlo.z), s, false);
   s = __builtin_amdgcn_fdot2(q[3], __builtin_bit_cast(h2_t, xlo.w), s, false);
@@ -182,11 +211,13 @@ __device__ __forceinline__ void nibbles_to_h2(const uint4 q, h2_t out[16]) {
 
 // sum_{i<32} q_i * x_i in fp32, sequential over the 16 pairs in K order;
 // xs[0..3] hold elements 0-7, 8-15, 16-23 and 24-31.
+template <bool ZA>
 __device__ __forceinline__ float dot32_f16(const h2_t q[16], const uint4 xs[4]) {
   float s = 0.0f;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    s = __builtin_amdgcn_fdot2(q[4 * i + 0], __builtin_bit_cast(h2_t, xs[i].x), s, false);
+    s = i == 0 ? dot2_from_zero<ZA>(q[0], __builtin_bit_cast(h2_t, xs[0].x))
+               : __builtin_amdgcn_fdot2(q[4 * i + 0], __builtin_bit_cast(h2_t, xs[i].x), s, false);
     s = __builtin_amdgcn_fdot2(q[4 * i + 1], __builtin_bit_cast(h2_t, xs[i].y), s, false);
     s = __builtin_amdgcn_fdot2(q[4 * i + 2], __builtin_bit_cast(h2_t, xs[i].z), s, false);
     s = __builtin_amdgcn_fdot2(q[4 * i + 3], __builtin_bit_cast(h2_t, xs[i].w), s, false);
@@ -246,7 +277,7 @@ __device__ __forceinline__ void chunk_fma(const uint4* q, const uint32_t* d, con
       const uint4 xhi = xb[(n * P + 1) * C + c];
 #pragma unroll
       for (int r = 0; r < R; ++r) {
-        const float sum = dot16_f16(qh[r], xlo, xhi);
+        const float sum = dot16_f16<(NT >= 4)>(qh[r], xlo, xhi);
         acc[n * R + r] = __builtin_fmaf(df[r], sum, acc[n * R + r]);
       }
     }
@@ -279,7 +310,7 @@ __device__ __forceinline__ void chunk_fma(const uint4* q, const uint32_t* d, con
       for (int h = 0; h < 4; ++h) xs[h] = xb[(n * P + h) * C + c];
 #pragma unroll
       for (int r = 0; r < R; ++r) {
-        const float sum = dot32_f16(qh[r], xs);
+        const float sum = dot32_f16<(NT >= 4)>(qh[r], xs);
         acc[n * R + r] = __builtin_fmaf(df[r], sum, acc[n * R + r]);
       }
     }

@@ -47,7 +47,7 @@ hipError_t launch_glu_once(int nt, const DevInfo& dev, const GluMap& map, const 
 }
 
 template <int F, int NT, int LPR, bool XF32, int MODE>
-__global__ __launch_bounds__(kBlock) void gemv_kernel(DenseMap map, DenseEpi epi, const char* x,
+__global__ __launch_bounds__(narrow_block<NT>()) void gemv_kernel(DenseMap map, DenseEpi epi, const char* x,
                                                       int64_t ldx_bytes, int C) {
   extern __shared__ uint4 lds_x[];
   using T = TuneM<NT, MODE>;
@@ -61,9 +61,10 @@ __global__ __launch_bounds__(kBlock) void gemv_kernel(DenseMap map, DenseEpi epi
     stage_fmt<F, NT, XF32>(rows, C, lds_x);
     __syncthreads();
   };
+  constexpr int WPB = narrow_block<NT>() / kWave;
   run_rows<NT, LPR, T::R, T::D, 1, XF32, F>(map, epi, lds_x, C, n_groups,
-                                            (int64_t)blockIdx.x * kWavesPerBlock + wave,
-                                            (int64_t)gridDim.x * kWavesPerBlock, 0, stage);
+                                            (int64_t)blockIdx.x * WPB + wave,
+                                            (int64_t)gridDim.x * WPB, 0, stage);
 }
 
 // ---------------------------------------------------------------- 9..16 tokens
@@ -160,7 +161,7 @@ struct GluTune {
 };
 
 template <int F, int NT, int LPR, bool XF32, bool BIG>
-__global__ __launch_bounds__(kBlock) void glu_kernel(GluMap map, GluEpi epi, const char* x,
+__global__ __launch_bounds__(narrow_block<NT>()) void glu_kernel(GluMap map, GluEpi epi, const char* x,
                                                      int64_t ldx_bytes, int C) {
   extern __shared__ uint4 lds_x[];
   constexpr int R = GluTune<NT, BIG>::R;
@@ -175,8 +176,8 @@ __global__ __launch_bounds__(kBlock) void glu_kernel(GluMap map, GluEpi epi, con
     __syncthreads();
   };
   run_rows<NT, LPR, R, 1, 2, XF32, F>(map, epi, lds_x, C, n_groups,
-                                      (int64_t)blockIdx.x * kWavesPerBlock + wave,
-                                      (int64_t)gridDim.x * kWavesPerBlock, 0, stage);
+                                      (int64_t)blockIdx.x * (narrow_block<NT>() / kWave) + wave,
+                                      (int64_t)gridDim.x * (narrow_block<NT>() / kWave), 0, stage);
 }
 
 template <int F, int NT, int LPR, bool XF32, bool BIG>
@@ -185,14 +186,15 @@ static hipError_t glu_launch_t(const DevInfo& dev, GluMap map, GluEpi epi, const
   constexpr int G = (kWave / LPR) * GluTune<NT, BIG>::R;
   const size_t lds = (size_t)NT * C * 16 * ChunkPlanes<F, XF32>::P;
   const int64_t n_groups = (map.M2 + G - 1) / G;
-  const int64_t need = (n_groups + kWavesPerBlock - 1) / kWavesPerBlock;
+  constexpr int NB = narrow_block<NT>();
+  const int64_t need = (n_groups + NB / kWave - 1) / (NB / kWave);
   auto fn = glu_kernel<F, NT, LPR, XF32, BIG>;
   if (hipError_t e = allow_dynamic_lds((const void*)fn, lds)) return e;
-  int64_t blocks = (int64_t)dev.cus * blocks_per_cu((const void*)fn, lds, kBlock);
+  int64_t blocks = (int64_t)dev.cus * blocks_per_cu((const void*)fn, lds, NB);
   if (blocks > need) blocks = need;
   if (blocks < 1) blocks = 1;
   void* args[] = {&map, &epi, (void*)&x, &ldx_bytes, &C};
-  return hipLaunchKernel((const void*)fn, dim3((unsigned)blocks), dim3(kBlock), args, lds, s);
+  return hipLaunchKernel((const void*)fn, dim3((unsigned)blocks), dim3(NB), args, lds, s);
 }
 
 template <int F, int LPR, bool XF32>
@@ -264,14 +266,15 @@ static hipError_t launch_t(const DevInfo& dev, DenseMap map, DenseEpi epi, const
   constexpr int G = (kWave / LPR) * TuneM<NT, MODE>::R;
   const size_t lds = (size_t)NT * C * 16 * ChunkPlanes<F, XF32>::P;
   const int64_t n_groups = (map.Mtot + G - 1) / G;
-  const int64_t need = (n_groups + kWavesPerBlock - 1) / kWavesPerBlock;
+  constexpr int NB = narrow_block<NT>();
+  const int64_t need = (n_groups + NB / kWave - 1) / (NB / kWave);
   auto fn = gemv_kernel<F, NT, LPR, XF32, MODE>;
   if (hipError_t e = allow_dynamic_lds((const void*)fn, lds)) return e;
-  int64_t blocks = (int64_t)dev.cus * blocks_per_cu((const void*)fn, lds, kBlock);
+  int64_t blocks = (int64_t)dev.cus * blocks_per_cu((const void*)fn, lds, NB);
   if (blocks > need) blocks = need;
   if (blocks < 1) blocks = 1;
   void* args[] = {&map, &epi, (void*)&x, &ldx_bytes, &C};
-  return hipLaunchKernel((const void*)fn, dim3((unsigned)blocks), dim3(kBlock), args, lds, s);
+  return hipLaunchKernel((const void*)fn, dim3((unsigned)blocks), dim3(NB), args, lds, s);
 }
 
 template <int F, int NT, int LPR, bool XF32>
