@@ -153,7 +153,9 @@ int q8_unpack_host(const int8_t *qs, int64_t ld_qs, const uint16_t *d, int64_t l
  *   64 lanes (K a multiple of 1024, e.g. 5120) and at least 12 row groups
  *   of 4 rows per CU (rows >= 12288 on a 256-CU MI355X; the 9..16-token
  *   verify of the pages' K+1 speculative step, memra wiki feature list),
- *   passes of up to 8 tokens otherwise;
+ *   passes of up to 8 tokens otherwise, all full passes of 4 or more
+ *   tokens in one launch where the one-group kernel applies (the pass is
+ *   the workgroup's y index; later passes find most weights in the L2);
  *   fewer if the x image of a pass would not fit the LDS. Per-token
  *   results are bitwise identical to N = 1 whatever the pass size. */
 int q8_gemv(const q8_matrix *W, const void *x, int x_dt, void *y, int y_dt, int N,
@@ -375,9 +377,10 @@ int q8_moe_router(const q8_matrix *Wr, const void *x, int x_dt, int T, int topk,
  * oracle propagates from the GEMV bounds (sigma' <= 1/4).
  *   ws [dev] at least q8_moe_shared_ws_bytes(F, H, T) bytes, 16-byte
  *   aligned, caller-owned scratch (h and the gate dots; no zero-fill
- *   needed). Launches per pass of up to 8 tokens: the SiLU pair with the
- *   gate row as one more row (the fused gate dot), then the down GEMV whose
- *   epilogue applies the gate and adds into out. */
+ *   needed). Two launches for all full passes of up to 8 tokens (one more
+ *   of each for a ragged last pass): the SiLU pair with the gate row as
+ *   one more row (the fused gate dot), then the down GEMV whose epilogue
+ *   applies the gate and adds into out. */
 size_t q8_moe_shared_ws_bytes(int64_t F, int64_t H, int T);
 int q8_moe_shared_expert(const q8_matrix *Wg, const q8_matrix *Wu, const q8_matrix *Wd,
                          const q8_matrix *Wsg, const void *x, int x_dt, int T, float *out,

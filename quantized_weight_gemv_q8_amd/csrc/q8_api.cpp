@@ -229,6 +229,16 @@ int q8_unpack_q4_0_host(const uint8_t* qs, int64_t ld_qs, const uint16_t* d, int
 }
 
 // ------------------------------------------------------------ dense GEMV
+// The next launch of a call over N tokens in passes of per_pass, from token
+// n0: its pass size nt and the number of such passes it runs. Where the
+// 9..16-token kernel does not apply (multi), every remaining full pass
+// goes into one launch (the one-group kernels run them as slices of one
+// grid); otherwise one pass per launch.
+static void next_launch(int N, int n0, int per_pass, bool multi, int* nt, int* slices) {
+  *nt = N - n0 < per_pass ? N - n0 : per_pass;
+  *slices = multi && *nt == per_pass ? (N - n0) / per_pass : 1;
+}
+
 static int gemv_impl(const q8_matrix* Wa, const q8_matrix* Wb, const void* x, int x_dt, void* ya,
                      void* yb, int y_dt, int N, void* stream) {
   int rc = check_matrix(Wa);
@@ -256,20 +266,20 @@ static int gemv_impl(const q8_matrix* Wa, const q8_matrix* Wb, const void* x, in
   if (rc) return rc;
   const bool xf = x_dt == Q8_DT_F32;
   const int64_t rows = Wa->M + (Wb ? Wb->M : 0);
-  const int per_pass = q8::wide_pass_applies(*dev, Wa->format, Wa->K, xf, rows)
-                           ? q8::max_tokens_per_pass_wide(*dev, Wa->K, xf)
-                           : q8::max_tokens_per_pass(*dev, Wa->K, xf);
+  const bool wide = q8::wide_pass_applies(*dev, Wa->format, Wa->K, xf, rows);
+  const int per_pass = wide ? q8::max_tokens_per_pass_wide(*dev, Wa->K, xf)
+                            : q8::max_tokens_per_pass(*dev, Wa->K, xf);
   if (per_pass < 1) return Q8_ERR_SHAPE;
   const HMat A = to_h(Wa);
   HMat B;
   if (Wb) B = to_h(Wb);
-  for (int n0 = 0; n0 < N; n0 += per_pass) {
-    const int nt = N - n0 < per_pass ? N - n0 : per_pass;
+  for (int n0 = 0, nt, slices; n0 < N; n0 += nt * slices) {
+    next_launch(N, n0, per_pass, !wide, &nt, &slices);
     const char* xp = (const char*)x + (size_t)n0 * Wa->K * xs;
     char* yap = (char*)ya + (size_t)n0 * Wa->M * ys;
     char* ybp = Wb ? (char*)yb + (size_t)n0 * Wb->M * ys : nullptr;
     hipError_t e = q8::launch_gemv(*dev, A, Wb ? &B : nullptr, xp, xf, Wa->K, yap, ybp,
-                                   y_dt == Q8_DT_F16, nt, (hipStream_t)stream);
+                                   y_dt == Q8_DT_F16, nt, (hipStream_t)stream, nullptr, slices);
     if (e != hipSuccess) return Q8_ERR_LAUNCH;
   }
   return Q8_OK;
@@ -302,16 +312,16 @@ int q8_gemv_pair_silu(const q8_matrix* Wg, const q8_matrix* Wu, const void* x, i
   rc = current_device(&dev);
   if (rc) return rc;
   const bool xf = x_dt == Q8_DT_F32;
-  const int per_pass = q8::wide_pass_applies(*dev, Wg->format, Wg->K, xf, 2 * Wg->M)
-                           ? q8::max_tokens_per_pass_wide(*dev, Wg->K, xf)
-                           : q8::max_tokens_per_pass(*dev, Wg->K, xf);
+  const bool wide = q8::wide_pass_applies(*dev, Wg->format, Wg->K, xf, 2 * Wg->M);
+  const int per_pass = wide ? q8::max_tokens_per_pass_wide(*dev, Wg->K, xf)
+                            : q8::max_tokens_per_pass(*dev, Wg->K, xf);
   if (per_pass < 1) return Q8_ERR_SHAPE;
   const HMat G = to_h(Wg), U = to_h(Wu);
-  for (int n0 = 0; n0 < N; n0 += per_pass) {
-    const int nt = N - n0 < per_pass ? N - n0 : per_pass;
+  for (int n0 = 0, nt, slices; n0 < N; n0 += nt * slices) {
+    next_launch(N, n0, per_pass, !wide, &nt, &slices);
     hipError_t e = q8::launch_glu(*dev, G, U, (const char*)x + (size_t)n0 * Wg->K * xs, xf,
                                   (char*)h + (size_t)n0 * Wg->M * hs, h_dt == Q8_DT_F16, nt,
-                                  (hipStream_t)stream);
+                                  (hipStream_t)stream, nullptr, nullptr, slices);
     if (e != hipSuccess) return Q8_ERR_LAUNCH;
   }
   return Q8_OK;
@@ -583,17 +593,17 @@ int q8_moe_shared_expert(const q8_matrix* Wg, const q8_matrix* Wu, const q8_matr
   // Two kinds of launch per pass: the gate/up pair with the gate row as an
   // extra row (h and the gate dots), then the down projection whose
   // epilogue adds sigmoid(gate dot) * (Wd h) into out.
-  for (int n0 = 0; n0 < T; n0 += pass_h) {
-    const int nt = T - n0 < pass_h ? T - n0 : pass_h;
+  for (int n0 = 0, nt, slices; n0 < T; n0 += nt * slices) {
+    next_launch(T, n0, pass_h, true, &nt, &slices);
     const char* xp = (const char*)x + (size_t)n0 * H * xs;
-    if (q8::launch_glu(*dev, G, U, xp, xf, h + (size_t)n0 * F, false, nt, s, &SG, gd + n0) !=
-        hipSuccess)
+    if (q8::launch_glu(*dev, G, U, xp, xf, h + (size_t)n0 * F, false, nt, s, &SG, gd + n0,
+                       slices) != hipSuccess)
       return Q8_ERR_LAUNCH;
   }
-  for (int n0 = 0; n0 < T; n0 += pass_f) {
-    const int nt = T - n0 < pass_f ? T - n0 : pass_f;
+  for (int n0 = 0, nt, slices; n0 < T; n0 += nt * slices) {
+    next_launch(T, n0, pass_f, true, &nt, &slices);
     if (q8::launch_gemv(*dev, D, nullptr, h + (size_t)n0 * F, true, F, out + (size_t)n0 * H,
-                        nullptr, false, nt, s, gd + n0) != hipSuccess)
+                        nullptr, false, nt, s, gd + n0, slices) != hipSuccess)
       return Q8_ERR_LAUNCH;
   }
   return Q8_OK;

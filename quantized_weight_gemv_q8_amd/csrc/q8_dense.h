@@ -40,6 +40,14 @@ struct DenseEpi {
   // fp32 and read-modify-written, y[n][m] += sigmoid(gate[n]) * v, with
   // sigmoid(z) = 1 / (1 + expf(-z)); gate[n] is the raw gate dot of token n.
   const float* gate = nullptr;
+  // Token slice of a launch that runs several passes at once: token n of
+  // the slice starting at token n0 is token n0 + n of the call.
+  __device__ __forceinline__ void shift(int n0) {
+    const int64_t es = f16 && gate == nullptr ? 2 : 4;
+    ya += (int64_t)n0 * Ma * es;
+    if (yb != nullptr) yb += (int64_t)n0 * (Mtot - Ma) * es;
+    if (gate != nullptr) gate += n0;
+  }
   template <int NT, int R, int CNT>
   __device__ __forceinline__ void emit(int64_t rbase, int base, bool owner, const float* v) {
     if (!owner) return;
@@ -106,6 +114,10 @@ struct GluEpi {
   bool f16;
   int nt = kMaxNTWide;  // live tokens, as for DenseEpi
   float* xdot = nullptr;  // with an extra row: its dot with token n goes to xdot[n]
+  __device__ __forceinline__ void shift(int n0) {  // as DenseEpi::shift
+    h += (int64_t)n0 * M * (f16 ? 2 : 4);
+    if (xdot != nullptr) xdot += n0;
+  }
   template <int NT, int R, int CNT>
   __device__ __forceinline__ void emit(int64_t rbase, int base, bool owner, const float* v) {
     static_assert(R % 2 == 0 && CNT == 2, "gate/up pairs");
@@ -130,14 +142,18 @@ struct GluEpi {
 // apply (the chunks per lane are not an instantiated count, or, for more
 // than 2 tokens, the row groups do not fit in the resident waves); the
 // caller then takes the persistent launch.
+// With slices > 1 the launch runs that many passes of nt tokens at once
+// (blockIdx.y is the pass; pass k reads x + k * nt * ldx_bytes and writes
+// tokens k * nt ..): the weights are streamed from HBM by the first pass
+// and mostly found in the L2 by the others.
 hipError_t launch_gemv_once(int nt, const DevInfo& dev, const DenseMap& map, const DenseEpi& epi,
                             int fmt, int lpr, bool x_f32, const char* x, int64_t ldx_bytes, int C,
-                            hipStream_t s);
+                            hipStream_t s, int slices = 1);
 
 // The same for the gate/up + SiLU pair (2M virtual rows), nt = 1..8 (from
 // 3 tokens only when every group fits in the resident waves).
 hipError_t launch_glu_once(int nt, const DevInfo& dev, const GluMap& map, const GluEpi& epi,
                            int fmt, int lpr, bool x_f32, const char* x, int64_t ldx_bytes, int C,
-                           hipStream_t s);
+                           hipStream_t s, int slices = 1);
 
 }  // namespace q8

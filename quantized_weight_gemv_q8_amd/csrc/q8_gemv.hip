@@ -22,10 +22,11 @@ namespace q8 {
 // One-group-per-wave launches by token count (instantiated in q8_once.hip).
 hipError_t launch_gemv_once(int nt, const DevInfo& dev, const DenseMap& map, const DenseEpi& epi,
                             int fmt, int lpr, bool x_f32, const char* x, int64_t ldx_bytes, int C,
-                            hipStream_t s) {
+                            hipStream_t s, int slices) {
   switch (nt) {
 #define Q8_ONCE_CASE(N) \
-  case N: return launch_once_nt<DenseKind, N>(dev, map, epi, fmt, lpr, x_f32, x, ldx_bytes, C, s);
+  case N:                                                                                     \
+    return launch_once_nt<DenseKind, N>(dev, map, epi, fmt, lpr, x_f32, x, ldx_bytes, C, s, slices);
     Q8_ONCE_CASE(1) Q8_ONCE_CASE(2) Q8_ONCE_CASE(3) Q8_ONCE_CASE(4)
     Q8_ONCE_CASE(5) Q8_ONCE_CASE(6) Q8_ONCE_CASE(7) Q8_ONCE_CASE(8)
 #undef Q8_ONCE_CASE
@@ -35,10 +36,11 @@ hipError_t launch_gemv_once(int nt, const DevInfo& dev, const DenseMap& map, con
 
 hipError_t launch_glu_once(int nt, const DevInfo& dev, const GluMap& map, const GluEpi& epi,
                            int fmt, int lpr, bool x_f32, const char* x, int64_t ldx_bytes, int C,
-                           hipStream_t s) {
+                           hipStream_t s, int slices) {
   switch (nt) {
 #define Q8_ONCE_CASE(N) \
-  case N: return launch_once_nt<GluKind, N>(dev, map, epi, fmt, lpr, x_f32, x, ldx_bytes, C, s);
+  case N:                                                                                     \
+    return launch_once_nt<GluKind, N>(dev, map, epi, fmt, lpr, x_f32, x, ldx_bytes, C, s, slices);
     Q8_ONCE_CASE(1) Q8_ONCE_CASE(2) Q8_ONCE_CASE(3) Q8_ONCE_CASE(4)
     Q8_ONCE_CASE(5) Q8_ONCE_CASE(6) Q8_ONCE_CASE(7) Q8_ONCE_CASE(8)
 #undef Q8_ONCE_CASE
@@ -218,7 +220,7 @@ static hipError_t glu_launch_nt(const DevInfo& dev, int nt, GluMap map, GluEpi e
 
 hipError_t launch_glu(const DevInfo& dev, const HMat& Gm, const HMat& Um, const void* x,
                       bool x_f32, void* h, bool h_f16, int nt, hipStream_t s, const HMat* extra,
-                      float* xdot) {
+                      float* xdot, int slices) {
   GluMap map;
   map.qg = Gm.qs;
   map.dg = Gm.d;
@@ -243,6 +245,20 @@ hipError_t launch_glu(const DevInfo& dev, const HMat& Gm, const HMat& Um, const 
   const int C = (int)chunks_per_row(Gm.fmt, Gm.K);
   const int64_t ldx_bytes = Gm.K * (x_f32 ? 4 : 2);
   const char* xp = (const char*)x;
+  if (slices > 1) {
+    if (nt > kMaxNT) return hipErrorInvalidValue;
+    const hipError_t e = launch_glu_once(nt, dev, map, epi, Gm.fmt, lanes_for(Gm.fmt, Gm.K),
+                                         x_f32, xp, ldx_bytes, C, s, slices);
+    if (e != hipErrorNotSupported) return e;
+    for (int k = 0; k < slices; ++k) {
+      const int n0 = k * nt;
+      const hipError_t ek = launch_glu(dev, Gm, Um, xp + (int64_t)n0 * ldx_bytes, x_f32,
+                                       (char*)h + (int64_t)n0 * Gm.M * (h_f16 ? 2 : 4), h_f16, nt,
+                                       s, extra, xdot ? xdot + n0 : nullptr);
+      if (ek != hipSuccess) return ek;
+    }
+    return hipSuccess;
+  }
   if (nt > kMaxNT) {
     if (!wide_pass_applies(dev, Gm.fmt, Gm.K, x_f32, map.M2)) return hipErrorInvalidValue;
     return wide_launch<kFmtQ8, 64, false>(dev, (const void*)glu_wide_kernel<kFmtQ8, 64, false>,
@@ -422,7 +438,7 @@ bool wide_pass_applies(const DevInfo& dev, int fmt, int64_t K, bool x_f32, int64
 
 hipError_t launch_gemv(const DevInfo& dev, const HMat& A, const HMat* B, const void* x,
                        bool x_f32, int64_t ldx, void* ya, void* yb, bool y_f16, int nt,
-                       hipStream_t s, const float* gate) {
+                       hipStream_t s, const float* gate, int slices) {
   DenseMap map;
   map.qa = A.qs;
   map.da = A.d;
@@ -444,6 +460,21 @@ hipError_t launch_gemv(const DevInfo& dev, const HMat& A, const HMat* B, const v
   const int C = (int)chunks_per_row(A.fmt, A.K);
   const int64_t ldx_bytes = ldx * (x_f32 ? 4 : 2);
   const char* xp = (const char*)x;
+  if (slices > 1) {
+    if (nt > kMaxNT) return hipErrorInvalidValue;
+    const hipError_t e = launch_gemv_once(nt, dev, map, epi, A.fmt, lanes_for(A.fmt, A.K), x_f32,
+                                          xp, ldx_bytes, C, s, slices);
+    if (e != hipErrorNotSupported) return e;
+    const int64_t ys = y_f16 && gate == nullptr ? 2 : 4;
+    for (int k = 0; k < slices; ++k) {
+      const int n0 = k * nt;
+      const hipError_t ek = launch_gemv(
+          dev, A, B, xp + (int64_t)n0 * ldx_bytes, x_f32, ldx, (char*)ya + n0 * A.M * ys,
+          B ? (char*)yb + n0 * B->M * ys : nullptr, y_f16, nt, s, gate ? gate + n0 : nullptr);
+      if (ek != hipSuccess) return ek;
+    }
+    return hipSuccess;
+  }
   if (nt > kMaxNT) {
     if (!wide_pass_applies(dev, A.fmt, A.K, x_f32, map.Mtot)) return hipErrorInvalidValue;
     return wide_launch<kFmtQ8, 64, false>(dev, (const void*)gemv_wide_kernel<kFmtQ8, 64, false>,

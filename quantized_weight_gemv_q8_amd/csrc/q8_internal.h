@@ -86,9 +86,12 @@ bool wide_pass_applies(const DevInfo& dev, int fmt, int64_t K, bool x_f32, int64
 
 // y[n] = A x[n] (and yb[n] = B x[n] when B != nullptr) for nt <= 16 tokens.
 // With gate set (fp32 y, no B): y[n] += sigmoid(gate[n]) * (A x[n]).
+// slices > 1 (nt <= 8): that many passes of nt tokens (slices * nt tokens,
+// x and y advancing by nt rows per pass), in one launch where the
+// one-group kernel applies, else one launch per pass.
 hipError_t launch_gemv(const DevInfo& dev, const HMat& A, const HMat* B, const void* x,
                        bool x_f32, int64_t ldx, void* ya, void* yb, bool y_f16, int nt,
-                       hipStream_t s, const float* gate = nullptr);
+                       hipStream_t s, const float* gate = nullptr, int slices = 1);
 
 // LM head pass: logits (may be null) and ids [nt]. The workspace holds the
 // argmax slots and counters; it must be zero before the first pass and is
@@ -152,9 +155,10 @@ hipError_t launch_moe_gate_up(const DevInfo& dev, const HBank& G, const HBank& U
 // h[n][m] = silu(G x_n)[m] * (U x_n)[m]; G, U of one shape; h fp32 or fp16.
 // With extra (one row of the same K and format): xdot[n] = extra . x_n too,
 // in the same launch.
+// slices as for launch_gemv.
 hipError_t launch_glu(const DevInfo& dev, const HMat& G, const HMat& U, const void* x,
                       bool x_f32, void* h, bool h_f16, int nt, hipStream_t s,
-                      const HMat* extra = nullptr, float* xdot = nullptr);
+                      const HMat* extra = nullptr, float* xdot = nullptr, int slices = 1);
 // Router: ids [T][topk] and softmax weights [T][topk] from logits [T][E].
 constexpr int kRouterMaxE = 4096;  // 64 experts per lane of the token's wave
 constexpr int kRouterMaxK = 64;    // one picked logit per lane

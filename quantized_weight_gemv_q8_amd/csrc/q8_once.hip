@@ -17,6 +17,7 @@ using OnceKind = DenseKind;
 
 template hipError_t launch_once_nt<OnceKind, Q8_ONCE_NT>(const DevInfo&, const OnceKind::Map&,
                                                          const OnceKind::Epi&, int, int, bool,
-                                                         const char*, int64_t, int, hipStream_t);
+                                                         const char*, int64_t, int, hipStream_t,
+                                                         int);
 
 }  // namespace q8

@@ -22,6 +22,11 @@ namespace q8 {
 // shapes, so the window follows the chunk count alone.
 constexpr int once_depth(int cpl) { return cpl <= 3 ? cpl : cpl < 8 ? 2 : 4; }
 
+// Fewest tokens per pass of a one-group kernel that runs several passes
+// per launch (blockIdx.y selects the pass); smaller passes take one launch
+// each.
+constexpr int kMinSliceNT = 4;
+
 // Rows per team: one up to 4 tokens; two from 5, which halves the groups
 // (so that 5120 rows fit in the waves the larger x image leaves resident)
 // and shares each LDS read of x between two rows.
@@ -63,6 +68,15 @@ __device__ __forceinline__ void once_body(const typename K::Map& map, typename K
   const int waves = __builtin_amdgcn_readfirstlane(blockDim.x / kWave);
   const int64_t g = (int64_t)blockIdx.x * waves + wave;
   uint4* const lds_s = lds_x + NT * CPL * LPR * P;
+  // Pass blockIdx.y of a launch of several passes, which only kernels of
+  // kMinSliceNT or more tokens take (the check alone made the one-token
+  // kernel 1.5-2% slower on 5120 x 5120).
+  if constexpr (NT >= kMinSliceNT) {
+    if (blockIdx.y != 0) {
+      x += (int64_t)blockIdx.y * NT * ldx_bytes;
+      epi.shift((int)blockIdx.y * NT);
+    }
+  }
   if constexpr (XB > 0) {
     EarlyStage<NT, P, XB, SYNC> stage{x, ldx_bytes, C, NT, lds_x};
     run_once<NT, LPR, R, CPL, D, K::kMinc, XF32, F>(map, epi, lds_x, lds_s, n_groups, g, 0,
@@ -153,7 +167,8 @@ static int once_waves(const DevInfo& dev, const void* fn, int64_t n_groups, size
 // (the caller then takes the persistent launch).
 template <class K, int F, int NT, int LPR, bool XF32, int CPL>
 static hipError_t once_launch_t(const DevInfo& dev, typename K::Map map, typename K::Epi epi,
-                                const char* x, int64_t ldx_bytes, int C, hipStream_t s) {
+                                const char* x, int64_t ldx_bytes, int C, hipStream_t s,
+                                int slices) {
   constexpr int G = kWave / LPR * K::rows_per_team(NT);
   const size_t lds_x = (size_t)NT * C * 16 * ChunkPlanes<F, XF32>::P;
   const size_t lds_wave = (size_t)G * row_scale_pieces(F, C) * 16;  // a wave's scale rows
@@ -179,17 +194,19 @@ static hipError_t once_launch_t(const DevInfo& dev, typename K::Map map, typenam
     }
   }
   void* args[] = {&map, &epi, (void*)&x, &ldx_bytes, &C};
-  return hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(w * kWave), args, lds, s);
+  return hipLaunchKernel(fn, dim3((unsigned)blocks, (unsigned)slices), dim3(w * kWave), args, lds,
+                         s);
 }
 
 template <class K, int F, int NT, int LPR, bool XF32>
 static hipError_t once_launch(const DevInfo& dev, const typename K::Map& map,
                               const typename K::Epi& epi, const char* x, int64_t ldx_bytes, int C,
-                              hipStream_t s) {
-  if (C % LPR != 0) return hipErrorNotSupported;
+                              hipStream_t s, int slices) {
+  if (C % LPR != 0 || slices < 1 || slices > 65535 || (slices > 1 && NT < kMinSliceNT))
+    return hipErrorNotSupported;
   switch (C / LPR) {
 #define Q8_ONCE(N) \
-  case N: return once_launch_t<K, F, NT, LPR, XF32, N>(dev, map, epi, x, ldx_bytes, C, s);
+  case N: return once_launch_t<K, F, NT, LPR, XF32, N>(dev, map, epi, x, ldx_bytes, C, s, slices);
     Q8_ONCE(1) Q8_ONCE(2) Q8_ONCE(3) Q8_ONCE(4) Q8_ONCE(5) Q8_ONCE(6) Q8_ONCE(7) Q8_ONCE(8)
     Q8_ONCE(10) Q8_ONCE(12) Q8_ONCE(14) Q8_ONCE(16)
 #undef Q8_ONCE
@@ -200,10 +217,10 @@ static hipError_t once_launch(const DevInfo& dev, const typename K::Map& map,
 template <class K, int NT>
 hipError_t launch_once_nt(const DevInfo& dev, const typename K::Map& map,
                           const typename K::Epi& epi, int fmt, int lpr, bool x_f32, const char* x,
-                          int64_t ldx_bytes, int C, hipStream_t s) {
+                          int64_t ldx_bytes, int C, hipStream_t s, int slices) {
   return dispatch_chunks(fmt, lpr, x_f32, [&](auto f, auto l, auto xf) {
     return once_launch<K, decltype(f)::value, NT, decltype(l)::value, decltype(xf)::value>(
-        dev, map, epi, x, ldx_bytes, C, s);
+        dev, map, epi, x, ldx_bytes, C, s, slices);
   });
 }
 
@@ -213,7 +230,8 @@ hipError_t launch_once_nt(const DevInfo& dev, const typename K::Map& map,
 #define Q8_ONCE_DECLARE(KIND, N)                                                              \
   extern template hipError_t launch_once_nt<KIND, N>(const DevInfo&, const KIND::Map&,       \
                                                      const KIND::Epi&, int, int, bool,         \
-                                                     const char*, int64_t, int, hipStream_t);
+                                                     const char*, int64_t, int, hipStream_t, \
+                                                     int);
 #define Q8_ONCE_DECLARE_ALL(KIND)                                                             \
   Q8_ONCE_DECLARE(KIND, 1) Q8_ONCE_DECLARE(KIND, 2) Q8_ONCE_DECLARE(KIND, 3)                  \
   Q8_ONCE_DECLARE(KIND, 4) Q8_ONCE_DECLARE(KIND, 5) Q8_ONCE_DECLARE(KIND, 6)                  \
