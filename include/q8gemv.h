@@ -352,10 +352,8 @@ int q8_moe_topk_softmax(const float *logits, int T, int E, int topk, int32_t *ex
 /* Router from a Q8_0 router matrix Wr [E][K]: logits = Wr x (as q8_gemv
  * with fp32 output, so bitwise independent of T), then
  * q8_moe_topk_softmax. x [dev] [T][K] of x_dt; logits [dev] fp32 [T][E]
- * (written, caller-owned). For 9..64 tokens over a Q8_0 matrix of at most
- * 256 rows with fp16 x, one launch (one workgroup per token); otherwise
- * the GEMV launches and the top-k launch. The outputs are the same either
- * way (bitwise). */
+ * (written, caller-owned). Launches: the GEMV's (all its passes in one
+ * launch where the one-group kernel applies), then the top-k launch. */
 int q8_moe_router(const q8_matrix *Wr, const void *x, int x_dt, int T, int topk, float *logits,
                   int32_t *expert_ids, float *gate_w, void *stream);
 

@@ -646,14 +646,7 @@ int q8_moe_router(const q8_matrix* Wr, const void* x, int x_dt, int T, int topk,
   if (overlap(x, xb, expert_ids, ob) || overlap(x, xb, gate_w, ob)) return Q8_ERR_ALIAS;
   if (!aligned(x, 16)) return Q8_ERR_ALIGN;
   if (overlap(x, xb, logits, (size_t)T * Wr->M * 4)) return Q8_ERR_ALIAS;
-  const DevInfo* dev = nullptr;
-  rc = current_device(&dev);
-  if (rc) return rc;
-  // One launch for up to kRouterFusedMaxT tokens; else (or when x and the
-  // logits do not fit one workgroup's LDS) the GEMV, then the top-k launch.
-  const hipError_t e = q8::launch_router(*dev, to_h(Wr), x, x_dt == Q8_DT_F32, T, topk, logits,
-                                         expert_ids, gate_w, (hipStream_t)stream);
-  if (e != hipErrorNotSupported) return launch_rc(e);
+  // The GEMV (all its passes in one launch where it can), then the top-k.
   rc = gemv_impl(Wr, nullptr, x, x_dt, logits, nullptr, Q8_DT_F32, T, stream);
   if (rc) return rc;
   return launch_rc(q8::launch_topk_softmax(logits, T, (int)Wr->M, topk, expert_ids, gate_w,

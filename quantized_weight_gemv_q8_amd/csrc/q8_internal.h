@@ -164,14 +164,6 @@ constexpr int kRouterMaxE = 4096;  // 64 experts per lane of the token's wave
 constexpr int kRouterMaxK = 64;    // one picked logit per lane
 hipError_t launch_topk_softmax(const float* logits, int T, int E, int topk, int32_t* ids,
                                float* gate_w, hipStream_t s);
-// The router in one launch (logits [T][E] = Wr x, then the top-k softmax),
-// one workgroup per token; hipErrorNotSupported outside kRouterFusedMinT..
-// kRouterFusedMaxT tokens, when x and the logits do not fit the workgroup's
-// LDS, or when the matrix is too large for one workgroup to stream quickly.
-constexpr int kRouterFusedMinT = 9;
-constexpr int kRouterFusedMaxT = 64;
-hipError_t launch_router(const DevInfo& dev, const HMat& Wr, const void* x, bool x_f32, int T,
-                         int topk, float* logits, int32_t* ids, float* gate_w, hipStream_t s);
 // out[t] = sum_j gate_w[t][j] * y_pair[t*topk + j] (slots with invalid ids skipped).
 hipError_t launch_moe_combine(const int32_t* ids, int E, const float* gate_w,
                               const float* y_pair, float* out, int T, int topk, int64_t M,

@@ -147,26 +147,25 @@ def test_routed_layer_graph_replays_match_eager(routed_layer):
 
 
 @pytest.mark.parametrize("T,E,K,q4,xf32,topk", [
-    (16, 128, 2048, False, False, 8),   # the routed layer's router: one launch, 8 rows per team
-    (1, 100, 1024, False, False, 6),    # one token: GEMV then top-k (keys in registers)
-    (9, 100, 1024, False, False, 6),    # ragged expert count, the fewest tokens of one launch
-    (64, 128, 2048, False, False, 8),   # the largest one-launch batch
-    (12, 64, 2048, False, False, 4),    # 4 rows per team, keys in one register per lane
-    (13, 200, 512, False, False, 16),   # 32 lanes per row, ragged last wave
+    (16, 128, 2048, False, False, 8),   # the routed layer's router: two passes in one launch
+    (1, 100, 1024, False, False, 6),    # one token (keys in registers)
+    (9, 100, 1024, False, False, 6),    # ragged expert count, a pass of 8 and one of 1
+    (64, 128, 2048, False, False, 8),   # eight passes in one launch
+    (12, 64, 2048, False, False, 4),    # keys in one register per lane
+    (13, 200, 512, False, False, 16),   # 32 lanes per row, ragged last group
     (17, 256, 256, False, False, 64),   # 16 lanes per row, topk at its maximum
-    (9, 9, 256, False, False, 9),       # topk = E = 9: three waves, every expert picked
+    (9, 9, 256, False, False, 9),       # topk = E = 9: every expert picked
     (64, 256, 512, False, False, 64),   # 64 tokens, four keys per lane
-    (7, 256, 256, False, False, 64),    # fewer than 9 tokens: two launches
-    (65, 128, 2048, False, False, 8),   # one token more: GEMV then top-k launch
-    (64, 128, 2048, False, True, 8),    # fp32 x: two launches
-    (16, 256, 4096, False, False, 8),   # too many loads per lane: two launches
-    (7, 4096, 512, False, False, 64),   # E and topk at their maximum: two launches
-    (16, 128, 2048, True, False, 8),    # Q4_0 router matrix: two launches
+    (7, 256, 256, False, False, 64),    # one pass of 7
+    (65, 128, 2048, False, False, 8),   # eight passes of 8 and one of 1
+    (64, 128, 2048, False, True, 8),    # fp32 x
+    (16, 256, 4096, False, False, 8),   # 256 experts over K = 4096
+    (7, 4096, 512, False, False, 64),   # E and topk at their maximum (keys in LDS)
+    (16, 128, 2048, True, False, 8),    # Q4_0 router matrix
     (5, 96, 96, True, True, 4),         # Q4_0, fp32 x, three blocks per row
 ])
 def test_router_equals_gemv_then_topk(T, E, K, q4, xf32, topk):
-    """q8_moe_router (one launch for 9 to 64 tokens over a small enough
-    Q8_0 router matrix with fp16 x, else the GEMV and top-k launches) returns bitwise q8_gemv's logits and bitwise
+    """q8_moe_router returns bitwise q8_gemv's logits and bitwise
     q8_moe_topk_softmax's ids and weights over them, with duplicated router
     rows so that equal logits occur; the picks also match the oracle's."""
     note(f"router T={T} E={E} K={K} q4={q4} xf32={xf32} topk={topk}")
