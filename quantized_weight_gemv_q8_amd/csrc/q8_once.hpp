@@ -127,7 +127,7 @@ constexpr bool once_early(int nt) { return nt == 2; }
 // Waves per workgroup for a one-group-per-wave launch of n_groups waves: 8,
 // unless the launch gives the compute units at least 8 waves each and
 // another resident size spreads them more evenly (the first in the order
-// 10, 16, 5, 4 among the most even). Measured on MI355X at N = 1 (us,
+// 10, 16, 5, 4 among the most even), or gives them fewer (below). Measured on MI355X at N = 1 (us,
 // sweeps of 4, 5, 8, 10 and 16 waves): 5120 x 5120 10 waves 6.60 against 8
 // waves 6.86 (640 workgroups, 2 or 3 per CU); with fewer waves per CU
 // larger workgroups win, e.g. 1024 x 16384 8 waves 6.71 against 4 waves
@@ -144,6 +144,22 @@ static int once_waves(const DevInfo& dev, const void* fn, int64_t n_groups, size
                       size_t lds_per_wave, bool stream) {
   static const int kSizes[] = {8, 10, 16, 5, 4};
   const bool spread = n_groups >= 8 * (int64_t)dev.cus;
+  // Fewer than 8 groups per CU: workgroups of ceil(groups / CUs) waves but
+  // at least 4, so that every CU gets one where the groups allow (smaller
+  // workgroups each stage x again). Measured on MI355X against 8-wave
+  // workgroups (same-process A/B): 2048 x 768 N = 1 / 2 / 8 2.90 / 3.20 /
+  // 6.21 -> 2.78 / 2.99 / 4.87 us, 1024 x 1024 N = 2 / 8 2.87 / 4.12 ->
+  // 2.69 / 3.69, a 128 x 2048 router at 8-64 tokens 10% faster, the shared
+  // expert 3%; with 1- to 3-wave workgroups the router lost up to 12%.
+  if (!spread) {
+    int64_t w = (n_groups + dev.cus - 1) / dev.cus;
+    w = w < 4 ? 4 : w > 8 ? 8 : w;
+    const size_t lds = lds_fixed + (size_t)w * lds_per_wave;
+    const int64_t blocks = (n_groups + w - 1) / w;
+    if (lds <= dev.lds_per_block &&
+        (blocks + dev.cus - 1) / dev.cus <= blocks_per_cu(fn, lds, (int)w * kWave))
+      return (int)w;
+  }
   int best = 0;
   double best_eff = 0.0;
   for (int w : kSizes) {
