@@ -127,11 +127,11 @@ constexpr bool once_early(int nt) { return nt == 2; }
 // Waves per workgroup for a one-group-per-wave launch of n_groups waves: 8,
 // unless the launch gives the compute units at least 8 waves each and
 // another resident size spreads them more evenly (the first in the order
-// 10, 16, 5, 4 among the most even), or gives them fewer (below). Measured on MI355X at N = 1 (us,
-// sweeps of 4, 5, 8, 10 and 16 waves): 5120 x 5120 10 waves 6.60 against 8
-// waves 6.86 (640 workgroups, 2 or 3 per CU); with fewer waves per CU
-// larger workgroups win, e.g. 1024 x 16384 8 waves 6.71 against 4 waves
-// 7.43 (each workgroup stages all of x).
+// 10, 16, 5, 4 among the most even), or gives them fewer (below).
+// Measured on MI355X at N = 1 (us, sweeps of 4, 5, 8, 10 and 16 waves):
+// 5120 x 5120 10 waves 6.60 against 8 waves 6.86 (640 workgroups, 2 or 3
+// per CU); with fewer waves per CU larger workgroups win, e.g. 1024 x
+// 16384 8 waves 6.71 against 4 waves 7.43 (each workgroup stages all of x).
 // LDS per workgroup: lds_fixed plus lds_per_wave for each wave. With
 // stream set, a launch whose groups do not all fit in the resident waves
 // still takes this kernel with 8-wave workgroups, the hardware starting
