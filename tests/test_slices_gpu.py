@@ -8,9 +8,9 @@ take fall back to one launch per pass inside the library.
 Checked through the C ABI, each token against the oracle bound and bitwise
 against the same token run alone: the dense GEMV (fp16 and fp32 x, fp32
 and fp16 y, 2-4 slices plus a ragged last pass), the pair (two outputs
-shifted per pass), the SiLU pair, passes of 5 tokens set by the LDS, a
-shape that falls back, and the shared expert (h, the gate dots and the
-gated add all shifted per pass).
+shifted per pass; Q8_0 and Q4_0), the SiLU pair, passes of 5 tokens set by
+the LDS, a shape that falls back, and the shared expert (h, the gate dots
+and the gated add all shifted per pass; Q8_0 with fp16 or fp32 x, Q4_0).
 """
 import numpy as np
 import pytest
@@ -56,13 +56,16 @@ def test_sliced_gemv(M, K, N, xf32, yf16):
         assert np.array_equal(_bits(y1[0]), _bits(y[n])), f"token {n}"
 
 
-def test_sliced_pair():
-    note("sliced pair 600+400 x 1024 N=16")
+@pytest.mark.parametrize("q4", [False, True])
+def test_sliced_pair(q4):
+    note(f"sliced pair 600+400 x 1024 N=16 q4={q4}")
     rng = np.random.default_rng(5)
-    qa, da = synth.draw_weights(rng, 600, 1024)
-    qb, db = synth.draw_weights(rng, 400, 1024)
+    draw = synth.draw_weights_q4_0 if q4 else synth.draw_weights
+    qa, da = draw(rng, 600, 1024)
+    qb, db = draw(rng, 400, 1024)
     x = synth.draw_x(rng, 16, 1024)
-    Wa, Wb = upload(qa, da), upload(qb, db)
+    pack = (lambda q, d: q8.pack_q4_0(synth.to_gguf_q4_0_blocks(q, d))) if q4 else upload
+    Wa, Wb = pack(qa, da), pack(qb, db)
     ya, yb = (host(t) for t in q8.gemv_pair(Wa, Wb, dev(x)))
     for q, d, y in ((qa, da, ya), (qb, db, yb)):
         ref, A = oracle.gemv(q, d, x, threads())
@@ -89,20 +92,22 @@ def test_sliced_silu_pair():
         assert np.array_equal(_bits(h1[0]), _bits(h[n])), f"token {n}"
 
 
-@pytest.mark.parametrize("T,xf32", [(24, False), (20, True)])
-def test_sliced_shared_expert(T, xf32):
-    note(f"sliced shared expert T={T} xf32={xf32}")
+@pytest.mark.parametrize("T,xf32,q4", [(24, False, False), (20, True, False), (16, False, True)])
+def test_sliced_shared_expert(T, xf32, q4):
+    note(f"sliced shared expert T={T} xf32={xf32} q4={q4}")
     F, H = 768, 2048
     rng = np.random.default_rng(T)
-    qg, dg = synth.draw_weights(rng, F, H)
-    qu, du = synth.draw_weights(rng, F, H)
-    qd, dd = synth.draw_weights(rng, H, F)
-    qs, ds = synth.draw_weights(rng, 1, H)
+    draw = synth.draw_weights_q4_0 if q4 else synth.draw_weights
+    qg, dg = draw(rng, F, H)
+    qu, du = draw(rng, F, H)
+    qd, dd = draw(rng, H, F)
+    qs, ds = draw(rng, 1, H)
     x = synth.draw_x(rng, T, H)
     if xf32:
         x = x.astype(np.float32)
     base = rng.standard_normal((T, H)).astype(np.float32)
-    mats = tuple(upload(a, b) for a, b in ((qg, dg), (qu, du), (qd, dd), (qs, ds)))
+    pack = (lambda q, d: q8.pack_q4_0(synth.to_gguf_q4_0_blocks(q, d))) if q4 else upload
+    mats = tuple(pack(a, b) for a, b in ((qg, dg), (qu, du), (qd, dd), (qs, ds)))
     out = dev(base.copy())
     q8.moe_shared_expert(*mats, dev(x), out)
     got = host(out)
