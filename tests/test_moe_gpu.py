@@ -128,6 +128,15 @@ def test_small_configs_stagewise(E, F, H, T, topk):
     stagewise(c, banks(c))
 
 
+def test_full_dims_larger_batch_stagewise():
+    """The layer's shapes at 40 tokens (320 pairs, about 2.5 per active
+    expert): experts spanning several two-pair slots, every stage against
+    the oracle."""
+    note("moe e128 top8 t40 stagewise")
+    c = synth.moe_case(E=128, F=768, H=2048, T=40, topk=8, seed=40)
+    stagewise(c, banks(c))
+
+
 def test_expert_permutation_invariance():
     note("moe expert permutation")
     c = synth.moe_case(E=12, F=64, H=256, T=6, topk=3, seed=3)
