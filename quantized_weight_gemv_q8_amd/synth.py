@@ -47,6 +47,30 @@ def draw_weights(rng: np.random.Generator, M: int, K: int):
     return q, d
 
 
+def draw_weights_tiled(rng: np.random.Generator, M: int, K: int, q_period: int = 4099,
+                       d_period: int = 4111):
+    """A Q8_0 matrix of several GB at a small fraction of the drawing cost:
+    the quants of q_period rows and the scales of d_period rows are drawn
+    as in ``draw_weights``, and row m takes quant row m % q_period and scale
+    row m % d_period. With two distinct primes no (quants, scales) pair
+    recurs within q_period * d_period rows, so a row read from a wrong
+    offset (a multiple of 2^31 or 2^32 bytes, say) meets other quants,
+    other scales or both. Elementwise the distributions are those of
+    ``draw_weights``."""
+    if K % QK:
+        raise ValueError(f"K={K} is not a multiple of {QK}")
+    qb = rng.integers(-127, 128, size=(q_period, K), dtype=np.int8)
+    db = (np.abs(rng.normal(0.0, 0.02, size=(d_period, K // QK))) / 127.0).astype(np.float16)
+
+    def tile(block, period):
+        out = np.empty((M,) + block.shape[1:], block.dtype)
+        for m0 in range(0, M, period):
+            out[m0:m0 + period] = block[:min(period, M - m0)]
+        return out
+
+    return tile(qb, q_period), tile(db, d_period)
+
+
 def draw_x(rng: np.random.Generator, N: int, K: int) -> np.ndarray:
     return rng.normal(0.0, 1.0, size=(N, K)).astype(np.float16)
 
@@ -156,15 +180,24 @@ def lmhead_case(V: int, K: int, N: int, seed: int = 0, lead_sigmas: float = 8.9)
     q, d = draw_weights(rng, V, K)
     x = draw_x(rng, N, K)
     rows = rng.choice(V, size=N, replace=False).astype(np.int64)
-    sigma = logit_sigma(K)
-    target = np.full(N, lead_sigmas * sigma, dtype=np.float64)
+    target = plant_argmax_rows(q, d, x, rows, lead_sigmas)
+    return LmHeadCase(q, d, x, rows, target)
+
+
+def plant_argmax_rows(q: np.ndarray, d: np.ndarray, x: np.ndarray, rows, lead_sigmas: float = 8.9):
+    """In place: row rows[n] becomes token n's planted argmax (quants
+    127*sign(x[n,k]), every scale the smallest fp16 D_n with
+    D_n * 127 * sum_k |x[n,k]| >= lead_sigmas * sigma). Returns the analytic
+    targets, float64 [N]."""
+    N, K = x.shape
+    target = np.full(N, lead_sigmas * logit_sigma(K), dtype=np.float64)
     for n in range(N):
         xn = x[n].astype(np.float64)
         r = int(rows[n])
         q[r] = (np.sign(xn) * 127).astype(np.int8)
         s_abs = float(np.abs(xn).sum())
         d[r] = fp16_at_least(target[n] / (127.0 * s_abs))
-    return LmHeadCase(q, d, x, rows, target)
+    return target
 
 
 @dataclasses.dataclass
