@@ -40,6 +40,17 @@
  *    HIP call. Unsupported inputs are refused, never silently routed to a
  *    slow path (topairepos memra listing, which prefers a clear failure to a
  *    quiet fallback).
+ *  - Sizes: a pass's activations are held in the LDS of one workgroup
+ *    (160 KiB on MI355X), so a K for which not even one token fits is
+ *    refused with Q8_ERR_SHAPE. q8_gemv, the pairs, the router and the
+ *    shared expert need K*2 bytes (fp16 x) or K*4 (fp32 x): K <= 81920 or
+ *    40960 on MI355X (the shared expert's down projection reads fp32 h, so
+ *    F <= 40960). The LM heads keep 1 KiB of their own: K <= 81408 or
+ *    40704. The routed experts stage four tokens' rows next to 1 KiB of
+ *    tables: K <= 20352 or 10176 (the FFN's down projection reads fp32 h,
+ *    so F <= 10176). Routed calls take E <= 4096 and T*topk <= 8192 pairs,
+ *    with (min(E, T*topk) + T*topk/2 + 1) * M < 2^31 (their row space is
+ *    indexed in 32 bits). Weights and outputs are addressed in 64 bits.
  *  - The library runs only on gfx950; on any other device every hot-path
  *    call returns Q8_ERR_DEVICE (memra wiki: the engine verifies at start-up
  *    that the binary matches the device and fails early otherwise).

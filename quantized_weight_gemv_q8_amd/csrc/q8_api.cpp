@@ -361,7 +361,7 @@ static int lmhead_impl(const q8_matrix* W, const int32_t* row_ids, const void* x
   rc = current_device(&dev);
   if (rc) return rc;
   const bool xf = x_dt == Q8_DT_F32;
-  const int per_pass = q8::max_tokens_per_pass(*dev, W->K, xf);
+  const int per_pass = q8::lmhead_max_tokens_per_pass(*dev, W->K, xf);
   if (per_pass < 1) return Q8_ERR_SHAPE;
   const HMat A = to_h(W);
   for (int n0 = 0; n0 < N; n0 += per_pass) {

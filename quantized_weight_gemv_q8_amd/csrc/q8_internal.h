@@ -97,6 +97,9 @@ hipError_t launch_gemv(const DevInfo& dev, const HMat& A, const HMat* B, const v
 // argmax slots and counters; it must be zero before the first pass and is
 // zero again after each completed pass.
 size_t lmhead_ws_bytes(int64_t V);
+// Tokens per LM-head pass: the x image of a pass plus the fused kernel's
+// static LDS fit one workgroup's LDS (<= 8; 0 if not even one token fits).
+int lmhead_max_tokens_per_pass(const DevInfo& dev, int64_t K, bool x_f32);
 hipError_t launch_lmhead(const DevInfo& dev, const HMat& W, const int32_t* row_ids, const void* x,
                          bool x_f32, float* logits, int64_t ld_logits, int32_t* ids, char* ws,
                          int nt, hipStream_t s);

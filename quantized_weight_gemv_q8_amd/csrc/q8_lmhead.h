@@ -7,6 +7,9 @@
 namespace q8 {
 
 constexpr int kLmMaxBlocks = 4096;
+// Static LDS of the fused head (lm_merge_keys' per-wave keys): the x image
+// of a pass gets what is left of the workgroup's LDS.
+constexpr size_t kLmStaticLds = sizeof(uint64_t) * (kOnceMaxBlock / kWave) * kMaxNT;
 
 __device__ __forceinline__ uint64_t argmax_key(float v, int64_t row) {
   if (v == 0.0f) v = 0.0f;  // -0 -> +0
@@ -109,6 +112,7 @@ template <int NT>
 __device__ __forceinline__ void lm_merge_keys(const uint64_t* key, const int32_t* row_ids,
                                               char* ws, int32_t* ids, int waves) {
   __shared__ uint64_t red[kOnceMaxBlock / kWave][kMaxNT];
+  static_assert(sizeof(red) == kLmStaticLds, "the pass size reserves exactly this");
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lane = threadIdx.x % kWave;
 #pragma unroll

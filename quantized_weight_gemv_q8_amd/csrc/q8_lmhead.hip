@@ -190,6 +190,14 @@ static bool two_launch_pays(const HMat& W, int nt, bool logits) {
   return bytes >= (logits ? 150e6 : 280e6);
 }
 
+int lmhead_max_tokens_per_pass(const DevInfo& dev, int64_t K, bool x_f32) {
+  const size_t per = x_lds_bytes(1, K, x_f32);
+  if (dev.lds_per_block <= kLmStaticLds) return 0;
+  size_t n = (dev.lds_per_block - kLmStaticLds) / per;
+  if (n > (size_t)kMaxNT) n = kMaxNT;
+  return (int)n;
+}
+
 // Slots and counters, then scratch logits for two tokens (256-byte aligned).
 size_t lmhead_ws_bytes(int64_t V) {
   const size_t scratch = ((size_t)(V > 0 ? V : 0) * 2 * sizeof(float) + 255) / 256 * 256;
