@@ -572,15 +572,30 @@ __device__ __forceinline__ float pair_sum(float v) {
 
 // One halving level over a pair of values (a, b): a lane whose DELTA bit is
 // clear returns a + (its partner's a), one whose bit is set b + (its
-// partner's b); the lane selects what to send and what to keep. (Adding
-// the two results of one permlane swap of a against b would give the same
-// sums without the selects, but this compiler folds that sum into twice
-// the first result, so the swap's results are only ever selected.)
-template <int DELTA>
+// partner's b).
+// With SW, distances 32 and 16 take one gfx950 half swap of a against b:
+// v_permlane32_swap_b32 exchanges the upper 32 lanes of a with the lower 32
+// lanes of b, v_permlane16_swap_b32 each odd 16-lane row of a with the even
+// row before it in b. Afterwards a first-half lane holds its own a and its
+// partner's a, a second-half lane its partner's b and its own b, so the
+// sum of the two results is the pair sum with no select. (Swapping a value
+// against itself must not take this path: this compiler folds the sum of
+// that swap's two results into twice the first, which is why pair_sum
+// selects.) Other distances, and every distance without SW, select what
+// to send and what to keep around one exchange. Both forms add the same
+// two values, so the choice never changes a result.
+template <int DELTA, bool SW>
 __device__ __forceinline__ float half_sum(float a, float b, bool hi) {
-  const float send = hi ? a : b;
-  const float keep = hi ? b : a;
-  return keep + xor_lane<DELTA>(send);
+  if constexpr (SW && (DELTA == 16 || DELTA == 32)) {
+    const unsigned x = __builtin_bit_cast(unsigned, a), y = __builtin_bit_cast(unsigned, b);
+    const auto sw = DELTA == 32 ? __builtin_amdgcn_permlane32_swap(x, y, false, false)
+                                : __builtin_amdgcn_permlane16_swap(x, y, false, false);
+    return __builtin_bit_cast(float, (unsigned)sw[0]) + __builtin_bit_cast(float, (unsigned)sw[1]);
+  } else {
+    const float send = hi ? a : b;
+    const float keep = hi ? b : a;
+    return keep + xor_lane<DELTA>(send);
+  }
 }
 
 // ---------------------------------------------------------------- team reduction
@@ -594,7 +609,7 @@ __device__ __forceinline__ float half_sum(float a, float b, bool hi) {
 // number of values carried, so the result of each (row, token) does not
 // depend on R or NT. fp32 addition is commutative, so the side a value
 // arrives from does not matter.
-template <int CNT, int MINC, int DELTA>
+template <int CNT, int MINC, int DELTA, bool SW = false>
 struct TeamReduce {
   static __device__ __forceinline__ void run(float* v, int p, int& base) {
     if constexpr (DELTA == 0) {
@@ -604,18 +619,37 @@ struct TeamReduce {
       const bool hi = (p & DELTA) != 0;
       float nv[H];
 #pragma unroll
-      for (int i = 0; i < H; ++i) nv[i] = half_sum<DELTA>(v[i], v[i + H], hi);
+      for (int i = 0; i < H; ++i) nv[i] = half_sum<DELTA, SW>(v[i], v[i + H], hi);
 #pragma unroll
       for (int i = 0; i < H; ++i) v[i] = nv[i];
       if (hi) base += H;
-      TeamReduce<H, MINC, DELTA / 2>::run(v, p, base);
+      TeamReduce<H, MINC, DELTA / 2, SW>::run(v, p, base);
     } else {
 #pragma unroll
       for (int i = 0; i < CNT; ++i) v[i] = pair_sum<DELTA>(v[i]);
-      TeamReduce<CNT, MINC, DELTA / 2>::run(v, p, base);
+      TeamReduce<CNT, MINC, DELTA / 2, SW>::run(v, p, base);
     }
   }
 };
+
+// Where the reduction takes the half swaps: Q8_0 weights, fp16 x and
+// 64-lane rows (the large matrices of the decode step). Measured on MI355X
+// (same-process A/B, bitwise equal outputs): 1.5-3.5% off 3- to 16-token
+// passes of 5120 x 5120 and of the 2 x 17408 x 5120 pair and SiLU pair,
+// 1.5% off the router; the 151936-row LM head at 8 tokens 2% slower.
+// Elsewhere the register allocation that follows cost occupancy or
+// spilled (Q4_0 and fp32-x one-group kernels at 5-7 tokens), so those keep
+// the selects.
+template <int F, int LPR, bool XF32>
+constexpr bool swap_reduce() { return F == kFmtQ8 && !XF32 && LPR == 64; }
+
+// Waves per SIMD the register budget of a persistent row kernel must
+// allow: six for 4-token passes with the half swaps, so that two 12-wave
+// workgroups share a CU as the LDS allows (the swaps' register allocation
+// would otherwise take 86 registers and leave room for one); otherwise no
+// bound beyond the workgroup's own.
+template <int F, int NT, int LPR, bool XF32>
+constexpr int narrow_waves_per_simd() { return NT == 4 && swap_reduce<F, LPR, XF32>() ? 6 : 1; }
 
 template <int V>
 struct Pow2 {
@@ -779,7 +813,7 @@ __device__ __forceinline__ void run_rows(const Map& map, Epi& epi, const uint4* 
           // No branch on cg here either (see run_once): past the last
           // group the owner flag is false and nothing is emitted.
           int base = 0;
-          TeamReduce<VP, MINC, LPR / 2>::run(acc, p, base);
+          TeamReduce<VP, MINC, LPR / 2, swap_reduce<F, LPR, XF32>()>::run(acc, p, base);
           const bool owner = (p & Shape::OWNER_MASK) == 0 && cg < n_groups;
           const int64_t rbase = row_origin + cg * G + (int64_t)team * R;
           epi.template emit<NT, R, Shape::CNT>(rbase, base, owner, acc);
@@ -894,7 +928,7 @@ __device__ __forceinline__ void run_once(const Map& map, Epi& epi, const uint4* 
   // here made the compiler restructure the whole kernel around it (about
   // 5% slower at 5120 x 5120); a dead wave's owner flag is simply false.
   int base = 0;
-  TeamReduce<VP, MINC, LPR / 2>::run(acc, p, base);
+  TeamReduce<VP, MINC, LPR / 2, swap_reduce<F, LPR, XF32>()>::run(acc, p, base);
   const bool owner = (p & Shape::OWNER_MASK) == 0 && g < n_groups;
   epi.template emit<NT, R, Shape::CNT>(rbase, base, owner, acc);
 }

@@ -49,7 +49,8 @@ hipError_t launch_glu_once(int nt, const DevInfo& dev, const GluMap& map, const 
 }
 
 template <int F, int NT, int LPR, bool XF32, int MODE>
-__global__ __launch_bounds__(narrow_block<NT>()) void gemv_kernel(DenseMap map, DenseEpi epi, const char* x,
+__global__ __launch_bounds__(narrow_block<NT>()) __attribute__((
+    amdgpu_waves_per_eu(narrow_waves_per_simd<F, NT, LPR, XF32>()))) void gemv_kernel(DenseMap map, DenseEpi epi, const char* x,
                                                       int64_t ldx_bytes, int C) {
   extern __shared__ uint4 lds_x[];
   using T = TuneM<NT, MODE>;
@@ -163,7 +164,8 @@ struct GluTune {
 };
 
 template <int F, int NT, int LPR, bool XF32, bool BIG>
-__global__ __launch_bounds__(narrow_block<NT>()) void glu_kernel(GluMap map, GluEpi epi, const char* x,
+__global__ __launch_bounds__(narrow_block<NT>()) __attribute__((
+    amdgpu_waves_per_eu(narrow_waves_per_simd<F, NT, LPR, XF32>()))) void glu_kernel(GluMap map, GluEpi epi, const char* x,
                                                      int64_t ldx_bytes, int C) {
   extern __shared__ uint4 lds_x[];
   constexpr int R = GluTune<NT, BIG>::R;

@@ -397,7 +397,7 @@ __device__ __forceinline__ void run_routed(const RowOf& rowof, Epi& epi, const u
       if (++cj == CPL) {
         if (cg < g_end) {
           int base = 0;
-          TeamReduce<VP, MINC, LPR / 2>::run(acc, p, base);
+          TeamReduce<VP, MINC, LPR / 2, swap_reduce<F, LPR, XF32>()>::run(acc, p, base);
           const bool owner = (p & Shape::OWNER_MASK) == 0;
           epi.pid = seg_pid + (cv - v0) * NT;
           epi.nt = nt;
