@@ -305,10 +305,14 @@ static hipError_t launch_sz(const DevInfo& dev, DenseMap map, DenseEpi epi, cons
   // fewer groups than the chip's wave slots. Measured on MI355X: 5120 x
   // 5120 at N = 2, 4, 8 runs 5%, 8% and 11% faster, 2048 x 768 at N = 1
   // 8% faster; with ~20 groups per CU (5120 x 5120, N = 1) the deeper
-  // window is 5% slower, so N = 1 keeps the usual mode there.
+  // window is 5% slower, so N = 1 keeps the usual mode there. Q4_0 passes
+  // of 6 or more tokens over at least 8 groups per CU keep the usual mode
+  // too (17408 x 5120, 8.5 groups per CU, at N = 6 and 8: 3% and 5%
+  // faster; at N = 4 it is 11% slower).
   constexpr int G0 = (kWave / LPR) * TuneM<NT, 0>::R;
   const int64_t groups = (map.Mtot + G0 - 1) / G0;
-  if (groups <= 2 * (int64_t)dev.cus || (NT > 1 && groups < (int64_t)dev.cus * 32))
+  const bool q4_wide = F == kFmtQ4 && NT >= 6 && groups >= 8 * (int64_t)dev.cus;
+  if (groups <= 2 * (int64_t)dev.cus || (NT > 1 && !q4_wide && groups < (int64_t)dev.cus * 32))
     return launch_t<F, NT, LPR, XF32, 2>(dev, map, epi, x, ldx_bytes, C, s);
   return launch_t<F, NT, LPR, XF32, 0>(dev, map, epi, x, ldx_bytes, C, s);
 }
