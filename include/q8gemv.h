@@ -50,7 +50,8 @@
  *    tables: K <= 20352 or 10176 (the FFN's down projection reads fp32 h,
  *    so F <= 10176). Routed calls take E <= 4096 and T*topk <= 8192 pairs,
  *    with (min(E, T*topk) + T*topk/2 + 1) * M < 2^31 (their row space is
- *    indexed in 32 bits). Weights and outputs are addressed in 64 bits.
+ *    indexed in 32 bits). A matrix has at most 2^31 - 1 rows. Weights and
+ *    outputs are addressed in 64 bits.
  *  - The library runs only on gfx950; on any other device every hot-path
  *    call returns Q8_ERR_DEVICE (memra wiki: the engine verifies at start-up
  *    that the binary matches the device and fails early otherwise).
