@@ -80,6 +80,36 @@ __device__ __forceinline__ void quants_to_h2(const uint4 q, h2_t out[8]) {
   }
 }
 
+// The same 8 fp16 pairs by converting each byte directly: SDWA byte
+// selects with sign extension into v_cvt_f16_i16, two instructions per
+// pair (the second writes the high half and keeps the low one) against
+// five per two pairs above. The values, and so every bit of every result,
+// are the same (int8 -> fp16 is exact both ways). Written as asm because
+// this compiler shifts each byte down and packs the halves instead of
+// using the byte selects and the preserving half write. Used by the
+// persistent loop from 4 tokens per pass, where the dot products bound the
+// kernel: measured on MI355X (same-process A/B, bitwise equal outputs),
+// the 2 x 17408 x 5120 pair at 5-7 tokens 2.6-3.4% faster, the SiLU pair
+// at 8 tokens 2.4%, the 151936-row LM head at 4-8 tokens 1.6-2.7%. In
+// the one-group kernels the register allocation around the asm blocks
+// spilled at 6-8 tokens (4096 x 4096 at 8 tokens 5% slower), so they keep
+// the conversion above.
+__device__ __forceinline__ void quants_to_h2_sdwa(const uint4 q, h2_t out[8]) {
+  const unsigned w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    unsigned lo, hi;
+    asm("v_cvt_f16_i16_sdwa %0, sext(%2) dst_sel:WORD_0 dst_unused:UNUSED_PAD src0_sel:BYTE_0\n\t"
+        "v_cvt_f16_i16_sdwa %0, sext(%2) dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_1\n\t"
+        "v_cvt_f16_i16_sdwa %1, sext(%2) dst_sel:WORD_0 dst_unused:UNUSED_PAD src0_sel:BYTE_2\n\t"
+        "v_cvt_f16_i16_sdwa %1, sext(%2) dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_3"
+        : "=&v"(lo), "=&v"(hi)
+        : "v"(w[i]));
+    out[2 * i] = __builtin_bit_cast(h2_t, lo);
+    out[2 * i + 1] = __builtin_bit_cast(h2_t, hi);
+  }
+}
+
 // The first pair of a dot-product chain, a*b summed onto a zero. With ZA
 // it is v_dot2_f32_f16 taking the zero as an inline constant; the builtin
 // given a zero accumulator becomes a move of 0 plus the two-address v_dot2c
@@ -259,7 +289,7 @@ __device__ __forceinline__ float dot16_f32_h(const h2_t w[8], const uint4 x[4], 
 
 // One chunk c of R rows (quants q[r], fp16 scale bits d[r]) against the LDS
 // image xb of the live tokens n < nt: acc[n*R + r] += fp32(d) * chunk sum.
-template <int F, int NT, int R, bool XF32>
+template <int F, int NT, int R, bool XF32, bool SDWA = false>
 __device__ __forceinline__ void chunk_fma(const uint4* q, const uint32_t* d, const uint4* xb, int C,
                                           int c, int nt, float* acc) {
   constexpr int P = ChunkPlanes<F, XF32>::P;
@@ -269,7 +299,10 @@ __device__ __forceinline__ void chunk_fma(const uint4* q, const uint32_t* d, con
   if constexpr (F == kFmtQ8 && !XF32) {
     h2_t qh[R][8];
 #pragma unroll
-    for (int r = 0; r < R; ++r) quants_to_h2(q[r], qh[r]);
+    for (int r = 0; r < R; ++r) {
+      if constexpr (SDWA) quants_to_h2_sdwa(q[r], qh[r]);
+      else quants_to_h2(q[r], qh[r]);
+    }
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
       if (n >= nt) continue;  // not break: a fixed trip count keeps acc[] in registers
@@ -806,7 +839,7 @@ __device__ __forceinline__ void run_rows(const Map& map, Epi& epi, const uint4* 
 #pragma unroll
     for (int s = 0; s < D; ++s) {
       const int c = p + LPR * cj;
-      if (c < C) chunk_fma<F, NT, R, XF32>(slot[s].q, slot[s].d, lds, C, c, nt, acc);
+      if (c < C) chunk_fma<F, NT, R, XF32, (NT >= 4)>(slot[s].q, slot[s].d, lds, C, c, nt, acc);
       issue(slot[s]);
       if (++cj == CPL) {
         {
