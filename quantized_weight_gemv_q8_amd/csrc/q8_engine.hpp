@@ -381,6 +381,17 @@ __device__ __forceinline__ void chunk_fma(const uint4* q, const uint32_t* d, con
   }
 }
 
+// The one-group kernels that take the SDWA conversion: Q8_0, fp16 x,
+// 64-lane rows of five chunks per lane (K = 5120) at 4 or 8 tokens, where
+// the registers allow it. Measured on MI355X (same-process A/B, bitwise
+// equal outputs): 5120 x 5120 at N = 4 / 8 / 9 / 16 5.0 / 2.8 / 1.9 /
+// 3.2% faster; at other widths and chunk counts the allocation spilled or
+// lost occupancy (4096 x 4096 at N = 8 5% slower).
+template <int F, int NT, int LPR, int CPL, bool XF32>
+constexpr bool once_sdwa() {
+  return F == kFmtQ8 && !XF32 && LPR == 64 && CPL == 5 && (NT == 4 || NT == 8);
+}
+
 // ---------------------------------------------------------------- x staging
 // LDS image of x for one pass: token n, plane h (16-byte piece h of a chunk:
 // 2 planes for fp16, 4 for fp32), chunk c at uint4 index (n*P + h)*C + c.
@@ -954,7 +965,7 @@ __device__ __forceinline__ void run_once(const Map& map, Epi& epi, const uint4* 
 #pragma unroll
     for (int r = 0; r < R; ++r)
       dd[r] = reinterpret_cast<const uint16_t*>(srow_lds + r * SP)[c >> Fmt<F>::kScaleShift];
-    chunk_fma<F, NT, R, XF32>(slot[j % D].q, dd, lds, C, c, nt, acc);
+    chunk_fma<F, NT, R, XF32, once_sdwa<F, NT, LPR, CPL, XF32>()>(slot[j % D].q, dd, lds, C, c, nt, acc);
     if (j + D < CPL) issue(slot[j % D], j + D);
   }
   // Reduced and emitted without a branch on g: a wave-uniform early exit
