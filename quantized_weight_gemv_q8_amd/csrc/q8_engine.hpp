@@ -381,15 +381,16 @@ __device__ __forceinline__ void chunk_fma(const uint4* q, const uint32_t* d, con
   }
 }
 
-// The one-group kernels that take the SDWA conversion: Q8_0, fp16 x,
-// 64-lane rows of five chunks per lane (K = 5120) at 4 or 8 tokens, where
-// the registers allow it. Measured on MI355X (same-process A/B, bitwise
-// equal outputs): 5120 x 5120 at N = 4 / 8 / 9 / 16 5.0 / 2.8 / 1.9 /
-// 3.2% faster; at other widths and chunk counts the allocation spilled or
-// lost occupancy (4096 x 4096 at N = 8 5% slower).
+// The one-group kernels that take the SDWA conversion: Q8_0, fp16 x and
+// 64-lane rows at 4 or 8 tokens, except the two chunk counts where the
+// register allocation around the asm spilled (8 tokens, 4 chunks per lane:
+// 4096 x 4096 at N = 8 5% slower) or lost occupancy (4 tokens, 10 chunks).
+// Measured on MI355X (same-process A/B, bitwise equal outputs): 5120 x
+// 5120 at N = 4 / 8 / 9 / 16 5.0 / 2.8 / 1.9 / 3.2% faster, 4096 x 4096
+// and 1024 x 1024 at N = 4 1.0 and 1.4%; 5 to 7 tokens gained nothing.
 template <int F, int NT, int LPR, int CPL, bool XF32>
 constexpr bool once_sdwa() {
-  return F == kFmtQ8 && !XF32 && LPR == 64 && CPL == 5 && (NT == 4 || NT == 8);
+  return F == kFmtQ8 && !XF32 && LPR == 64 && ((NT == 4 && CPL != 10) || (NT == 8 && CPL != 4));
 }
 
 // ---------------------------------------------------------------- x staging
