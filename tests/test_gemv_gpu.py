@@ -46,6 +46,27 @@ def test_unit_vector_every_int8_bitwise(K, j):
     assert np.array_equal(y[0], (np.arange(256) - 128).astype(np.float32))
 
 
+@pytest.mark.parametrize("M,N", [(256, 4), (256, 8), (40000, 4), (40000, 8)])
+def test_unit_vectors_every_int8_batched_bitwise(M, N):
+    """Every int8 value through the batched conversions: 5120-wide rows at
+    4 and 8 tokens take the SDWA byte converts (the one-group kernel for 256
+    rows, the persistent one for 40000). Token n reads column j_n alone, so
+    y[n][m] = q[m][j_n] exactly, and column j_n holds all 256 values."""
+    K = 5120
+    note(f"unit vectors every int8 M={M} N={N}")
+    rng = np.random.default_rng(M + N)
+    q = np.tile(rng.integers(-128, 128, size=(251, K)).astype(np.int8), (M // 251 + 1, 1))[:M]
+    cols = rng.choice(K, size=N, replace=False)
+    x = np.zeros((N, K), np.float16)
+    for n, j in enumerate(cols):
+        q[:, j] = ((np.arange(M) + 37 * n) % 256 - 128).astype(np.int8)
+        x[n, j] = 1.0
+    d = np.full((M, K // 32), 1.0, np.float16)
+    y = host(q8.gemv(upload(q, d), dev(x)))
+    for n, j in enumerate(cols):
+        assert np.array_equal(y[n], q[:, j].astype(np.float32)), f"token {n}"
+
+
 def test_subnormal_scale_and_activation_bitwise():
     note("subnormals")
     K = 64
